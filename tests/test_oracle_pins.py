@@ -1,0 +1,344 @@
+"""Pins of the CPU oracle against facts it does not compute itself.
+
+Each test ties one oracle function to something independent: a closed form,
+an exact rational computation, a hand-computed case from the pages' own
+examples, a textbook library routine, or an invariant. A plausible mistake
+in the oracle (a dropped term, a wrong index or sign, a transposed operand,
+a wrong tree) fails at least one of them. These run on the CPU only.
+"""
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as oatt
+from oracle import gemm as ogemm
+from oracle import logprob as olp
+from oracle import moe as omoe
+from oracle import numerics
+from oracle import rmsnorm as orms
+from oracle import tree as otree
+from split_invariant_deterministic_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- bf16 cast
+
+def _stratified_f32_bits(n_random=1 << 18, seed=0):
+    rng = np.random.default_rng(seed)
+    r = rng.integers(0, 1 << 32, size=n_random, dtype=np.uint64).astype(np.uint32)
+    hi = np.arange(0, 1 << 16, dtype=np.uint32) << 16
+    # every exponent/sign/mantissa-high pattern with the low half at and next
+    # to the rounding midpoint, plus exact bf16 values
+    lows = np.array([0x0000, 0x7FFF, 0x8000, 0x8001, 0xFFFF], dtype=np.uint32)
+    edge = (hi[:, None] | lows[None, :]).ravel()
+    return np.concatenate([r, edge])
+
+
+def test_bf16_cast_matches_torch_rne():
+    bits = _stratified_f32_bits()
+    f = bits.view(np.float32)
+    with np.errstate(invalid="ignore"):  # signalling-NaN patterns
+        ours = numerics.to_bf16(f.astype(np.float64))
+    ref = torch.from_numpy(f.copy()).to(torch.bfloat16).to(torch.float32).numpy()
+    nan = np.isnan(f)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan].astype(np.float32).view(np.uint32),
+                          ref[~nan].view(np.uint32))
+
+
+def test_bf16_hand_ties():
+    one = 1.0
+    assert numerics.to_bf16(one + 2.0 ** -8) == 1.0            # tie -> even (mantissa 0)
+    assert numerics.to_bf16(one + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6  # tie -> even (mantissa 2)
+    assert numerics.to_bf16(one + 2.0 ** -8 + 2.0 ** -30) == 1.0 + 2.0 ** -7
+    assert numerics.to_bf16(-0.0) == 0.0 and math.copysign(1, numerics.to_bf16(-0.0)) < 0
+    assert numerics.to_bf16(3.5e38) == np.inf
+    assert numerics.to_bf16(2.0 ** -133) == 2.0 ** -133          # smallest subnormal
+    assert numerics.to_bf16(2.0 ** -134) == 0.0                  # tie -> even zero
+
+
+# ---------------------------------------------------------------- tree shape
+
+def test_tree_schedules_hand_case():
+    g = json.load(open(os.path.join(GOLDEN, "tree_order.json")))
+    leaves = [np.float32(v) for v in g["leaves"]]
+    add = lambda a, b: np.float32(a + b)
+    assert otree.combine(leaves, add, otree.BALANCED) == np.float32(g["balanced"])
+    assert otree.combine(leaves, add, otree.LEFT_FOLD) == np.float32(g["left_fold"])
+
+
+def test_tree_shape_through_gemm_oracle():
+    g = json.load(open(os.path.join(GOLDEN, "tree_order.json")))
+    r = g["gemm_realisation"]
+    A = np.zeros((1, r["K"]))
+    B = np.zeros((1, r["K"]))
+    for k, v in r["A"].items():
+        A[0, int(k)] = v
+    for k, v in r["B"].items():
+        B[0, int(k)] = v
+    P = ogemm.leaf_partials(A, B, r["leaves"])
+    assert P[:, 0, 0].tolist() == g["leaves"]
+    assert ogemm.gemm_tree(A, B, 4, "fp32")[0, 0] == g["balanced"]
+    assert ogemm.gemm_tree(A, B, 4, "fp32", otree.LEFT_FOLD)[0, 0] == g["left_fold"]
+    assert ogemm.gemm_tree(A, B, 4, "bf16")[0, 0] == 1.0
+    # the plain definition sees the exact sum 1 + 2**24 + 1 - 2**24 = 2
+    assert ogemm.gemm(A, B, "fp32")[0, 0] == 2.0
+
+
+def test_balanced_is_adjacent_pairs_for_powers_of_two():
+    # recursive halving == pairing (0,1),(2,3),... level by level
+    names = [f"x{i}" for i in range(8)]
+    s = otree.balanced(names, lambda a, b: f"({a}+{b})")
+    assert s == "(((x0+x1)+(x2+x3))+((x4+x5)+(x6+x7)))"
+    # every aligned 2-, 4-block is a subtree (rank-local reduction is possible)
+    for blk in ("(x0+x1)", "(x6+x7)", "((x0+x1)+(x2+x3))", "((x4+x5)+(x6+x7))"):
+        assert blk in s
+
+
+# ---------------------------------------------------------------- GEMM leaves
+
+def test_leaf_sums_against_exact_rationals():
+    t = synth.tiny()
+    A = t["x"].float().numpy()
+    B = t["W"].float().numpy()[:48]  # 48 output columns keep Fraction work small
+    P = ogemm.leaf_partials(A, B, 4)
+    ex = ogemm.exact_leaf_sums(A, B, 4)
+    absp = ogemm.abs_products(A, B, 4)
+    for l in range(4):
+        for m in range(A.shape[0]):
+            for n in range(B.shape[0]):
+                e = ex[l][m][n]
+                err = abs(Fraction(float(P[l, m, n])) - e)
+                # half an fp32 ulp of the exact value plus the float64 sum error
+                bound = Fraction(2.0 ** -24) * abs(e) + Fraction(64 * 2.0 ** -53) * Fraction(absp[l, m, n])
+                assert err <= bound, (l, m, n)
+
+
+def test_leaf_partition_covers_k_and_tree_matches_plain_sum():
+    t = synth.tiny()
+    A = t["x"].float().numpy()
+    B = t["W"].float().numpy()
+    P = ogemm.leaf_partials(A, B, 4)
+    # a wrong leaf range (gap/overlap/transposed operand) breaks this identity
+    exact = A.astype(np.float64) @ B.astype(np.float64).T
+    assert np.allclose(P.astype(np.float64).sum(0), exact, rtol=0, atol=1e-5)
+    C = ogemm.combine_partials(P)
+    bound = ogemm.leaf_error_bound(64 + 2, ogemm.abs_products(A, B, 1)[0])
+    assert np.all(np.abs(C.astype(np.float64) - exact) <= bound)
+
+
+def test_integer_valued_gemm_is_exact_for_every_schedule():
+    rng = np.random.default_rng(1)
+    A = rng.integers(-8, 9, size=(5, 256)).astype(np.float64)
+    B = rng.integers(-8, 9, size=(7, 256)).astype(np.float64) * 0.25
+    exact = A @ B.T  # every partial sum < 2**24: all orders exact
+    for leaves in (1, 2, 4, 8):
+        for sch in (otree.BALANCED, otree.LEFT_FOLD):
+            assert np.array_equal(ogemm.gemm_tree(A, B, leaves, "fp32", sch), exact.astype(np.float32))
+
+
+# ---------------------------------------------------------------- RMSNorm
+
+def test_rmsnorm_closed_forms():
+    H = 256
+    g = np.ones(H)
+    assert np.all(orms.rmsnorm(np.zeros((1, H)), g) == 0.0)
+    assert np.all(orms.rmsnorm(np.ones((1, H)), g) == 1.0)        # 1/sqrt(1+eps) -> 1.0
+    x = np.zeros((1, H))
+    x[0, 17] = 1.0
+    y = orms.rmsnorm(x, g)
+    assert y[0, 17] == 16.0 and np.count_nonzero(y) == 1          # sqrt(256)*(1-1.3e-4) -> 16
+    # gamma multiplies per column, sign carries through
+    gg = np.linspace(-2, 2, H)
+    y2 = orms.rmsnorm(np.ones((1, H)) * -3.0, gg)
+    assert np.array_equal(y2[0], numerics.to_bf16(-gg / math.sqrt(1 + np.float32(1e-6) / 9)))
+
+
+def test_rmsnorm_sum_of_squares_exact_on_tiny():
+    x = synth.tiny()["x"].float().numpy().astype(np.float64)
+    eps = float(np.float32(1e-6))
+    for m in range(x.shape[0]):
+        ss = sum((Fraction(float(v)) ** 2 for v in x[m]), Fraction(0))
+        r_exact = 1.0 / math.sqrt(float(ss / x.shape[1]) + eps)
+        assert abs(orms.inv_rms(x[m:m + 1])[0] - r_exact) <= 4e-16 * r_exact
+
+
+# ---------------------------------------------------------------- logprob
+
+def test_logprob_constant_logits_is_minus_log_v():
+    g = json.load(open(os.path.join(GOLDEN, "logprob_constant.json")))
+    V = g["V"]
+    x = np.full((3, V), g["value"])
+    lp = olp.logprob(x, np.array([0, 5, V - 1]))
+    assert np.allclose(lp, g["expected"], rtol=0, atol=1e-15)
+    ms, ss = olp.chunk_stats(x, g["chunks"])
+    assert np.all(ss == g["chunk_sum"]) and np.all(ms == g["value"])
+
+
+def test_logprob_matches_torch_log_softmax_and_normalises():
+    rng = np.random.default_rng(3)
+    x = rng.normal(size=(6, 300)) * 3
+    t = rng.integers(0, 300, size=6)
+    ref = torch.log_softmax(torch.from_numpy(x), dim=-1).numpy()
+    assert np.allclose(olp.logprob(x, t), ref[np.arange(6), t], rtol=0, atol=1e-13)
+    all_t = np.stack([olp.logprob(x, np.full(6, v)) for v in range(300)], 1)
+    assert np.allclose(np.exp(all_t).sum(1), 1.0, rtol=0, atol=1e-12)
+
+
+def test_logprob_chunked_tree_equals_plain_lse():
+    rng = np.random.default_rng(4)
+    x = rng.normal(size=(4, 2374 * 3 + 5)) * 2
+    for C in (1, 2, 4, 64):
+        ms, ss = olp.chunk_stats(x, C)
+        for sch in (otree.BALANCED, otree.LEFT_FOLD):
+            assert np.allclose(olp.merge_tree(ms, ss, sch), olp.lse(x), rtol=0, atol=1e-12)
+
+
+def test_lse_merge_identity_and_halves():
+    m, s = np.array([0.7]), np.array([3.25])
+    mi, si = olp.merge((np.array([-np.inf]), np.array([0.0])), (m, s))
+    assert mi[0] == m[0] and si[0] == s[0]
+    mh, sh = olp.merge((m, s), (m, s))
+    assert mh[0] == m[0] and sh[0] == 2 * s[0]
+    # the merge is the LSE of the union
+    x = np.array([[0.1, 2.0, -1.0, 0.5, 3.0]])
+    a = (np.array([2.0]), np.array([np.exp(0.1 - 2) + 1 + np.exp(-3)]))
+    b = (np.array([3.0]), np.array([np.exp(0.5 - 3) + 1]))
+    mm, ssum = olp.merge(a, b)
+    assert abs(mm[0] + np.log(ssum[0]) - olp.lse(x)[0]) < 1e-14
+
+
+def test_logprob_bad_target_is_nan():
+    x = np.zeros((3, 10))
+    lp = olp.logprob(x, np.array([-1, 10, 3]))
+    assert np.isnan(lp[0]) and np.isnan(lp[1]) and not np.isnan(lp[2])
+
+
+# ---------------------------------------------------------------- attention
+
+def _attn_case(lengths, Hq=8, Hkv=2, D=16, seed=5):
+    rng = np.random.default_rng(seed)
+    lengths = np.asarray(lengths)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    q = numerics.to_bf16(rng.normal(size=(len(lengths), Hq, D)))
+    k = numerics.to_bf16(rng.normal(size=(cu[-1], Hkv, D)))
+    v = numerics.to_bf16(rng.normal(size=(cu[-1], Hkv, D)))
+    return q, k, v, cu, np.arange(len(lengths)), lengths - 1
+
+
+def test_split_bounds_partition_the_visible_keys():
+    for L in (1, 2, 15, 16, 17, 63, 64, 65, 1023, 1024, 1025, 32768, 5000):
+        b = oatt.split_bounds(L, 16, 64)
+        assert b[0][0] == 0 and b[-1][1] == L
+        for (a0, a1), (c0, c1) in zip(b, b[1:]):
+            assert a1 == c0 and a0 <= a1
+        for a, e in b:
+            assert a % 64 == 0 or a == L
+    # one chunk: only the last split is non-empty
+    assert [a < e for a, e in oatt.split_bounds(40, 16, 64)] == [False] * 15 + [True]
+
+
+def test_attention_single_key_returns_v0():
+    q, k, v, cu, qs, qp = _attn_case([1, 1])
+    out = oatt.attention(q, k, v, cu, qs, qp, 2)
+    for i in range(2):
+        for h in range(8):
+            assert np.array_equal(out[i, h], v[cu[i], h // 4])
+
+
+def test_attention_equal_keys_is_mean_of_v():
+    q, k, v, cu, qs, qp = _attn_case([37])
+    k[:] = k[0]
+    out = oatt.attention(q, k, v, cu, qs, qp, 2)
+    for h in range(8):
+        assert np.array_equal(out[0, h], numerics.to_bf16(v[:, h // 4].mean(0)))
+
+
+def test_attention_matches_torch_sdpa_float64():
+    q, k, v, cu, qs, qp = _attn_case([5, 130, 64])
+    out = oatt.attention(q, k, v, cu, qs, qp, 2, round_bf16=False)
+    for i in range(3):
+        kk = torch.from_numpy(k[cu[i]:cu[i] + qp[i] + 1]).permute(1, 0, 2).repeat_interleave(4, 0)
+        vv = torch.from_numpy(v[cu[i]:cu[i] + qp[i] + 1]).permute(1, 0, 2).repeat_interleave(4, 0)
+        qq = torch.from_numpy(q[i]).unsqueeze(1)
+        ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv)[:, 0].numpy()
+        assert np.allclose(out[i], ref, rtol=0, atol=1e-12)
+
+
+def test_attention_split_states_merge_to_plain():
+    q, k, v, cu, qs, qp = _attn_case([1, 3, 64, 65, 700, 1025], seed=6)
+    plain = oatt.attention(q, k, v, cu, qs, qp, 2, round_bf16=False)
+    for S, ch in ((1, 64), (4, 32), (16, 64)):
+        for sch in (otree.BALANCED, otree.LEFT_FOLD):
+            got = oatt.attention_splits(q, k, v, cu, qs, qp, 2, S, ch, sch)
+            assert np.allclose(got, plain, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- MoE
+
+def test_route_matches_torch_topk_and_ties():
+    rng = np.random.default_rng(7)
+    x = rng.normal(size=(20, 128))
+    ids, w = omoe.route(x, 8)
+    top = torch.topk(torch.from_numpy(x), 8, dim=1).indices.numpy()
+    assert np.array_equal(ids, np.sort(top, axis=1))
+    z = np.take_along_axis(x, ids, 1)
+    assert np.allclose(w, np.exp(z) / np.exp(z).sum(1, keepdims=True), atol=1e-7)
+    ids2, w2 = omoe.route(np.zeros((2, 16)), 4)
+    assert ids2.tolist() == [[0, 1, 2, 3]] * 2 and np.all(w2 == 0.25)
+    x3 = np.zeros((1, 16))
+    x3[0, [3, 9, 12]] = 5.0
+    x3[0, [1, 2]] = 1.0
+    x3[0, [0, 4]] = 1.0  # 0,1,2,4 tie at 1.0: lower ids win
+    ids3, _ = omoe.route(x3, 5)
+    assert ids3[0].tolist() == [0, 1, 3, 9, 12]
+
+
+def test_swiglu_closed_forms():
+    gu = np.array([[0.0, 2.0, 1.0, 1.0], [-60.0, 30.0, 3.0, 0.5]])
+    a = omoe.swiglu(gu)
+    assert a[0, 0] == 0.0                                   # silu(0) = 0
+    assert a[0, 1] == numerics.to_bf16(2.0 / (1 + math.exp(-2.0)))
+    assert a[1, 0] == numerics.to_bf16(-60.0 / (1 + math.exp(60.0)) * 3.0)
+    assert a[1, 1] == 15.0                                  # silu(30) = 30 (to bf16), * 0.5
+
+
+def test_moe_identical_experts_equal_one_expert():
+    rng = np.random.default_rng(8)
+    T, H, F, E = 6, 64, 32, 16
+    x = numerics.to_bf16(rng.normal(size=(T, H)))
+    W1 = numerics.to_bf16(rng.normal(size=(2 * F, H)) * 0.1)
+    W2 = numerics.to_bf16(rng.normal(size=(H, F)) * 0.1)
+    out, ids, w = omoe.moe_layer(x, np.zeros((T, E)), np.stack([W1] * E), np.stack([W2] * E), 8)
+    assert np.all(w == 0.125) and ids.tolist() == [list(range(8))] * T
+    single = numerics.to_bf16(omoe.expert_ffn(x, W1, W2).astype(np.float64))
+    assert np.array_equal(out, single)
+
+
+# ---------------------------------------------------------------- generator
+
+def test_synth_tiny_is_fixed_per_seed():
+    g = json.load(open(os.path.join(GOLDEN, "synth_hashes.json")))
+    t = synth.tiny(0)
+    import hashlib
+    for name in ("x", "W", "targets"):
+        h = hashlib.sha256(t[name].contiguous().view(torch.uint8).numpy().tobytes()).hexdigest()
+        assert h == g[name], name
+
+
+def test_oracle_reproduces_stored_tiny_values():
+    """Regression pin: a later change to the oracle's arithmetic must be deliberate."""
+    g = np.load(os.path.join(GOLDEN, "tiny_expected.npz"))
+    t = synth.tiny(0)
+    y = orms.rmsnorm(t["x"].float().numpy(), t["gamma"].float().numpy(), 1e-6)
+    assert np.array_equal(y.astype(np.float32), g["rms_y"])
+    lt = ogemm.gemm_tree(y, t["W"].float().numpy(), 4, "fp32")
+    assert np.array_equal(lt, g["logits_tree"])
+    assert np.array_equal(olp.logprob(lt, t["targets"].numpy()), g["logprob"])
