@@ -296,8 +296,12 @@ inv_status inv_moe_permute(const inv_contract* c, const int32_t* ids, int32_t* o
  * Y[r, :] = inv_gemm row of A = X[rows[r], :] (or X[r, :] if rows is NULL)
  * against B = W[e] [N, K]. Same leaves, tree and instruction chain as
  * inv_gemm, so each row is bitwise what inv_gemm gives for it alone.
- * X [*, K] bf16, W [E, N, K] bf16, Y [T*k, N] out_dtype. ranks must be 1. */
-inv_status inv_moe_gemm(const inv_contract* c, const void* X, const int32_t* rows,
+ * X [x_rows, K] bf16, W [E, N, K] bf16, Y [R, N] out_dtype, offsets [E+1]
+ * int32 non-decreasing with offsets[E] <= R (as inv_moe_permute writes it).
+ * Offsets are clamped to [0, R] and a gathered index outside [0, x_rows)
+ * reads a zero row, so malformed tables cannot address outside the buffers.
+ * ranks must be 1. */
+inv_status inv_moe_gemm(const inv_contract* c, const void* X, int64_t x_rows, const int32_t* rows,
                         const int32_t* offsets, const void* W, void* Y, int64_t R, int32_t E,
                         int64_t N, int64_t K, hipStream_t stream);
 
@@ -309,10 +313,12 @@ inv_status inv_swiglu(const inv_contract* c, const void* GU, void* Aout, int64_t
 
 /* Combine: out[t, :] = bf16( tree over j of w[t,j] * Y[slot[t,j], :] ) with
  * the k = c->leaves leaves in ascending expert id (the order inv_moe_route
- * emits), fp32 products and fp32 balanced tree. Y [*, H] fp32,
- * out [T, H] bf16. */
+ * emits), fp32 products and the contract's fp32 tree (balanced; left fold
+ * only as the contrasting schedule). Y [y_rows, H] fp32, w [T, k] fp32,
+ * slot [T, k] int32, out [T, H] bf16. A slot outside [0, y_rows) makes that
+ * token's row NaN. */
 inv_status inv_moe_combine(const inv_contract* c, const float* Y, const float* w,
-                           const int32_t* slot, void* out, int64_t T, int64_t H,
+                           const int32_t* slot, int64_t y_rows, void* out, int64_t T, int64_t H,
                            hipStream_t stream);
 
 #ifdef __cplusplus

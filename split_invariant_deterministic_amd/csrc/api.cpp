@@ -1,0 +1,448 @@
+// C-ABI layer of libinv: contract and shape validation (host only, before any
+// HIP call), workspace sizing, and dispatch to the gfx950 kernel launchers.
+//
+// The contract mirrors the execution contract of the IsoExec blog ("Unified
+// execution contract"): every constant that can move a rounding is explicit.
+// The topology claim of that section -- a parallel size is accepted only if
+// it has been proven invariant -- becomes the rank check here: ranks must be
+// a power of two dividing the leaf count, because then each rank owns an
+// aligned block of leaves, which is a subtree of the balanced tree, and its
+// local sum is a node of the same tree.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstring>
+#include <new>
+
+#include "../../include/inv.h"
+#include "launch.h"
+
+namespace {
+
+bool is_pow2(uint64_t v) { return v != 0 && (v & (v - 1)) == 0; }
+
+inv_status hip_status(hipError_t e) { return e == hipSuccess ? INV_OK : INV_E_HIP; }
+
+// Common contract checks; op-specific limits follow in each entry point.
+inv_status check_contract(const inv_contract* c) {
+  if (!c) return INV_E_ARG;
+  if (c->struct_size != sizeof(inv_contract) || c->abi_version != INV_ABI_VERSION) return INV_E_ARG;
+  if (c->reserved != 0) return INV_E_ARG;
+  if (c->accum_dtype != INV_FP32 || c->leaf_dtype != INV_FP32) return INV_E_CONTRACT;
+  if (c->out_dtype != INV_BF16 && c->out_dtype != INV_FP32) return INV_E_CONTRACT;
+  if (c->tree != INV_TREE_BALANCED && c->tree != INV_TREE_LEFT_FOLD) return INV_E_CONTRACT;
+  if (!is_pow2(c->leaves)) return INV_E_CONTRACT;
+  if (!is_pow2(c->ranks) || c->ranks > c->leaves || c->leaves % c->ranks != 0) return INV_E_TOPOLOGY;
+  return INV_OK;
+}
+
+inv_status check_gemm_contract(const inv_contract* c, int64_t K) {
+  inv_status s = check_contract(c);
+  if (s != INV_OK) return s;
+  if (c->tree != INV_TREE_BALANCED) return INV_E_CONTRACT;  // the in-kernel tree is balanced only
+  if (c->leaves > 8) return INV_E_UNSUPPORTED;
+  if (K < 0) return INV_E_ARG;
+  if (K % c->leaves != 0) return INV_E_CONTRACT;
+  if ((K / c->leaves) % 32 != 0) return INV_E_CONTRACT;
+  if (K == 0) return INV_E_CONTRACT;
+  return INV_OK;
+}
+
+inv_status check_attn_contract(const inv_contract* c) {
+  inv_status s = check_contract(c);
+  if (s != INV_OK) return s;
+  if (!is_pow2(c->split_kv) || c->split_kv > 32) return INV_E_CONTRACT;
+  if (c->kv_chunk != 32 && c->kv_chunk != 64 && c->kv_chunk != 128) return INV_E_CONTRACT;
+  if (c->out_dtype != INV_BF16) return INV_E_CONTRACT;
+  return INV_OK;
+}
+
+inv_status check_logprob_contract(const inv_contract* c, int64_t V) {
+  inv_status s = check_contract(c);
+  if (s != INV_OK) return s;
+  if (c->leaves > 512) return INV_E_UNSUPPORTED;
+  if (V > 0 && (int64_t)c->leaves > V) return INV_E_CONTRACT;  // every chunk non-empty
+  return INV_OK;
+}
+
+bool out_is_bf16(const inv_contract* c) { return c->out_dtype == INV_BF16; }
+
+}  // namespace
+
+extern "C" {
+
+inv_status inv_contract_default(inv_contract* c) {
+  if (!c) return INV_E_ARG;
+  std::memset(c, 0, sizeof(*c));
+  c->struct_size = sizeof(inv_contract);
+  c->abi_version = INV_ABI_VERSION;
+  c->leaves = 8;
+  c->ranks = 1;
+  c->tree = INV_TREE_BALANCED;
+  c->accum_dtype = INV_FP32;
+  c->leaf_dtype = INV_FP32;
+  c->out_dtype = INV_BF16;
+  c->split_kv = 16;
+  c->kv_chunk = 64;
+  c->eps = 1e-6f;
+  c->reserved = 0;
+  return INV_OK;
+}
+
+inv_status inv_contract_check(const inv_contract* c, int op, int64_t K) {
+  switch (op) {
+    case INV_OP_GEMM:
+    case INV_OP_MOE_GEMM:
+      return check_gemm_contract(c, K);
+    case INV_OP_TREE_COMBINE:
+    case INV_OP_MOE_COMBINE:
+    case INV_OP_MOE_ROUTE:
+      return check_contract(c);
+    case INV_OP_RMSNORM: {
+      inv_status s = check_contract(c);
+      if (s != INV_OK) return s;
+      if (!(c->eps >= 0.0f) || !std::isfinite(c->eps)) return INV_E_CONTRACT;
+      return INV_OK;
+    }
+    case INV_OP_LOGPROB:
+      return check_logprob_contract(c, 0);
+    case INV_OP_DECODE_ATTN:
+      return check_attn_contract(c);
+    default:
+      return INV_E_ARG;
+  }
+}
+
+size_t inv_workspace_bytes(const inv_contract* c, int op, int64_t d0, int64_t d1, int64_t d2) {
+  if (d0 < 0 || d1 < 0 || d2 < 0) return (size_t)-1;
+  switch (op) {
+    case INV_OP_GEMM:
+      if (check_gemm_contract(c, d2) != INV_OK) return (size_t)-1;
+      return c->ranks > 1 ? (size_t)c->ranks * (size_t)d0 * (size_t)d1 * sizeof(float) : 0;
+    case INV_OP_DECODE_ATTN:
+      if (check_attn_contract(c) != INV_OK) return (size_t)-1;
+      return (size_t)d0 * (size_t)d1 * (size_t)c->split_kv * (size_t)(d2 + 2) * sizeof(float);
+    default:
+      if (inv_contract_check(c, op, d2) != INV_OK) return (size_t)-1;
+      return 0;
+  }
+}
+
+const char* inv_status_string(inv_status s) {
+  switch (s) {
+    case INV_OK: return "ok";
+    case INV_E_ARG: return "invalid argument";
+    case INV_E_CONTRACT: return "contract constant not implemented";
+    case INV_E_TOPOLOGY: return "rank count outside the proven set";
+    case INV_E_UNSUPPORTED: return "shape outside the implemented range";
+    case INV_E_HIP: return "HIP launch or query failed";
+    case INV_E_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+// ------------------------------------------------------------------ GEMM
+
+static inv::GemmLaunch gemm_launch(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                                   int kl, int leaf_lo, int nl, int groups, bool out_bf16) {
+  inv::GemmLaunch g;
+  g.A = A;
+  g.B = B;
+  g.C = C;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.c_group_stride = M * N;
+  g.kl = kl;
+  g.leaf_lo = leaf_lo;
+  g.nl = nl;
+  g.groups = groups;
+  g.out_bf16 = out_bf16;
+  g.rows = nullptr;
+  g.offsets = nullptr;
+  g.E = 0;
+  g.a_rows = M;
+  g.b_expert_stride = 0;
+  return g;
+}
+
+static inv_status gemm_shape_check(const void* A, const void* B, const void* C, int64_t M, int64_t N,
+                                   int64_t K) {
+  if (M < 0 || N < 0 || K <= 0) return INV_E_ARG;
+  if (M > (int64_t)1 << 31 || N > (int64_t)1 << 31) return INV_E_UNSUPPORTED;
+  if (M > 0 && N > 0 && (!A || !B || !C)) return INV_E_ARG;
+  // 16-byte vector loads along K
+  if ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) & 15u) return INV_E_ARG;
+  return INV_OK;
+}
+
+inv_status inv_gemm(const inv_contract* c, const void* A, const void* B, void* C, int64_t M, int64_t N,
+                    int64_t K, void* ws, size_t ws_bytes, hipStream_t stream) {
+  inv_status s = check_gemm_contract(c, K);
+  if (s != INV_OK) return s;
+  if ((s = gemm_shape_check(A, B, C, M, N, K)) != INV_OK) return s;
+  if (M == 0 || N == 0) return INV_OK;
+  const int L = (int)c->leaves, R = (int)c->ranks;
+  const int kl = (int)(K / L);
+  if (R == 1) return hip_status(inv::launch_gemm(gemm_launch(A, B, C, M, N, K, kl, 0, L, 1, out_is_bf16(c)), stream));
+  const size_t need = (size_t)R * (size_t)M * (size_t)N * sizeof(float);
+  if (!ws || ws_bytes < need) return INV_E_WORKSPACE;
+  // every emulated rank reduces its aligned subtree into its own fp32 plane ...
+  hipError_t e = inv::launch_gemm(gemm_launch(A, B, ws, M, N, K, kl, 0, L / R, R, false), stream);
+  if (e != hipSuccess) return INV_E_HIP;
+  // ... and the top log2(R) levels of the same tree finish the sum
+  return hip_status(inv::launch_tree_combine(static_cast<const float*>(ws), R, M * N, C, out_is_bf16(c), false,
+                                             stream));
+}
+
+inv_status inv_gemm_rank(const inv_contract* c, const void* A, const void* B, float* P_r, int64_t M, int64_t N,
+                         int64_t K, uint32_t rank, hipStream_t stream) {
+  inv_status s = check_gemm_contract(c, K);
+  if (s != INV_OK) return s;
+  if ((s = gemm_shape_check(A, B, P_r, M, N, K)) != INV_OK) return s;
+  if (rank >= c->ranks) return INV_E_ARG;
+  if (M == 0 || N == 0) return INV_OK;
+  const int L = (int)c->leaves, R = (int)c->ranks;
+  const int nl = L / R;
+  return hip_status(
+      inv::launch_gemm(gemm_launch(A, B, P_r, M, N, K, (int)(K / L), (int)rank * nl, nl, 1, false), stream));
+}
+
+inv_status inv_gemm_leaves(const inv_contract* c, const void* A, const void* B, float* P, int64_t M, int64_t N,
+                           int64_t K, uint32_t leaf_lo, uint32_t leaf_hi, hipStream_t stream) {
+  inv_status s = check_gemm_contract(c, K);
+  if (s != INV_OK) return s;
+  if ((s = gemm_shape_check(A, B, P, M, N, K)) != INV_OK) return s;
+  if (leaf_lo >= leaf_hi || leaf_hi > c->leaves) return INV_E_ARG;
+  if (M == 0 || N == 0) return INV_OK;
+  const int L = (int)c->leaves;
+  return hip_status(inv::launch_gemm(
+      gemm_launch(A, B, P, M, N, K, (int)(K / L), (int)leaf_lo, 1, (int)(leaf_hi - leaf_lo), false), stream));
+}
+
+inv_status inv_tree_combine(const inv_contract* c, const float* P, uint32_t count, void* C, int64_t M, int64_t N,
+                            hipStream_t stream) {
+  inv_status s = check_contract(c);
+  if (s != INV_OK) return s;
+  if (M < 0 || N < 0) return INV_E_ARG;
+  if (!is_pow2(count) || count > 64) return INV_E_UNSUPPORTED;
+  if (M == 0 || N == 0) return INV_OK;
+  if (!P || !C) return INV_E_ARG;
+  return hip_status(inv::launch_tree_combine(P, (int)count, M * N, C, out_is_bf16(c), c->tree == INV_TREE_LEFT_FOLD,
+                                             stream));
+}
+
+inv_status inv_cast_bf16(const float* x, uint16_t* y, int64_t n, hipStream_t stream) {
+  if (n < 0) return INV_E_ARG;
+  if (n == 0) return INV_OK;
+  if (!x || !y) return INV_E_ARG;
+  return hip_status(inv::launch_cast_bf16(x, y, n, stream));
+}
+
+// --------------------------------------------------------------- RMSNorm
+
+inv_status inv_rmsnorm(const inv_contract* c, const void* x, const void* gamma, void* y, int64_t M, int64_t H,
+                       hipStream_t stream) {
+  inv_status s = inv_contract_check(c, INV_OP_RMSNORM, 0);
+  if (s != INV_OK) return s;
+  if (M < 0 || H < 0) return INV_E_ARG;
+  if (H % 8 != 0 || H > 16384 || (H > 0 && H < 8)) return INV_E_UNSUPPORTED;
+  if (M == 0 || H == 0) return INV_OK;
+  if (!x || !gamma || !y) return INV_E_ARG;
+  if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(gamma) | reinterpret_cast<uintptr_t>(y)) & 15u)
+    return INV_E_ARG;
+  if (c->out_dtype != INV_BF16) return INV_E_CONTRACT;
+  return hip_status(inv::launch_rmsnorm(x, gamma, y, M, H, c->eps, stream));
+}
+
+// --------------------------------------------------------------- logprob
+
+inv_status inv_logprob(const inv_contract* c, const float* logits, int64_t ldl, const int32_t* target, float* out,
+                       int64_t M, int64_t V, hipStream_t stream) {
+  inv_status s = check_logprob_contract(c, V);
+  if (s != INV_OK) return s;
+  if (M < 0 || V <= 0 || ldl < V) return INV_E_ARG;
+  if (M == 0) return INV_OK;
+  if (!logits || !target || !out) return INV_E_ARG;
+  return hip_status(inv::launch_logprob(logits, ldl, target, out, nullptr, nullptr, M, V, (int)c->leaves, 0,
+                                        (int)c->leaves, c->tree == INV_TREE_LEFT_FOLD, false, stream));
+}
+
+inv_status inv_logprob_partials(const inv_contract* c, const float* logits, int64_t ldl, const int32_t* target,
+                                float* stats, float* tlogit, int64_t M, int64_t V, uint32_t chunk_lo,
+                                uint32_t chunk_hi, hipStream_t stream) {
+  inv_status s = check_logprob_contract(c, V);
+  if (s != INV_OK) return s;
+  if (M < 0 || V <= 0 || ldl < V) return INV_E_ARG;
+  if (chunk_lo >= chunk_hi || chunk_hi > c->leaves) return INV_E_ARG;
+  if (M == 0) return INV_OK;
+  if (!logits || !target || !stats || !tlogit) return INV_E_ARG;
+  return hip_status(inv::launch_logprob(logits, ldl, target, nullptr, stats, tlogit, M, V, (int)c->leaves,
+                                        (int)chunk_lo, (int)chunk_hi, false, true, stream));
+}
+
+inv_status inv_logprob_combine(const inv_contract* c, const float* stats, const float* tlogit,
+                               const int32_t* target, float* out, int64_t M, int64_t V, hipStream_t stream) {
+  inv_status s = check_logprob_contract(c, V);
+  if (s != INV_OK) return s;
+  if (M < 0 || V <= 0) return INV_E_ARG;
+  if (M == 0) return INV_OK;
+  if (!stats || !tlogit || !target || !out) return INV_E_ARG;
+  return hip_status(inv::launch_logprob_combine(stats, tlogit, target, out, M, V, (int)c->leaves,
+                                                c->tree == INV_TREE_LEFT_FOLD, stream));
+}
+
+// ------------------------------------------------------------- attention
+
+static inv_status attn_check(const inv_contract* c, const void* q, const void* k, const void* v,
+                             const int32_t* cu, int32_t num_seqs, const int32_t* q_seq, const int32_t* q_pos,
+                             int64_t Tq, int32_t Hq, int32_t Hkv, int32_t D) {
+  inv_status s = check_attn_contract(c);
+  if (s != INV_OK) return s;
+  if (Tq < 0 || Hq <= 0 || Hkv <= 0 || num_seqs < 0) return INV_E_ARG;
+  if (D != 128) return INV_E_UNSUPPORTED;
+  if (Hq % Hkv != 0 || Hq / Hkv > 16) return INV_E_UNSUPPORTED;
+  if (Tq > 0 && (!q || !k || !v || !cu || !q_seq || !q_pos || num_seqs == 0)) return INV_E_ARG;
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v)) & 15u)
+    return INV_E_ARG;
+  return INV_OK;
+}
+
+static inv::AttnLaunch attn_launch(const inv_contract* c, const void* q, const void* k, const void* v,
+                                   const int32_t* cu, int32_t num_seqs, const int32_t* q_seq, const int32_t* q_pos,
+                                   int64_t Tq, int32_t Hq, int32_t Hkv, int32_t D, uint32_t lo, uint32_t hi,
+                                   void* ws) {
+  inv::AttnLaunch a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.cu_seqlens = cu;
+  a.q_seq = q_seq;
+  a.q_pos = q_pos;
+  a.Tq = Tq;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.num_seqs = num_seqs;
+  a.split_kv = (int)c->split_kv;
+  a.kv_chunk = (int)c->kv_chunk;
+  a.split_lo = (int)lo;
+  a.split_hi = (int)hi;
+  a.ws = static_cast<float*>(ws);
+  return a;
+}
+
+inv_status inv_decode_attn(const inv_contract* c, const void* q, const void* k, const void* v,
+                           const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* q_seq, const int32_t* q_pos,
+                           void* out, int64_t Tq, int32_t Hq, int32_t Hkv, int32_t D, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  inv_status s = attn_check(c, q, k, v, cu_seqlens, num_seqs, q_seq, q_pos, Tq, Hq, Hkv, D);
+  if (s != INV_OK) return s;
+  if (Tq == 0) return INV_OK;
+  if (!out) return INV_E_ARG;
+  const size_t need = inv_workspace_bytes(c, INV_OP_DECODE_ATTN, Tq, Hq, D);
+  if (!ws || ws_bytes < need) return INV_E_WORKSPACE;
+  hipError_t e = inv::launch_attn_splits(
+      attn_launch(c, q, k, v, cu_seqlens, num_seqs, q_seq, q_pos, Tq, Hq, Hkv, D, 0, c->split_kv, ws), stream);
+  if (e != hipSuccess) return INV_E_HIP;
+  return hip_status(inv::launch_attn_combine(static_cast<const float*>(ws), out, Tq, Hq, D, (int)c->split_kv,
+                                             c->tree == INV_TREE_LEFT_FOLD, stream));
+}
+
+inv_status inv_attn_splits(const inv_contract* c, const void* q, const void* k, const void* v,
+                           const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* q_seq, const int32_t* q_pos,
+                           int64_t Tq, int32_t Hq, int32_t Hkv, int32_t D, uint32_t split_lo, uint32_t split_hi,
+                           void* ws, size_t ws_bytes, hipStream_t stream) {
+  inv_status s = attn_check(c, q, k, v, cu_seqlens, num_seqs, q_seq, q_pos, Tq, Hq, Hkv, D);
+  if (s != INV_OK) return s;
+  if (split_lo >= split_hi || split_hi > c->split_kv) return INV_E_ARG;
+  if (Tq == 0) return INV_OK;
+  const size_t need = inv_workspace_bytes(c, INV_OP_DECODE_ATTN, Tq, Hq, D);
+  if (!ws || ws_bytes < need) return INV_E_WORKSPACE;
+  return hip_status(inv::launch_attn_splits(
+      attn_launch(c, q, k, v, cu_seqlens, num_seqs, q_seq, q_pos, Tq, Hq, Hkv, D, split_lo, split_hi, ws), stream));
+}
+
+inv_status inv_attn_combine(const inv_contract* c, const void* ws, size_t ws_bytes, void* out, int64_t Tq,
+                            int32_t Hq, int32_t D, hipStream_t stream) {
+  inv_status s = check_attn_contract(c);
+  if (s != INV_OK) return s;
+  if (Tq < 0 || Hq <= 0) return INV_E_ARG;
+  if (D != 128) return INV_E_UNSUPPORTED;
+  if (Tq == 0) return INV_OK;
+  if (!out) return INV_E_ARG;
+  const size_t need = inv_workspace_bytes(c, INV_OP_DECODE_ATTN, Tq, Hq, D);
+  if (!ws || ws_bytes < need) return INV_E_WORKSPACE;
+  return hip_status(inv::launch_attn_combine(static_cast<const float*>(ws), out, Tq, Hq, D, (int)c->split_kv,
+                                             c->tree == INV_TREE_LEFT_FOLD, stream));
+}
+
+// ------------------------------------------------------------------- MoE
+
+inv_status inv_moe_route(const inv_contract* c, const float* logits, int32_t* ids, float* w, int64_t T, int32_t E,
+                         hipStream_t stream) {
+  inv_status s = check_contract(c);
+  if (s != INV_OK) return s;
+  if (T < 0 || E <= 0) return INV_E_ARG;
+  if (E > 256 || (int64_t)c->leaves > E || c->leaves > 32) return INV_E_UNSUPPORTED;
+  if (T == 0) return INV_OK;
+  if (!logits || !ids || !w) return INV_E_ARG;
+  return hip_status(inv::launch_moe_route(logits, ids, w, T, E, (int)c->leaves, stream));
+}
+
+inv_status inv_moe_permute(const inv_contract* c, const int32_t* ids, int32_t* offsets, int32_t* rows,
+                           int32_t* slot, int64_t T, int32_t E, hipStream_t stream) {
+  inv_status s = check_contract(c);
+  if (s != INV_OK) return s;
+  if (T < 0 || E <= 0) return INV_E_ARG;
+  if (E > 256 || (int64_t)c->leaves > E || c->leaves > 32) return INV_E_UNSUPPORTED;
+  if (T * (int64_t)c->leaves > ((int64_t)1 << 31) - 1) return INV_E_UNSUPPORTED;
+  if (!offsets) return INV_E_ARG;
+  if (T > 0 && (!ids || !rows || !slot)) return INV_E_ARG;
+  return hip_status(inv::launch_moe_permute(ids, offsets, rows, slot, T, E, (int)c->leaves, stream));
+}
+
+inv_status inv_moe_gemm(const inv_contract* c, const void* X, int64_t x_rows, const int32_t* rows,
+                        const int32_t* offsets, const void* W, void* Y, int64_t R, int32_t E, int64_t N, int64_t K,
+                        hipStream_t stream) {
+  inv_status s = check_gemm_contract(c, K);
+  if (s != INV_OK) return s;
+  if (c->ranks != 1) return INV_E_TOPOLOGY;
+  if (R < 0 || N < 0 || E <= 0 || x_rows < 0) return INV_E_ARG;
+  if (E > 65536) return INV_E_UNSUPPORTED;
+  if (R == 0 || N == 0) return INV_OK;
+  if (!X || !offsets || !W || !Y) return INV_E_ARG;
+  if (!rows && x_rows < R) return INV_E_ARG;
+  if ((reinterpret_cast<uintptr_t>(X) | reinterpret_cast<uintptr_t>(W)) & 15u) return INV_E_ARG;
+  inv::GemmLaunch g = gemm_launch(X, W, Y, R, N, K, (int)(K / c->leaves), 0, (int)c->leaves, 1, out_is_bf16(c));
+  g.rows = rows;
+  g.offsets = offsets;
+  g.E = E;
+  g.a_rows = x_rows;
+  g.b_expert_stride = N * K;
+  return hip_status(inv::launch_gemm(g, stream));
+}
+
+inv_status inv_swiglu(const inv_contract* c, const void* GU, void* Aout, int64_t R, int64_t F, hipStream_t stream) {
+  inv_status s = check_contract(c);
+  if (s != INV_OK) return s;
+  if (R < 0 || F < 0) return INV_E_ARG;
+  if (R == 0 || F == 0) return INV_OK;
+  if (!GU || !Aout) return INV_E_ARG;
+  return hip_status(inv::launch_swiglu(GU, Aout, R, F, stream));
+}
+
+inv_status inv_moe_combine(const inv_contract* c, const float* Y, const float* w, const int32_t* slot,
+                           int64_t y_rows, void* out, int64_t T, int64_t H, hipStream_t stream) {
+  inv_status s = check_contract(c);
+  if (s != INV_OK) return s;
+  if (c->leaves > 32) return INV_E_UNSUPPORTED;
+  if (T < 0 || H < 0 || y_rows < 0) return INV_E_ARG;
+  if (T == 0 || H == 0) return INV_OK;
+  if (!Y || !w || !slot || !out) return INV_E_ARG;
+  if (c->out_dtype != INV_BF16) return INV_E_CONTRACT;
+  return hip_status(inv::launch_moe_combine(Y, w, slot, y_rows, out, T, H, (int)c->leaves,
+                                            c->tree == INV_TREE_LEFT_FOLD, stream));
+}
+
+}  // extern "C"

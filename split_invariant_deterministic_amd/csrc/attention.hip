@@ -1,0 +1,317 @@
+// Split-KV attention with a pinned split rule and merge order, for gfx950.
+//
+// IsoExec blog, "Unified execution contract": the split-KV partition count is
+// a pinned constant of the composition. RL-Kernel write-up, section 4: the
+// softmax over the visible keys is an LSE reduction whose block maxima, sums
+// and merge order must be fixed; section 7 (optional ROCm path): fixed block
+// partition, chunk order and rescale-merge order.
+//
+// Schedule for a query row with L visible keys (depends on L only):
+//   keys form chunks of CH from position 0, n = ceil(L / CH) chunks;
+//   split j of S owns chunks [floor(j n / S), floor((j+1) n / S));
+//   per chunk, in ascending order (online softmax, all fp32):
+//     s     = (q . k) * (1/sqrt(D))      q.k: 4 chained MFMAs over d from +0
+//     m'    = max(m, max_chunk s)
+//     alpha = exp2((m - m') * log2e)
+//     p     = bf16( exp2((s - m') * log2e) ), masked keys give 0
+//     l'    = l * alpha + sum_chunk p   (lane sums in (block, row) order,
+//                                        then xor 16, 32)
+//     o'    = MFMA chain of P.V over the chunk's 32-key steps, started from
+//             o * alpha
+//   empty splits are (m, l, o) = (-inf, 0, 0).
+// The S split states are then merged by the contract's tree with
+// m = max(m1,m2), l = l1 f1 + l2 f2, o = o1 f1 + o2 f2 (f = exp2((m_i - m)
+// log2e)), and out = bf16(o / l).
+//
+// One wave computes one (row, kv head, split) for the whole GQA group of
+// query heads (rows of the MFMA tile), so a row's bits depend only on its q,
+// its visible keys and L: a decode row equals the same position's row in a
+// multi-row (prefill) launch. Scores are produced transposed (keys x heads):
+// each lane then holds the 8 probabilities of one head that the P.V MFMA
+// takes as its A operand; V is transposed through LDS so that the B operand
+// holds the same 8 keys in the same slots.
+#include "common.h"
+#include "launch.h"
+
+namespace inv {
+namespace {
+
+constexpr int kD = 128;
+constexpr int kVtStride = 0;  // unused marker (stride below is per CH)
+
+template <int CH>
+struct AttnCfg {
+  static constexpr int KB = CH / 16;     // 16-key blocks per chunk
+  static constexpr int PV = CH / 32;     // 32-key MFMA steps per chunk
+  static constexpr int VT = CH + 4;      // LDS row stride (bf16) of V^T
+  static constexpr int VLOADS = CH * 16 / 64;  // 16-byte V loads per lane per chunk
+};
+
+template <int CH>
+__global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a, float scale) {
+  using Cfg = AttnCfg<CH>;
+  __shared__ __attribute__((aligned(16))) uint16_t vt[kD * Cfg::VT];
+
+  const int lane = threadIdx.x;
+  const int g4 = lane >> 4, c16 = lane & 15;
+  const int nsplit = a.split_hi - a.split_lo;
+  int64_t idx = blockIdx.x;
+  const int j = a.split_lo + (int)(idx % nsplit);
+  idx /= nsplit;
+  const int kvh = (int)(idx % a.Hkv);
+  const int64_t row = idx / a.Hkv;
+  const int grp = a.Hq / a.Hkv;
+  const int S = a.split_kv;
+
+  const int seq = a.q_seq[row];
+  const int64_t start = a.cu_seqlens[seq];
+  const int64_t L = (int64_t)a.q_pos[row] + 1;
+  const int64_t n = (L + CH - 1) / CH;
+  const int64_t c0 = ((int64_t)j * n) / S, c1 = ((int64_t)(j + 1) * n) / S;
+
+  const uint16_t* Q = static_cast<const uint16_t*>(a.q);
+  const uint16_t* K = static_cast<const uint16_t*>(a.k);
+  const uint16_t* Vg = static_cast<const uint16_t*>(a.v);
+  const int64_t kv_row = (int64_t)a.Hkv * kD;  // elements between consecutive keys
+
+  // Q^T as the B operand: column = head c16 of the group, k = d.
+  bf16x8 qf[4];
+  {
+    const bool hv = c16 < grp;
+    const uint16_t* qp = Q + (row * a.Hq + (int64_t)kvh * grp + (hv ? c16 : 0)) * kD;
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) {
+      u32x4 v = *reinterpret_cast<const u32x4*>(qp + ds * 32 + 8 * g4);
+      if (!hv) v = u32x4{0u, 0u, 0u, 0u};
+      qf[ds] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  float m_run = -INFINITY, l_run = 0.0f;  // per head c16 (identical in the 4 lanes of a head)
+  f32x4 o[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int64_t c = c0; c < c1; ++c) {
+    const int64_t kbase = c * CH;  // position of the chunk's first key
+    // ---- loads: K fragments (A operand: key rows, k = d) and V rows
+    bf16x8 kf[Cfg::KB][4];
+#pragma unroll
+    for (int kb = 0; kb < Cfg::KB; ++kb) {
+      const int64_t pos = kbase + kb * 16 + c16;
+      const bool ok = pos < L;
+      const uint16_t* kp = K + (start + (ok ? pos : 0)) * kv_row + (int64_t)kvh * kD + 8 * g4;
+#pragma unroll
+      for (int ds = 0; ds < 4; ++ds) {
+        u32x4 v = *reinterpret_cast<const u32x4*>(kp + ds * 32);
+        if (!ok) v = u32x4{0u, 0u, 0u, 0u};
+        kf[kb][ds] = __builtin_bit_cast(bf16x8, v);
+      }
+    }
+    u32x4 vv[Cfg::VLOADS];
+#pragma unroll
+    for (int i = 0; i < Cfg::VLOADS; ++i) {
+      const int key = 4 * i + g4;  // 16 lanes share a key: 16 x 16 B = one 128-d row
+      const int64_t pos = kbase + key;
+      const bool ok = pos < L;
+      u32x4 v = *reinterpret_cast<const u32x4*>(Vg + (start + (ok ? pos : 0)) * kv_row + (int64_t)kvh * kD + 8 * c16);
+      if (!ok) v = u32x4{0u, 0u, 0u, 0u};
+      vv[i] = v;
+    }
+    // ---- S^T = K Q^T: lane holds keys kb*16 + 4*g4 + r for head c16
+    f32x4 st[Cfg::KB];
+#pragma unroll
+    for (int kb = 0; kb < Cfg::KB; ++kb) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ds = 0; ds < 4; ++ds) acc = mfma16(kf[kb][ds], qf[ds], acc);
+      st[kb] = acc;
+    }
+    float cmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < Cfg::KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t pos = kbase + kb * 16 + 4 * g4 + r;
+        float s = st[kb][r] * scale;
+        if (pos >= L) s = -INFINITY;
+        st[kb][r] = s;
+        cmax = fmaxf(cmax, s);
+      }
+    cmax = fmaxf(cmax, shfl_xor(cmax, 16));
+    cmax = fmaxf(cmax, shfl_xor(cmax, 32));
+    const float m_new = fmaxf(m_run, cmax);
+    const float alpha = exp_shifted(m_run, m_new);
+    float psum = 0.0f;
+    uint32_t pw[Cfg::KB][2];  // bf16 p, packed pairs
+#pragma unroll
+    for (int kb = 0; kb < Cfg::KB; ++kb) {
+      float pb[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = exp_shifted(st[kb][r], m_new);
+        pb[r] = bf16_bits_to_f32(f32_to_bf16_bits(p));
+        psum = psum + pb[r];
+      }
+      pw[kb][0] = pack_bf16x2(pb[0], pb[1]);
+      pw[kb][1] = pack_bf16x2(pb[2], pb[3]);
+    }
+    psum = psum + shfl_xor(psum, 16);
+    psum = psum + shfl_xor(psum, 32);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+
+    // ---- V^T into LDS: vt[d][key]
+#pragma unroll
+    for (int i = 0; i < Cfg::VLOADS; ++i) {
+      const int key = 4 * i + g4;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int d = 8 * c16 + 2 * q;
+        vt[d * Cfg::VT + key] = (uint16_t)(vv[i][q] & 0xffffu);
+        vt[(d + 1) * Cfg::VT + key] = (uint16_t)(vv[i][q] >> 16);
+      }
+    }
+    __syncthreads();
+
+    // ---- o = P V, started from o * alpha. Output rows = heads 4*g4 + r.
+    float al[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) al[r] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((4 * g4 + r) << 2, __builtin_bit_cast(int, alpha)));
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[db][r] = o[db][r] * al[r];
+#pragma unroll
+    for (int t = 0; t < Cfg::PV; ++t) {
+      // A operand: head c16, keys {32t + 4 g4 + e} (e < 4) and {32t + 16 + 4 g4 + e - 4}
+      u32x4 pa;
+      pa[0] = pw[2 * t][0];
+      pa[1] = pw[2 * t][1];
+      pa[2] = pw[2 * t + 1][0];
+      pa[3] = pw[2 * t + 1][1];
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, pa);
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const uint16_t* vrow = vt + (db * 16 + c16) * Cfg::VT + 32 * t + 4 * g4;
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
+        u32x4 vb;
+        vb[0] = lo.x;
+        vb[1] = lo.y;
+        vb[2] = hi.x;
+        vb[3] = hi.y;
+        o[db] = mfma16(pf, __builtin_bit_cast(bf16x8, vb), o[db]);
+      }
+    }
+    __syncthreads();  // vt is rewritten by the next chunk
+  }
+
+  // ---- split state: o (rows = heads 4 g4 + r, col d = 16 db + c16), m, l (head c16)
+  float* ws = a.ws;
+  const int64_t hbase = row * a.Hq + (int64_t)kvh * grp;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int h = 4 * g4 + r;
+    if (h < grp) {
+      float* st = ws + ((hbase + h) * S + j) * (kD + 2);
+#pragma unroll
+      for (int db = 0; db < 8; ++db) st[db * 16 + c16] = o[db][r];
+    }
+  }
+  if (g4 == 0 && c16 < grp) {
+    float* st = ws + ((hbase + c16) * S + j) * (kD + 2);
+    st[kD] = m_run;
+    st[kD + 1] = l_run;
+  }
+}
+
+struct AttnState {
+  float m, l, o0, o1;
+};
+
+__device__ __forceinline__ AttnState attn_merge(const AttnState& a, const AttnState& b) {
+  const float m = fmaxf(a.m, b.m);
+  if (m == -INFINITY) return a;
+  const float fa = exp_shifted(a.m, m);
+  const float fb = exp_shifted(b.m, m);
+  AttnState r;
+  r.m = m;
+  r.l = a.l * fa + b.l * fb;
+  r.o0 = a.o0 * fa + b.o0 * fb;
+  r.o1 = a.o1 * fa + b.o1 * fb;
+  return r;
+}
+
+// One wave per (row, head); lane owns d = lane and lane + 64.
+template <int S, bool FOLD>
+__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ ws, uint16_t* __restrict__ out,
+                                                           int64_t rows_heads) {
+  const int64_t rh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (rh >= rows_heads) return;
+  const int lane = threadIdx.x & 63;
+  const float* base = ws + rh * S * (kD + 2);
+  AttnState st[S];
+#pragma unroll
+  for (int j = 0; j < S; ++j) {
+    const float* p = base + j * (kD + 2);
+    st[j] = AttnState{p[kD], p[kD + 1], p[lane], p[lane + 64]};
+  }
+  AttnState r;
+  if constexpr (FOLD) {
+    r = st[0];
+#pragma unroll
+    for (int j = 1; j < S; ++j) r = attn_merge(r, st[j]);
+  } else {
+#pragma unroll
+    for (int w = S; w > 1; w /= 2)
+#pragma unroll
+      for (int j = 0; j < w / 2; ++j) st[j] = attn_merge(st[2 * j], st[2 * j + 1]);
+    r = st[0];
+  }
+  out[rh * kD + lane] = f32_to_bf16_bits(r.o0 / r.l);
+  out[rh * kD + lane + 64] = f32_to_bf16_bits(r.o1 / r.l);
+}
+
+template <int S>
+hipError_t combine_s(const float* ws, void* out, int64_t rh, bool fold, hipStream_t s) {
+  dim3 grid((unsigned)((rh + 3) / 4));
+  auto O = static_cast<uint16_t*>(out);
+  if (fold) hipLaunchKernelGGL((attn_combine_kernel<S, true>), grid, dim3(256), 0, s, ws, O, rh);
+  else hipLaunchKernelGGL((attn_combine_kernel<S, false>), grid, dim3(256), 0, s, ws, O, rh);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_splits(const AttnLaunch& a, hipStream_t s) {
+  const float scale = 1.0f / __builtin_sqrtf((float)a.D);
+  const int64_t wgs = a.Tq * a.Hkv * (int64_t)(a.split_hi - a.split_lo);
+  if (wgs <= 0) return hipSuccess;
+  dim3 grid((unsigned)wgs), block(64);
+  switch (a.kv_chunk) {
+    case 32: hipLaunchKernelGGL(attn_split_kernel<32>, grid, block, 0, s, a, scale); break;
+    case 64: hipLaunchKernelGGL(attn_split_kernel<64>, grid, block, 0, s, a, scale); break;
+    case 128: hipLaunchKernelGGL(attn_split_kernel<128>, grid, block, 0, s, a, scale); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_combine(const float* ws, void* out, int64_t Tq, int Hq, int D, int split_kv, bool left_fold,
+                               hipStream_t s) {
+  (void)D;
+  const int64_t rh = Tq * Hq;
+  if (rh <= 0) return hipSuccess;
+  switch (split_kv) {
+    case 1: return combine_s<1>(ws, out, rh, left_fold, s);
+    case 2: return combine_s<2>(ws, out, rh, left_fold, s);
+    case 4: return combine_s<4>(ws, out, rh, left_fold, s);
+    case 8: return combine_s<8>(ws, out, rh, left_fold, s);
+    case 16: return combine_s<16>(ws, out, rh, left_fold, s);
+    case 32: return combine_s<32>(ws, out, rh, left_fold, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace inv

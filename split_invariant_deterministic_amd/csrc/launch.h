@@ -1,0 +1,81 @@
+// Internal launcher interface between the C-ABI layer (api.cpp) and the HIP
+// kernels. Arguments here are already validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace inv {
+
+// ---- GEMM -----------------------------------------------------------------
+// One launch reduces, for every output element, `groups` independent balanced
+// subtrees of `nl` consecutive leaves each: group z covers leaves
+// [leaf_lo + z*nl, leaf_lo + (z+1)*nl) and writes C + z*c_group_stride.
+struct GemmLaunch {
+  const void* A;           // [rows, K] bf16
+  const void* B;           // [N, K] bf16 (grouped: [E, N, K])
+  void* C;                 // [M, N] out dtype (per group)
+  int64_t M, N, K;
+  int64_t c_group_stride;  // elements between groups' outputs
+  int kl;                  // leaf length (multiple of 32)
+  int leaf_lo;             // first leaf of group 0
+  int nl;                  // leaves per group (power of two, <= 8)
+  int groups;              // number of groups (grid z)
+  bool out_bf16;           // else fp32
+  // grouped (MoE) mode: offsets != nullptr
+  const int32_t* rows;     // gather of A rows (nullable)
+  const int32_t* offsets;  // [E+1] grouped row ranges per expert
+  int E;
+  int64_t a_rows;          // rows of A (gathered indices outside [0, a_rows) read as zero rows)
+  int64_t b_expert_stride; // elements between experts' B
+};
+hipError_t launch_gemm(const GemmLaunch& g, hipStream_t s);
+
+// C = cast(tree(P[0..count-1])), P [count, plane] fp32.
+hipError_t launch_tree_combine(const float* P, int count, int64_t plane, void* C, bool out_bf16,
+                               bool left_fold, hipStream_t s);
+
+hipError_t launch_cast_bf16(const float* x, uint16_t* y, int64_t n, hipStream_t s);
+
+// ---- RMSNorm ----------------------------------------------------------------
+hipError_t launch_rmsnorm(const void* x, const void* gamma, void* y, int64_t M, int64_t H,
+                          float eps, hipStream_t s);
+
+// ---- logprob ----------------------------------------------------------------
+// mode 0: full logprob -> out; mode 1: partial stats for chunks [lo, hi).
+hipError_t launch_logprob(const float* logits, int64_t ldl, const int32_t* target, float* out,
+                          float* stats, float* tlogit, int64_t M, int64_t V, int C, int chunk_lo,
+                          int chunk_hi, bool left_fold, bool partial, hipStream_t s);
+hipError_t launch_logprob_combine(const float* stats, const float* tlogit, const int32_t* target,
+                                  float* out, int64_t M, int64_t V, int C, bool left_fold,
+                                  hipStream_t s);
+
+// ---- attention --------------------------------------------------------------
+struct AttnLaunch {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* cu_seqlens;
+  const int32_t* q_seq;
+  const int32_t* q_pos;
+  int64_t Tq;
+  int Hq, Hkv, D;
+  int num_seqs;
+  int split_kv, kv_chunk;
+  int split_lo, split_hi;
+  float* ws;  // [Tq, Hq, split_kv, D+2]
+};
+hipError_t launch_attn_splits(const AttnLaunch& a, hipStream_t s);
+hipError_t launch_attn_combine(const float* ws, void* out, int64_t Tq, int Hq, int D, int split_kv,
+                               bool left_fold, hipStream_t s);
+
+// ---- MoE --------------------------------------------------------------------
+hipError_t launch_moe_route(const float* logits, int32_t* ids, float* w, int64_t T, int E, int k,
+                            hipStream_t s);
+hipError_t launch_moe_permute(const int32_t* ids, int32_t* offsets, int32_t* rows, int32_t* slot,
+                              int64_t T, int E, int k, hipStream_t s);
+hipError_t launch_swiglu(const void* gu, void* a, int64_t R, int64_t F, hipStream_t s);
+hipError_t launch_moe_combine(const float* Y, const float* w, const int32_t* slot, int64_t y_rows,
+                              void* out, int64_t T, int64_t H, int k, bool left_fold, hipStream_t s);
+
+}  // namespace inv

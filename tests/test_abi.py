@@ -1,0 +1,141 @@
+"""Host-side tests of the C-ABI library (no GPU, no kernel launch).
+
+The library loads without a GPU; every symbol that include/inv.h declares is
+exported; contract and shape validation runs on the host before any HIP call
+and returns the documented status (the IsoExec blog, "Unified execution
+contract": a parallel size without a proven-invariance claim is rejected).
+Only calls that fail validation or that are empty are made, so nothing is
+ever enqueued.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "split_invariant_deterministic_amd", "libinv.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libinv.so not built")
+
+
+def _inv():
+    from split_invariant_deterministic_amd import inv
+    return inv
+
+
+def declared_symbols():
+    txt = open(os.path.join(ROOT, "include", "inv.h")).read()
+    return sorted(set(re.findall(r"^(?:inv_status|size_t|const char\*)\s+(inv_\w+)\s*\(", txt, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(LIB)
+    decl = declared_symbols()
+    assert len(decl) >= 20
+    for name in decl:
+        assert hasattr(lib, name), name
+    assert sorted(_inv().EXPORTS) == decl
+
+
+def test_contract_defaults():
+    c = _inv().contract()
+    assert (c.leaves, c.ranks, c.split_kv, c.kv_chunk) == (8, 1, 16, 64)
+    assert abs(c.eps - 1e-6) < 1e-12
+    assert c.struct_size == ctypes.sizeof(c) == 48
+
+
+@pytest.mark.parametrize("ranks,status", [(1, 0), (2, 0), (4, 0), (8, 0), (3, 3), (5, 3), (6, 3), (16, 3)])
+def test_rank_claims(ranks, status):
+    inv = _inv()
+    c = inv.contract(leaves=8, ranks=ranks)
+    assert inv.contract_check(c, inv.OP_GEMM, 4096) == status
+
+
+def test_contract_violations():
+    inv = _inv()
+    assert inv.contract_check(inv.contract(leaves=8), inv.OP_GEMM, 4096 + 8) == inv.E_CONTRACT  # K % L
+    assert inv.contract_check(inv.contract(leaves=8), inv.OP_GEMM, 8 * 48) == inv.E_CONTRACT    # leaf % 32
+    assert inv.contract_check(inv.contract(leaves=6), inv.OP_GEMM, 6 * 64) == inv.E_CONTRACT    # not 2^n
+    assert inv.contract_check(inv.contract(leaves=16), inv.OP_GEMM, 16 * 64) == inv.E_UNSUPPORTED
+    assert inv.contract_check(inv.contract(accum="bf16"), inv.OP_GEMM, 4096) == inv.E_CONTRACT
+    assert inv.contract_check(inv.contract(leaf="bf16"), inv.OP_GEMM, 4096) == inv.E_CONTRACT
+    assert inv.contract_check(inv.contract(tree="left_fold"), inv.OP_GEMM, 4096) == inv.E_CONTRACT
+    assert inv.contract_check(inv.contract(tree="left_fold"), inv.OP_LOGPROB) == inv.OK
+    assert inv.contract_check(inv.contract(split_kv=12), inv.OP_DECODE_ATTN) == inv.E_CONTRACT
+    assert inv.contract_check(inv.contract(kv_chunk=48), inv.OP_DECODE_ATTN) == inv.E_CONTRACT
+    assert inv.contract_check(inv.contract(eps=float("nan")), inv.OP_RMSNORM) == inv.E_CONTRACT
+    c = inv.contract()
+    c.struct_size = 40
+    assert inv.contract_check(c, inv.OP_GEMM, 4096) == inv.E_ARG
+    c = inv.contract()
+    c.reserved = 1
+    assert inv.contract_check(c, inv.OP_GEMM, 4096) == inv.E_ARG
+
+
+def test_workspace_sizes():
+    inv = _inv()
+    assert inv.workspace_bytes(inv.contract(ranks=1), inv.OP_GEMM, 64, 128, 4096) == 0
+    assert inv.workspace_bytes(inv.contract(ranks=4), inv.OP_GEMM, 64, 128, 4096) == 4 * 64 * 128 * 4
+    assert inv.workspace_bytes(inv.contract(), inv.OP_DECODE_ATTN, 3, 32, 128) == 3 * 32 * 16 * 130 * 4
+    assert inv.workspace_bytes(inv.contract(ranks=3), inv.OP_GEMM, 64, 128, 4096) == ctypes.c_size_t(-1).value
+
+
+def test_entry_points_reject_before_any_launch():
+    inv = _inv()
+    lib = inv._lib
+    c = inv.contract(ranks=3)
+    null = ctypes.c_void_p(0)
+    by = ctypes.byref
+    assert lib.inv_gemm(by(c), null, null, null, 4, 4, 4096, null, 0, null) == inv.E_TOPOLOGY
+    c = inv.contract()
+    assert lib.inv_gemm(by(c), null, null, null, 4, 4, 4096, null, 0, null) == inv.E_ARG  # null operands
+    assert lib.inv_gemm(by(c), null, null, null, -1, 4, 4096, null, 0, null) == inv.E_ARG
+    assert lib.inv_gemm(by(c), null, null, null, 0, 4, 4096, null, 0, null) == inv.OK     # empty: no launch
+    c2 = inv.contract(ranks=2)
+    # ranks > 1 without workspace: rejected (misaligned pointers are caught first, so use aligned fakes)
+    fake = ctypes.c_void_p(1 << 20)
+    assert lib.inv_gemm(by(c2), fake, fake, fake, 4, 4, 4096, null, 0, null) == inv.E_WORKSPACE
+    assert lib.inv_gemm_leaves(by(c), fake, fake, fake, 4, 4, 4096, 3, 3, null) == inv.E_ARG
+    assert lib.inv_gemm_leaves(by(c), fake, fake, fake, 4, 4, 4096, 0, 9, null) == inv.E_ARG
+    assert lib.inv_gemm_rank(by(c2), fake, fake, fake, 4, 4, 4096, 2, null) == inv.E_ARG
+    assert lib.inv_tree_combine(by(c), fake, 3, fake, 4, 4, null) == inv.E_UNSUPPORTED
+    assert lib.inv_rmsnorm(by(c), fake, fake, fake, 4, 12, null) == inv.E_UNSUPPORTED
+    assert lib.inv_rmsnorm(by(c), fake, fake, fake, 4, 16392, null) == inv.E_UNSUPPORTED
+    assert lib.inv_rmsnorm(by(c), null, null, null, 0, 4096, null) == inv.OK
+    clp = inv.contract(leaves=64)
+    assert lib.inv_logprob(by(clp), fake, 10, fake, fake, 4, 32, null) == inv.E_CONTRACT      # C > V
+    assert lib.inv_logprob(by(clp), fake, 10, fake, fake, 4, 100, null) == inv.E_ARG          # ldl < V
+    assert lib.inv_logprob(by(inv.contract(leaves=1024)), fake, 4096, fake, fake, 4, 4096, null) \
+        == inv.E_UNSUPPORTED
+    ca = inv.contract()
+    assert lib.inv_decode_attn(by(ca), fake, fake, fake, fake, 1, fake, fake, fake, 1, 32, 8, 64, fake,
+                               1 << 30, null) == inv.E_UNSUPPORTED                              # D != 128
+    assert lib.inv_decode_attn(by(ca), fake, fake, fake, fake, 1, fake, fake, fake, 1, 32, 6, 128, fake,
+                               1 << 30, null) == inv.E_UNSUPPORTED                              # Hq % Hkv
+    assert lib.inv_decode_attn(by(ca), fake, fake, fake, fake, 1, fake, fake, fake, 1, 32, 8, 128, fake,
+                               16, null) == inv.E_WORKSPACE
+    assert lib.inv_attn_splits(by(ca), fake, fake, fake, fake, 1, fake, fake, 1, 32, 8, 128, 4, 4, fake,
+                               1 << 30, null) == inv.E_ARG
+    cm = inv.contract(leaves=8)
+    assert lib.inv_moe_route(by(cm), fake, fake, fake, 4, 300, null) == inv.E_UNSUPPORTED
+    assert lib.inv_moe_route(by(cm), fake, fake, fake, 4, 4, null) == inv.E_UNSUPPORTED      # k > E
+    assert lib.inv_moe_gemm(by(inv.contract(ranks=2)), fake, 4, fake, fake, fake, fake, 4, 2, 64, 4096,
+                            null) == inv.E_TOPOLOGY
+    assert lib.inv_moe_combine(by(cm), null, null, null, 0, null, 0, 2048, null) == inv.OK
+
+
+def test_status_strings():
+    inv = _inv()
+    for s in range(7):
+        assert inv._lib.inv_status_string(s)
+    assert inv._lib.inv_status_string(99) == b"unknown status"
+
+
+def test_no_atomics_in_kernels():
+    """Atomics make accumulation order depend on scheduling ([VeXact] section 3.1)."""
+    csrc = os.path.join(ROOT, "split_invariant_deterministic_amd", "csrc")
+    for f in os.listdir(csrc):
+        txt = open(os.path.join(csrc, f)).read()
+        assert not re.search(r"\batomic\w*\s*\(", txt, re.I), f

@@ -1,0 +1,180 @@
+"""MoE layer on the GPU: routing, grouping, expert FFN and the fixed-order
+combine; oracle parity per stage and bitwise invariance across token splits.
+
+IsoExec blog, "Unified model": deterministic routing and combination;
+"Parallelism-invariant kernels": expert outputs combined in a fixed routing
+order, not rank order; "Unified execution contract": moe.combine as a tree of
+8 fp32 leaves. RL-Kernel write-up, sections 6-7: packed gate/up GEMM, SwiGLU,
+down GEMM as separate stages.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe as omoe
+from oracle import numerics
+from split_invariant_deterministic_amd import synth
+from tests.helpers import bitwise_equal, check_bf16, check_fp32_gemm, mismatch_report
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def inv():
+    from split_invariant_deterministic_amd import inv as m
+    return m
+
+
+def _np(t):
+    return t.float().cpu().numpy()
+
+
+def test_route_against_oracle(inv):
+    logits = synth.randn((300, 128), 5, dtype=torch.float32)
+    ids, w = inv.moe_route(logits.to(DEV), inv.contract(leaves=8))
+    oid, ow = omoe.route(logits.double().numpy(), 8)
+    assert np.array_equal(ids.cpu().numpy(), oid)
+    assert np.allclose(w.cpu().numpy(), ow, rtol=1e-6, atol=0)
+
+
+def test_route_ties_go_to_lower_ids(inv):
+    x = torch.zeros((3, 16))
+    x[1, [3, 9, 12]] = 5.0
+    x[1, [0, 1, 2, 4]] = 1.0
+    x[2] = torch.arange(16, dtype=torch.float32) * 0  # all equal
+    ids, w = inv.moe_route(x.to(DEV), inv.contract(leaves=4))
+    oid, ow = omoe.route(x.double().numpy(), 4)
+    assert np.array_equal(ids.cpu().numpy(), oid)
+    assert torch.all(w[0] == 0.25) and torch.all(w[2] == 0.25)
+    ids5, _ = inv.moe_route(x[1:2].to(DEV), inv.contract(leaves=2))
+    assert ids5.cpu().tolist() == [[3, 9]]
+
+
+def test_route_nan_rows_are_marked(inv):
+    x = torch.randn((2, 16), generator=torch.Generator().manual_seed(1))
+    x[0, :13] = float("nan")   # only 3 selectable experts for k = 4
+    ids, w = inv.moe_route(x.to(DEV), inv.contract(leaves=4))
+    assert (ids[0] == -1).sum().item() == 1 and torch.isnan(w[0]).any()
+    assert (ids[1] >= 0).all() and not torch.isnan(w[1]).any()
+
+
+def _grouping(ids, E):
+    k = ids.shape[1]
+    flat = ids.reshape(-1)
+    order = np.argsort(flat, kind="stable")
+    counts = np.bincount(flat, minlength=E)
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    slot = np.empty_like(flat)
+    slot[order] = np.arange(len(flat))
+    return offsets, order // k, slot.reshape(ids.shape)
+
+
+def test_permute_is_the_stable_grouping(inv):
+    logits = synth.randn((1000, 128), 6, dtype=torch.float32)
+    c = inv.contract(leaves=8)
+    ids, _ = inv.moe_route(logits.to(DEV), c)
+    offsets, rows, slot = inv.moe_permute(ids, 128, c)
+    o, r, s = _grouping(ids.cpu().numpy(), 128)
+    assert np.array_equal(offsets.cpu().numpy(), o)
+    assert np.array_equal(rows.cpu().numpy(), r)
+    assert np.array_equal(slot.cpu().numpy(), s)
+
+
+class _Experts:
+    """Lazy float64 view of a bf16 expert tensor: converts one expert at a time."""
+
+    def __init__(self, W):
+        self.W = W
+        self.shape = tuple(W.shape)
+
+    def __getitem__(self, e):
+        return self.W[int(e)].float().cpu().numpy().astype(np.float64)
+
+
+@pytest.fixture(scope="module")
+def moe_full():
+    return synth.moe(T=8192, seed=0, device=DEV)
+
+
+def test_moe_stages_against_oracle(inv, moe_full):
+    d = moe_full
+    T = 96
+    x, logits = d["x"][:T].contiguous(), d["logits"][:T].contiguous()
+    cg, cr = inv.contract(leaves=8), inv.contract(leaves=8)
+    st = {}
+    out = inv.moe_layer(x, logits, d["W1"], d["W2"], cg, cr, out_stage=st)
+    xn = _np(x).astype(np.float64)
+    ids = st["ids"].cpu().numpy()
+    oid, ow = omoe.route(logits.double().cpu().numpy(), 8)
+    assert np.array_equal(ids, oid)
+    rows = st["rows"].cpu().numpy()
+    offs = st["offsets"].cpu().numpy()
+    W1, W2 = _Experts(d["W1"]), _Experts(d["W2"])
+    GU, A, Y = _np(st["GU"]), _np(st["A"]), st["Y"].cpu().numpy()
+    for e in np.unique(ids):
+        r0, r1 = offs[e], offs[e + 1]
+        # each stage consumes the GPU's previous stage (stage-wise parity)
+        check_bf16(GU[r0:r1], omoe.gate_up(xn[rows[r0:r1]], W1[e]), f"gate/up e={e}")
+        check_bf16(A[r0:r1], omoe.swiglu(GU[r0:r1]), f"swiglu e={e}")
+        check_fp32_gemm(Y[r0:r1], omoe.down(A[r0:r1], W2[e]), f"down e={e}")
+    # the combine replays bit for bit from the GPU's Y and weights
+    slot = st["slot"].cpu().numpy()
+    ref = omoe.combine(Y[slot], st["w"].cpu().numpy())
+    assert np.array_equal(_np(out), ref.astype(np.float32))
+    # free-running chain (information bar: 1 ulp may cascade, so normwise only)
+    full, _, _ = omoe.moe_layer(xn, logits.double().cpu().numpy(), W1, W2, 8)
+    rel = np.linalg.norm(_np(out) - full) / np.linalg.norm(full)
+    assert rel < 2e-2
+
+
+def test_moe_token_splits_are_bitwise_equal(inv, moe_full):
+    d = moe_full
+    c = inv.contract(leaves=8)
+    full = inv.moe_layer(d["x"], d["logits"], d["W1"], d["W2"], c, c)
+    for S in (4, 16):
+        n = 8192 // S
+        parts = [inv.moe_layer(d["x"][i * n:(i + 1) * n].contiguous(), d["logits"][i * n:(i + 1) * n].contiguous(),
+                               d["W1"], d["W2"], c, c) for i in range(S)]
+        cnt, bad, dmax = mismatch_report(torch.cat(parts), full)
+        assert bad == 0, f"split {S}: {bad}/{cnt}, max {dmax}"
+    one = inv.moe_layer(d["x"][4000:4001].contiguous(), d["logits"][4000:4001].contiguous(), d["W1"], d["W2"], c, c)
+    assert bitwise_equal(one[0], full[4000])
+
+
+def test_identical_experts_equal_one_expert(inv):
+    """Eight identical experts with equal logits: w = 1/8 exactly and the
+    combine returns the single expert's FFN output (oracle pin, GPU side)."""
+    T, H, F, E = 40, 256, 256, 16
+    x = synth.randn((T, H), 21).to(DEV)
+    W1e = synth.randn((2 * F, H), 22, 0.05).to(DEV)
+    W2e = synth.randn((H, F), 23, 0.05).to(DEV)
+    W1 = W1e.unsqueeze(0).expand(E, 2 * F, H).contiguous()
+    W2 = W2e.unsqueeze(0).expand(E, H, F).contiguous()
+    c = inv.contract(leaves=8)
+    st = {}
+    out = inv.moe_layer(x, torch.zeros((T, E), device=DEV), W1, W2, c, c, out_stage=st)
+    assert torch.all(st["w"] == 0.125)
+    g = inv.gemm(x, W1e, inv.contract(leaves=8))
+    a = inv.swiglu(g, c)
+    y = inv.gemm(a, W2e, inv.contract(leaves=8, out="fp32"))
+    assert bitwise_equal(out, inv.cast_bf16(y))
+
+
+def test_grouped_gemm_rows_equal_plain_gemm(inv, moe_full):
+    """A grouped row is bitwise what the plain K-leaf GEMM gives for it alone."""
+    d = moe_full
+    c = inv.contract(leaves=8)
+    T = 512
+    ids, w = inv.moe_route(d["logits"][:T].contiguous(), c)
+    offsets, rows, slot = inv.moe_permute(ids, 128, c)
+    GU = inv.moe_gemm(d["x"], rows, offsets, d["W1"], T * 8, c)
+    offs = offsets.cpu().numpy()
+    for e in (0, 5, 127):
+        r0, r1 = int(offs[e]), int(offs[e + 1])
+        if r1 == r0:
+            continue
+        ref = inv.gemm(d["x"][rows[r0:r1].long()].contiguous(), d["W1"][e], c)
+        assert bitwise_equal(GU[r0:r1], ref), e
