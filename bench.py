@@ -71,24 +71,32 @@ class Timer:
         self.ev = {}
 
 
-def cpu_baseline(dense_X, W_up, W_down, rows=256):
-    """The oracle's 8-leaf GEMM schedule on a bounded row sample of both
-    dense projections (TFLOP/s of useful GEMM work, same unit as value)."""
+def cpu_baseline(dense_X, W_up, W_down, target_s=15.0):
+    """The oracle's 8-leaf GEMM schedule on a bounded row sample of both dense
+    projections (TFLOP/s of useful GEMM work, the unit of ``value``). A 32-row
+    probe sizes the sample to about ``target_s`` seconds of host work."""
     from threadpoolctl import threadpool_info
 
     from oracle import gemm as ogemm
-    X = dense_X[:rows].float().cpu().numpy()
     Wu = W_up.float().cpu().numpy()
     Wd = W_down.float().cpu().numpy()
-    t0 = time.perf_counter()
-    y = ogemm.gemm_tree(X, Wu, 8, "bf16")
-    ogemm.gemm_tree(y, Wd, 8, "bf16")
-    dt = time.perf_counter() - t0
+
+    def run(rows):
+        X = dense_X[:rows].float().cpu().numpy()
+        t0 = time.perf_counter()
+        y = ogemm.gemm_tree(X, Wu, 8, "bf16")
+        ogemm.gemm_tree(y, Wd, 8, "bf16")
+        return time.perf_counter() - t0
+
+    probe = run(32)
+    rows = int(max(32, min(dense_X.shape[0], 32 * target_s / max(probe, 1e-3))))
+    rows -= rows % 32
+    dt = run(rows)
     flops = 2.0 * rows * (W_up.shape[0] * W_up.shape[1] + W_down.shape[0] * W_down.shape[1])
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{rows} of 4096 token rows through both dense projections (4096->12288->4096), "
-                      f"8-leaf fp32 tree schedule with float64 leaf sums; {dt:.1f} s"}
+    return {"value": round(flops / dt / 1e12, 4), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} of {dense_X.shape[0]} token rows through both dense projections "
+                      f"(4096->12288->4096), 8-leaf fp32 tree schedule with float64 leaf sums, {dt:.1f} s"}
 
 
 def log(msg):

@@ -242,8 +242,9 @@ inv_status inv_logprob_combine(const inv_contract* c, const float* stats, const 
  * position 0, n = ceil(L/kv_chunk); split j (of S = split_kv) owns chunks
  * [floor(j*n/S), floor((j+1)*n/S)), processed in ascending order with an
  * online-softmax update per chunk: scores = (q.k) * (1/sqrt(D)) in fp32,
- * p = exp2((score - m) * log2e) rounded to bf16, row sum and P.V taken from the
- * same bf16 p. Empty splits are the identity (m = -inf, l = 0, o = 0).
+ * p = exp2((score - m) * log2e) split into bf16 parts p_hi = bf16(p) and
+ * p_lo = bf16(p - p_hi), row sum and P.V taken from the same p_hi + p_lo
+ * (two chained MFMAs per step, high part first). Empty splits are the identity (m = -inf, l = 0, o = 0).
  * The S split states are merged by the contract's tree (o scaled like l) and
  * out = bf16(o / l). Every row's bits depend only on its own q, its visible
  * keys and L, so a decode row equals the same position's prefill row.

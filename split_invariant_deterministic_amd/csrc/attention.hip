@@ -13,11 +13,13 @@
 //     s     = (q . k) * (1/sqrt(D))      q.k: 4 chained MFMAs over d from +0
 //     m'    = max(m, max_chunk s)
 //     alpha = exp2((m - m') * log2e)
-//     p     = bf16( exp2((s - m') * log2e) ), masked keys give 0
-//     l'    = l * alpha + sum_chunk p   (lane sums in (block, row) order,
-//                                        then xor 16, 32)
+//     p     = exp2((s - m') * log2e), masked keys give 0, split into two
+//             bf16 parts p_hi = bf16(p), p_lo = bf16(p - p_hi) so that the
+//             P.V MFMAs see p to about 16 bits instead of bf16's 8
+//     l'    = l * alpha + sum_chunk (p_hi + p_lo)  (lane sums in (block,
+//                                        row) order, then xor 16, 32)
 //     o'    = MFMA chain of P.V over the chunk's 32-key steps, started from
-//             o * alpha
+//             o * alpha; per step the p_hi MFMA, then the p_lo MFMA
 //   empty splits are (m, l, o) = (-inf, 0, 0).
 // The S split states are then merged by the contract's tree with
 // m = max(m1,m2), l = l1 f1 + l2 f2, o = o1 f1 + o2 f2 (f = exp2((m_i - m)
@@ -37,7 +39,6 @@ namespace inv {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kVtStride = 0;  // unused marker (stride below is per CH)
 
 template <int CH>
 struct AttnCfg {
@@ -63,9 +64,30 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a, float scal
   const int grp = a.Hq / a.Hkv;
   const int S = a.split_kv;
 
+  // Row indices come from device memory: a sequence id outside [0, num_seqs)
+  // or a position outside that sequence makes the row's state NaN (the
+  // combine then returns NaN) instead of reading outside the key buffers.
   const int seq = a.q_seq[row];
-  const int64_t start = a.cu_seqlens[seq];
-  const int64_t L = (int64_t)a.q_pos[row] + 1;
+  bool valid = seq >= 0 && seq < a.num_seqs;
+  int64_t start = 0, L = 1;
+  if (valid) {
+    start = a.cu_seqlens[seq];
+    const int64_t len = (int64_t)a.cu_seqlens[seq + 1] - start;
+    const int64_t p = a.q_pos[row];
+    valid = p >= 0 && p < len;
+    L = p + 1;
+  }
+  if (!valid) {  // uniform over the block (one wave, one row)
+    float* ws = a.ws;
+    const int64_t hb = row * a.Hq + (int64_t)kvh * grp;
+    for (int h = 0; h < grp; ++h) {
+      float* st = ws + ((hb + h) * S + j) * (kD + 2);
+      st[lane] = __builtin_nanf("");
+      st[lane + 64] = __builtin_nanf("");
+      if (lane < 2) st[kD + lane] = __builtin_nanf("");
+    }
+    return;
+  }
   const int64_t n = (L + CH - 1) / CH;
   const int64_t c0 = ((int64_t)j * n) / S, c1 = ((int64_t)(j + 1) * n) / S;
 
@@ -143,18 +165,22 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a, float scal
     const float m_new = fmaxf(m_run, cmax);
     const float alpha = exp_shifted(m_run, m_new);
     float psum = 0.0f;
-    uint32_t pw[Cfg::KB][2];  // bf16 p, packed pairs
+    uint32_t pw[Cfg::KB][2];  // bf16 high parts of p, packed pairs
+    uint32_t pl[Cfg::KB][2];  // bf16 low parts: p - high, rounded
 #pragma unroll
     for (int kb = 0; kb < Cfg::KB; ++kb) {
-      float pb[4];
+      float ph[4], plo[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float p = exp_shifted(st[kb][r], m_new);
-        pb[r] = bf16_bits_to_f32(f32_to_bf16_bits(p));
-        psum = psum + pb[r];
+        ph[r] = bf16_bits_to_f32(f32_to_bf16_bits(p));
+        plo[r] = bf16_bits_to_f32(f32_to_bf16_bits(p - ph[r]));  // p - ph is exact in fp32
+        psum = psum + (ph[r] + plo[r]);                          // exact: at most 16 significant bits
       }
-      pw[kb][0] = pack_bf16x2(pb[0], pb[1]);
-      pw[kb][1] = pack_bf16x2(pb[2], pb[3]);
+      pw[kb][0] = pack_bf16x2(ph[0], ph[1]);
+      pw[kb][1] = pack_bf16x2(ph[2], ph[3]);
+      pl[kb][0] = pack_bf16x2(plo[0], plo[1]);
+      pl[kb][1] = pack_bf16x2(plo[2], plo[3]);
     }
     psum = psum + shfl_xor(psum, 16);
     psum = psum + shfl_xor(psum, 32);
@@ -185,12 +211,17 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a, float scal
 #pragma unroll
     for (int t = 0; t < Cfg::PV; ++t) {
       // A operand: head c16, keys {32t + 4 g4 + e} (e < 4) and {32t + 16 + 4 g4 + e - 4}
-      u32x4 pa;
+      u32x4 pa, pb;
       pa[0] = pw[2 * t][0];
       pa[1] = pw[2 * t][1];
       pa[2] = pw[2 * t + 1][0];
       pa[3] = pw[2 * t + 1][1];
+      pb[0] = pl[2 * t][0];
+      pb[1] = pl[2 * t][1];
+      pb[2] = pl[2 * t + 1][0];
+      pb[3] = pl[2 * t + 1][1];
       const bf16x8 pf = __builtin_bit_cast(bf16x8, pa);
+      const bf16x8 pfl = __builtin_bit_cast(bf16x8, pb);
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
         const uint16_t* vrow = vt + (db * 16 + c16) * Cfg::VT + 32 * t + 4 * g4;
@@ -201,7 +232,9 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a, float scal
         vb[1] = lo.y;
         vb[2] = hi.x;
         vb[3] = hi.y;
-        o[db] = mfma16(pf, __builtin_bit_cast(bf16x8, vb), o[db]);
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, vb);
+        o[db] = mfma16(pf, vf, o[db]);   // high parts first,
+        o[db] = mfma16(pfl, vf, o[db]);  // then the low parts, in this fixed order
       }
     }
     __syncthreads();  // vt is rewritten by the next chunk

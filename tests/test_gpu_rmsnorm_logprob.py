@@ -88,7 +88,8 @@ def test_logprob_against_oracle(inv, M, V, C):
     x = _rand_logits(M, V, V)
     t = torch.randint(0, V, (M,), generator=torch.Generator().manual_seed(C)).to(torch.int32)
     lp = inv.logprob(x.to(DEV), t.to(DEV), inv.contract(leaves=C))
-    check_logprob(lp, olp.logprob(x.double().numpy(), t.numpy()), f"{M}x{V}/{C}")
+    xd = x.double().numpy()
+    check_logprob(lp, olp.logprob(xd, t.numpy()), f"{M}x{V}/{C}", lse=olp.lse(xd))
 
 
 def test_logprob_peaked_logits(inv):
@@ -97,7 +98,8 @@ def test_logprob_peaked_logits(inv):
     t = torch.argmax(x, 1).to(torch.int32)
     t[::2] = torch.randint(0, 151936, (8,), generator=torch.Generator().manual_seed(2)).to(torch.int32)
     lp = inv.logprob(x.to(DEV), t.to(DEV), inv.contract(leaves=64))
-    check_logprob(lp, olp.logprob(x.double().numpy(), t.numpy()), "peaked")
+    xd = x.double().numpy()
+    check_logprob(lp, olp.logprob(xd, t.numpy()), "peaked", lse=olp.lse(xd))
 
 
 def test_logprob_constant_logits(inv):
@@ -144,7 +146,8 @@ def test_logprob_batch_invariance_lm_head_size(inv, lm_logits):
     one = torch.stack([inv.logprob(x[i:i + 1], t[i:i + 1], c)[0] for i in (0, 1000, 4095)])
     assert bitwise_equal(one, full[[0, 1000, 4095]])
     rows = [0, 1, 2047, 4095]
-    check_logprob(full[rows], olp.logprob(x[rows].double().cpu().numpy(), t[rows].cpu().numpy()), "sampled")
+    xr = x[rows].double().cpu().numpy()
+    check_logprob(full[rows], olp.logprob(xr, t[rows].cpu().numpy()), "sampled", lse=olp.lse(xr))
 
 
 def test_logprob_vocab_shards_are_bitwise_equal(inv, lm_logits):
