@@ -61,7 +61,9 @@ def build(verbose=True, jobs=None):
             raise RuntimeError(f"hipcc failed on {src}")
         objs.append(obj)
     tmp = LIB + ".tmp"
-    cmd = ["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    # -z defs: an unresolved symbol (say a kernel stub the compiler failed to
+    # emit) fails the build here instead of the first dlopen on a GPU host
+    cmd = ["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs", "-o", tmp] + objs
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
         raise RuntimeError("link failed:\n" + p.stderr)

@@ -15,9 +15,11 @@
 // kernels are free to choose tiles by M; padding rows are zero-filled.
 //
 // Kernels
-//   gemm_tile_kernel    LDS-staged 2x2-wave tile (128 x 128) for large M; the
-//                       balanced subtree of up to 8 leaves is evaluated in
-//                       registers in post-order (log2(nl)+1 live sets).
+//   gemm_ring_kernel    large M: 128 x 128 tile per workgroup, operands
+//                       through a deep LDS ring filled by direct global->LDS
+//                       loads; the balanced subtree of up to 8 leaves is
+//                       evaluated in registers in post-order (log2(nl)+1
+//                       live accumulator sets).
 //   gemm_stream_kernel  small M (<= 64): each wave owns whole leaves of one
 //                       16FM x 16 tile and streams its K range straight from
 //                       HBM into MFMA fragments; the waves' subtrees are then
@@ -28,8 +30,6 @@
 
 namespace inv {
 namespace {
-
-constexpr int kPad = 40;  // staged row stride in bf16 (32 k + 8 pad: conflict-free b128 reads)
 
 template <int FM, int FN>
 struct AccT {
@@ -82,80 +82,149 @@ struct TileParams {
   int64_t b_expert_stride;
 };
 
-// ---------------------------------------------------------------- tile kernel
+// ---------------------------------------------------------------- ring kernel
+//
+// Large-M kernel. A workgroup of 4 waves owns a 128 x 128 output tile, each
+// wave 64 x 64 (4 x 4 MFMA blocks). Operands stream through a 128 KB LDS ring
+// of NS stages of BK k (BK = 64: 4 stages; BK = 32 for leaves that are an odd
+// multiple of 32: 8 stages), filled by global_load_lds_dwordx4: each wave-wide
+// load writes 64 x 16 bytes contiguously at its LDS base, so a stage is laid
+// out as rows of BK bf16 with no padding, and the 16-byte chunk c of row r is
+// stored at slot c ^ ((r / RPW) % CPR). With that XOR swizzle the 16 lanes
+// that read one MFMA operand block (16 rows, same chunk) hit 16 distinct
+// 16-byte bank groups. Loads run NS-1 stages ahead of the MFMAs; the only
+// waits are an explicit vmcnt/lgkmcnt wait and a plain s_barrier per stage
+// (no fence, so prefetches stay in flight across it).
+//
+// Rows past M and columns past N load a clamped valid row instead of zeros;
+// row m of an MFMA result depends only on row m of A (and column n only on
+// row n of B), so those rows never touch a stored output.
 
-template <int FM, int FN>
-struct TileCtx {
-  static constexpr int BM = 32 * FM, BN = 32 * FN;
-  static constexpr int CHUNKS = (BM + BN) * 4;  // 16-byte chunks per 32-k stage
-  static constexpr int CPT = CHUNKS / 256;
-  using Acc = AccT<FM, FN>;
+template <int BK, int RING = 131072>
+struct Ring {
+  static constexpr int BM = 128, BN = 128;
+  static constexpr int ROWB = BK * 2;          // bytes per staged row
+  static constexpr int CPR = BK / 8;           // 16-byte chunks per row
+  static constexpr int RPW = 16 / CPR;         // rows per 256-byte bank window
+  static constexpr int RPL = 1024 / ROWB;      // rows per wave-wide 1 KB load
+  static constexpr int ABYTES = BM * ROWB, BBYTES = BN * ROWB, STAGE = ABYTES + BBYTES;
+  static constexpr int LA = ABYTES / 4096;     // 1 KB loads per wave per stage (4 waves)
+  static constexpr int LB = BBYTES / 4096;
+  static constexpr int LOADS = LA + LB;
+  static constexpr int NS = RING / STAGE;      // stages in the ring
+  static __device__ __forceinline__ int slot(int r, int c) { return c ^ ((r / RPW) % CPR); }
+  static __device__ __forceinline__ int off(int r, int c) { return r * ROWB + (slot(r, c) << 4); }
+};
 
-  uint16_t* lds;  // [2][(BM+BN) * kPad]
-  const uint16_t* src[CPT];
-  int dst[CPT];
-  u32x4 stage[CPT];
-  int64_t kbase;   // first k of the WG's leaf range
-  int g;           // next stage to compute (global within the range)
-  int total;       // stages in the range
-  int spl;         // stages per leaf
-  int lane, wm, wn;
-
-  __device__ __forceinline__ void gload(int st) {
-    const int64_t k = kbase + (int64_t)st * 32;
-#pragma unroll
-    for (int u = 0; u < CPT; ++u)
-      stage[u] = src[u] ? *reinterpret_cast<const u32x4*>(src[u] + k) : u32x4{0u, 0u, 0u, 0u};
+// s_waitcnt vmcnt(n) lgkmcnt(0) for n = PER * rem, rem <= MAXR (immediate operand)
+template <int PER, int R>
+__device__ __forceinline__ void wait_vm_rem(int rem) {
+  if constexpr (R < 0) {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  } else {
+    if (rem >= R) {
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(PER * R) : "memory");
+    } else {
+      wait_vm_rem<PER, R - 1>(rem);
+    }
   }
-  __device__ __forceinline__ void lstore(int buf) {
-    uint16_t* base = lds + buf * ((BM + BN) * kPad);
+}
+
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int BK, int RING>
+struct RingCtx {
+  using R = Ring<BK, RING>;
+  using Acc = AccT<4, 4>;
+  uint8_t* lds;
+  const uint16_t* asrc[R::LA];
+  const uint16_t* bsrc[R::LB];
+  int64_t kbase;  // first k of the workgroup's leaf range
+  int g;          // next stage to compute
+  int total;      // stages in the range
+  int spl;        // stages per leaf
+  int lane, wave, wm, wn;
+
+  // The direct-to-LDS builtin is compiled in the device pass only: seen by the
+  // host pass it silently suppresses the host launch stubs of the kernel
+  // template's instantiations.
+  __device__ __forceinline__ void issue(int st) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const int64_t k = kbase + (int64_t)st * BK;
+    uint8_t* base = lds + (st % R::NS) * R::STAGE;
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) *reinterpret_cast<u32x4*>(base + dst[u]) = stage[u];
+    for (int u = 0; u < R::LA; ++u)
+      __builtin_amdgcn_global_load_lds(asrc[u] + k, &base[(wave + 4 * u) * 1024], 16, 0, 0);
+#pragma unroll
+    for (int u = 0; u < R::LB; ++u)
+      __builtin_amdgcn_global_load_lds(bsrc[u] + k, &base[R::ABYTES + (wave + 4 * u) * 1024], 16, 0, 0);
+#else
+    (void)st;
+#endif
   }
-  __device__ __forceinline__ void compute(int buf, Acc& acc) {
-    const uint16_t* base = lds + buf * ((BM + BN) * kPad);
-    const int col = 8 * (lane >> 4);
-    bf16x8 af[FM], bfr[FN];
+  __device__ __forceinline__ void compute(int st, Acc& acc) {
+    const uint8_t* base = lds + (st % R::NS) * R::STAGE;
+    const int g4 = lane >> 4, r16 = lane & 15;
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-      af[i] = *reinterpret_cast<const bf16x8*>(base + (wm * 16 * FM + 16 * i + (lane & 15)) * kPad + col);
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      bf16x8 af[4], bfr[4];
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-      bfr[j] = *reinterpret_cast<const bf16x8*>(base + (BM + wn * 16 * FN + 16 * j + (lane & 15)) * kPad + col);
+      for (int i = 0; i < 4; ++i) {
+        const int r = wm * 64 + 16 * i + r16;
+        af[i] = *reinterpret_cast<const bf16x8*>(&base[R::off(r, 4 * ks + g4)]);
+      }
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+      for (int j = 0; j < 4; ++j) {
+        const int r = wn * 64 + 16 * j + r16;
+        bfr[j] = *reinterpret_cast<const bf16x8*>(&base[R::ABYTES + R::off(r, 4 * ks + g4)]);
+      }
 #pragma unroll
-      for (int j = 0; j < FN; ++j) acc.v[i][j] = mfma16(af[i], bfr[j], acc.v[i][j]);
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc.v[i][j] = mfma16(af[i], bfr[j], acc.v[i][j]);
+    }
   }
   // One leaf: acc starts at +0 and takes the leaf's stages in ascending k.
   __device__ __forceinline__ void leaf(Acc& acc) {
     acc_zero(acc);
     for (int s = 0; s < spl; ++s) {
-      const bool more = (g + 1) < total;
-      if (more) gload(g + 1);
-      compute(g & 1, acc);
-      if (more) lstore((g + 1) & 1);
-      __syncthreads();
+      // this thread's loads of stage g are done once at most the loads of
+      // the (up to NS-2) later stages already issued are outstanding
+      wait_vm_rem<R::LOADS, R::NS - 2>(total - 1 - g);
+      block_barrier();  // every wave's stage g is in LDS; stage g-1 reads are done
+      if (g + R::NS - 1 < total) issue(g + R::NS - 1);
+      compute(g, acc);
       ++g;
     }
   }
 };
 
-template <int FM, int FN, int NL, bool OUT_BF16, bool GROUPED>
-__global__ __launch_bounds__(256) void gemm_tile_kernel(TileParams p) {
-  using Ctx = TileCtx<FM, FN>;
-  constexpr int BM = Ctx::BM, BN = Ctx::BN;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (BM + BN) * kPad];
+// With 8 leaves the post-order tree needs four live 64 x 64 accumulator sets
+// per wave, more than the register file holds next to the operands; the
+// finished left half (leaves 0-3) then waits in LDS (64 KB, each lane its
+// own values) while the right half runs in registers, and the ring shrinks
+// to 96 KB. The arithmetic is the same tree.
+template <int NL>
+constexpr int ring_bytes() { return NL == 8 ? 98304 : 131072; }
+
+template <int NL, int BK, bool OUT_BF16, bool GROUPED>
+__global__ __launch_bounds__(256, 1) void gemm_ring_kernel(TileParams p) {
+  constexpr int RING = ring_bytes<NL>();
+  constexpr int SPILL = NL == 8 ? 65536 : 0;
+  using R = Ring<BK, RING>;
+  using Ctx = RingCtx<BK, RING>;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[R::NS * R::STAGE + SPILL];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int64_t n0 = (int64_t)blockIdx.x * BN;
-  int64_t m0, m_end;
+  const int tiles_n = (int)((p.N + R::BN - 1) / R::BN);
+  int64_t m0, m_end, n0;
   const uint16_t* B = p.B;
   if constexpr (GROUPED) {
-    // Tile slot -> (expert, rows): experts own consecutive runs of tiles of
-    // ceil(count_e / BM) each, in expert order.
-    const int t = blockIdx.y;
+    // slot -> (expert, rows): experts own consecutive runs of ceil(count_e / BM)
+    // row tiles, in expert order; every row tile spans all column tiles
+    const int t = (int)(blockIdx.x / tiles_n);
+    n0 = (int64_t)(blockIdx.x % tiles_n) * R::BN;
     int e = 0, tstart = 0;
     int64_t r0 = 0, r1 = 0;
     bool found = false;
@@ -164,7 +233,7 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(TileParams p) {
       // never address rows outside [0, M)
       r0 = min(max((int64_t)p.offsets[e], (int64_t)0), p.M);
       r1 = min(max((int64_t)p.offsets[e + 1], r0), p.M);
-      const int nt = (int)((r1 - r0 + BM - 1) / BM);
+      const int nt = (int)((r1 - r0 + R::BM - 1) / R::BM);
       if (t < tstart + nt) {
         found = true;
         break;
@@ -172,11 +241,26 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(TileParams p) {
       tstart += nt;
     }
     if (!found) return;  // slot past the last tile: uniform exit before any barrier
-    m0 = r0 + (int64_t)(t - tstart) * BM;
+    m0 = r0 + (int64_t)(t - tstart) * R::BM;
     m_end = r1;
     B += (int64_t)e * p.b_expert_stride;
   } else {
-    m0 = (int64_t)blockIdx.y * BM;
+    // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so
+    // give XCD x a contiguous run of tile ids, and walk tile ids in bands
+    // of 4 row tiles so that the workgroups resident on one XCD share A and
+    // B panels in its L2.
+    const int tiles_m = (int)((p.M + R::BM - 1) / R::BM);
+    const int nb = tiles_m * tiles_n;
+    int t = (int)blockIdx.x;
+    if (nb % 8 == 0) t = (t % 8) * (nb / 8) + t / 8;
+    constexpr int GM = 4;
+    const int band = t / (GM * tiles_n);
+    const int rows_in_band = min(GM, tiles_m - band * GM);
+    const int within = t - band * GM * tiles_n;
+    const int tm = band * GM + within % rows_in_band;
+    const int tn = within / rows_in_band;
+    m0 = (int64_t)tm * R::BM;
+    n0 = (int64_t)tn * R::BN;
     m_end = p.M;
   }
   const int z = blockIdx.z;
@@ -185,59 +269,86 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(TileParams p) {
   Ctx c;
   c.lds = lds;
   c.lane = lane;
+  c.wave = wave;
   c.wm = wave >> 1;
   c.wn = wave & 1;
   c.kbase = (int64_t)leaf0 * p.kl;
-  c.spl = p.kl / 32;
+  c.spl = p.kl / BK;
   c.total = c.spl * NL;
   c.g = 0;
 #pragma unroll
-  for (int u = 0; u < Ctx::CPT; ++u) {
-    const int ch = tid + 256 * u;
-    const int cc = ch & 3;
-    if (ch < BM * 4) {
-      const int r = ch >> 2;
-      const int64_t row = m0 + r;
-      const uint16_t* ptr = nullptr;
-      if (row < m_end) {
-        const int64_t arow = (GROUPED && p.rows) ? (int64_t)p.rows[row] : row;
-        if (arow >= 0 && arow < p.a_rows) ptr = p.A + arow * p.K + cc * 8;
+  for (int u = 0; u < R::LA; ++u) {
+    const int r = (wave + 4 * u) * R::RPL + lane / R::CPR;
+    const int chunk = R::slot(r, lane % R::CPR);  // the slot map is its own inverse
+    int64_t row = min(m0 + r, m_end - 1);
+    if constexpr (GROUPED) {
+      if (p.rows) {
+        const int64_t gr = p.rows[row];
+        row = (gr >= 0 && gr < p.a_rows) ? gr : 0;
       }
-      c.src[u] = ptr;
-      c.dst[u] = r * kPad + cc * 8;
-    } else {
-      const int r = (ch >> 2) - BM;
-      const int64_t col = n0 + r;
-      c.src[u] = (col < p.N) ? B + col * p.K + cc * 8 : nullptr;
-      c.dst[u] = (BM + r) * kPad + cc * 8;
     }
+    c.asrc[u] = p.A + row * p.K + chunk * 8;
   }
-  c.gload(0);
-  c.lstore(0);
-  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < R::LB; ++u) {
+    const int r = (wave + 4 * u) * R::RPL + lane / R::CPR;
+    const int chunk = R::slot(r, lane % R::CPR);
+    const int64_t col = min(n0 + r, p.N - 1);
+    c.bsrc[u] = B + col * p.K + chunk * 8;
+  }
+  for (int st = 0; st < R::NS - 1; ++st)
+    if (st < c.total) c.issue(st);
 
   typename Ctx::Acc acc;
-  run_tree<NL>(c, acc);
+  if constexpr (NL == 8) {
+    float* spill = reinterpret_cast<float*>(&lds[R::NS * R::STAGE]) + wave * 64 * 64 + lane;
+    run_tree<4>(c, acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) spill[((i * 4 + j) * 4 + r) * 64] = acc.v[i][j][r];
+    run_tree<4>(c, acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc.v[i][j][r] = spill[((i * 4 + j) * 4 + r) * 64] + acc.v[i][j][r];
+  } else {
+    run_tree<NL>(c, acc);
+  }
 
   // Epilogue: lane holds rows 4*(lane/16)+r of each 16x16 block, column lane%16.
-  const int64_t rbase = m0 + c.wm * 16 * FM + 4 * (lane >> 4);
-  const int64_t cbase = n0 + c.wn * 16 * FN + (lane & 15);
+  const int64_t rbase = m0 + c.wm * 64 + 4 * (lane >> 4);
+  const int64_t cbase = n0 + c.wn * 64 + (lane & 15);
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t row = rbase + 16 * i + r;
-        const int64_t col = cbase + 16 * j;
-        if (row < m_end && col < p.N) {
-          const int64_t off = (int64_t)z * p.c_group_stride + row * p.N + col;
-          if constexpr (OUT_BF16)
-            reinterpret_cast<uint16_t*>(p.C)[off] = f32_to_bf16_bits(acc.v[i][j][r]);
-          else
-            reinterpret_cast<float*>(p.C)[off] = acc.v[i][j][r];
+    for (int r = 0; r < 4; ++r) {
+      const int64_t row = rbase + 16 * i + r;
+      if (row >= m_end) continue;
+      bool bad = false;
+      if constexpr (GROUPED) {
+        if (p.rows) {
+          const int64_t gr = p.rows[row];
+          bad = gr < 0 || gr >= p.a_rows;  // a malformed gather index gives a NaN row
         }
       }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t col = cbase + 16 * j;
+        if (col < p.N) {
+          const int64_t off = (int64_t)z * p.c_group_stride + row * p.N + col;
+          const float v = bad ? __builtin_nanf("") : acc.v[i][j][r];
+          if constexpr (OUT_BF16)
+            reinterpret_cast<uint16_t*>(p.C)[off] = f32_to_bf16_bits(v);
+          else
+            reinterpret_cast<float*>(p.C)[off] = v;
+        }
+      }
+    }
 }
 
 // -------------------------------------------------------------- stream kernel
@@ -389,21 +500,27 @@ __global__ __launch_bounds__(256) void cast_bf16_kernel(const float* __restrict_
 
 // ------------------------------------------------------------------ dispatch
 
-// Wave tile per subtree size: up to 4 leaves keep 64x64 per wave (<= 3 live
-// accumulator sets); 8 leaves need 4 live sets and use 64x32 per wave.
-inline int tile_bn(int nl) { return nl >= 8 ? 64 : 128; }
+#define INV_RING_CASE(NL_, BK_)                                                                              \
+  hipLaunchKernelGGL((gemm_ring_kernel<NL_, BK_, OUT_BF16, GROUPED>), grid, dim3(256), 0, s, p);             \
+  break;
 
 template <bool OUT_BF16, bool GROUPED>
-hipError_t tile_dispatch(const TileParams& p, dim3 grid, int nl, hipStream_t s) {
-  switch (nl) {
-    case 1: hipLaunchKernelGGL((gemm_tile_kernel<4, 4, 1, OUT_BF16, GROUPED>), grid, dim3(256), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((gemm_tile_kernel<4, 4, 2, OUT_BF16, GROUPED>), grid, dim3(256), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((gemm_tile_kernel<4, 4, 4, OUT_BF16, GROUPED>), grid, dim3(256), 0, s, p); break;
-    case 8: hipLaunchKernelGGL((gemm_tile_kernel<4, 2, 8, OUT_BF16, GROUPED>), grid, dim3(256), 0, s, p); break;
+hipError_t ring_dispatch(const TileParams& p, dim3 grid, int nl, hipStream_t s) {
+  const bool bk64 = p.kl % 64 == 0;  // else the leaf is an odd multiple of 32
+  switch (nl * 2 + (bk64 ? 1 : 0)) {
+    case 2: INV_RING_CASE(1, 32)
+    case 3: INV_RING_CASE(1, 64)
+    case 4: INV_RING_CASE(2, 32)
+    case 5: INV_RING_CASE(2, 64)
+    case 8: INV_RING_CASE(4, 32)
+    case 9: INV_RING_CASE(4, 64)
+    case 16: INV_RING_CASE(8, 32)
+    case 17: INV_RING_CASE(8, 64)
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
+#undef INV_RING_CASE
 
 template <int FM, bool OUT_BF16>
 hipError_t stream_dispatch_nw(const TileParams& p, dim3 grid, int nw, hipStream_t s) {
@@ -461,11 +578,11 @@ hipError_t launch_gemm(const GemmLaunch& g, hipStream_t s) {
   p.a_rows = g.a_rows;
   p.b_expert_stride = g.b_expert_stride;
 
-  if (g.offsets) {  // grouped: tile slots = an upper bound on sum_e ceil(count_e / 128)
+  if (g.offsets) {  // grouped: row-tile slots = an upper bound on sum_e ceil(count_e / 128)
     const int64_t slots = g.M / 128 + g.E;
-    const int bn = tile_bn(g.nl);
-    dim3 grid((unsigned)((g.N + bn - 1) / bn), (unsigned)slots, (unsigned)g.groups);
-    return g.out_bf16 ? tile_dispatch<true, true>(p, grid, g.nl, s) : tile_dispatch<false, true>(p, grid, g.nl, s);
+    const int64_t tiles_n = (g.N + 127) / 128;
+    dim3 grid((unsigned)(slots * tiles_n), 1u, (unsigned)g.groups);
+    return g.out_bf16 ? ring_dispatch<true, true>(p, grid, g.nl, s) : ring_dispatch<false, true>(p, grid, g.nl, s);
   }
   if (g.M <= 64) {
     const int fm = (int)((g.M + 15) / 16);
@@ -473,9 +590,9 @@ hipError_t launch_gemm(const GemmLaunch& g, hipStream_t s) {
     dim3 grid((unsigned)((g.N + 15) / 16), 1u, (unsigned)g.groups);
     return g.out_bf16 ? stream_dispatch<true>(p, fm, grid, g.nl, s) : stream_dispatch<false>(p, fm, grid, g.nl, s);
   }
-  const int bn = tile_bn(g.nl);
-  dim3 grid((unsigned)((g.N + bn - 1) / bn), (unsigned)((g.M + 127) / 128), (unsigned)g.groups);
-  return g.out_bf16 ? tile_dispatch<true, false>(p, grid, g.nl, s) : tile_dispatch<false, false>(p, grid, g.nl, s);
+  const int64_t tiles = ((g.M + 127) / 128) * ((g.N + 127) / 128);
+  dim3 grid((unsigned)tiles, 1u, (unsigned)g.groups);
+  return g.out_bf16 ? ring_dispatch<true, false>(p, grid, g.nl, s) : ring_dispatch<false, false>(p, grid, g.nl, s);
 }
 
 hipError_t launch_tree_combine(const float* P, int count, int64_t plane, void* C, bool out_bf16, bool left_fold,
