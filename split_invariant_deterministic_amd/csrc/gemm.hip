@@ -136,65 +136,174 @@ template <int BK, int RING>
 struct RingCtx {
   using R = Ring<BK, RING>;
   using Acc = AccT<4, 4>;
+  static constexpr int USED = R::NS * R::STAGE;  // ring bytes in use
   uint8_t* lds;
-  const uint16_t* asrc[R::LA];
-  const uint16_t* bsrc[R::LB];
-  int64_t kbase;  // first k of the workgroup's leaf range
+  // DMA sources: wave-uniform bases advanced along K, plus per-lane byte
+  // offsets fixed for the whole kernel (row * K + 16-byte chunk), so an issue
+  // costs scalar adds and the loads take the saddr + voffset form.
+  const uint8_t* abase;
+  const uint8_t* bbase;
+  uint32_t aoff[R::LA];
+  uint32_t boff[R::LB];
+  int64_t iss_k;  // first k of the next stage to issue
+  int iss_off;    // its ring slot (byte offset)
+  int issued;     // stages issued so far
+  // Fragment reads: per-lane byte offsets of operand block 0 for k substeps
+  // 0 and 1 (block i adds 16 * i rows, an immediate: the swizzle depends on
+  // the row only through (row / RPW) % CPR, which 16 rows leave unchanged).
+  uint32_t rd_a[BK / 32], rd_b[BK / 32];
+  int rd_off;     // ring slot of stage g
   int g;          // next stage to compute
   int total;      // stages in the range
   int spl;        // stages per leaf
-  int lane, wave, wm, wn;
+  int wave;       // wave-uniform
 
   // The direct-to-LDS builtin is compiled in the device pass only: seen by the
   // host pass it silently suppresses the host launch stubs of the kernel
   // template's instantiations.
-  __device__ __forceinline__ void issue(int st) {
+  // Stage issue split in two: the loads are interleaved with the MFMAs of the
+  // second k substep (one load per two MFMAs) instead of leaving the barrier
+  // as one burst, so the wave never sits in the load queue while its MFMA
+  // pipe drains.
+  __device__ __forceinline__ void issue_one(int u) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    const int64_t k = kbase + (int64_t)st * BK;
-    uint8_t* base = lds + (st % R::NS) * R::STAGE;
-#pragma unroll
-    for (int u = 0; u < R::LA; ++u)
-      __builtin_amdgcn_global_load_lds(asrc[u] + k, &base[(wave + 4 * u) * 1024], 16, 0, 0);
-#pragma unroll
-    for (int u = 0; u < R::LB; ++u)
-      __builtin_amdgcn_global_load_lds(bsrc[u] + k, &base[R::ABYTES + (wave + 4 * u) * 1024], 16, 0, 0);
-#else
-    (void)st;
+    uint8_t* dst = lds + iss_off;
+    if (u < R::LA)
+      __builtin_amdgcn_global_load_lds(abase + iss_k * 2 + aoff[u], &dst[(wave + 4 * u) * 1024], 16, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds(bbase + iss_k * 2 + boff[u - R::LA],
+                                       &dst[R::ABYTES + (wave + 4 * (u - R::LA)) * 1024], 16, 0, 0);
 #endif
   }
-  __device__ __forceinline__ void compute(int st, Acc& acc) {
-    const uint8_t* base = lds + (st % R::NS) * R::STAGE;
-    const int g4 = lane >> 4, r16 = lane & 15;
+  __device__ __forceinline__ void issue_done() {
+    iss_k += BK;
+    iss_off += R::STAGE;
+    if (iss_off == USED) iss_off = 0;
+    ++issued;
+  }
+  __device__ __forceinline__ void issue_next() {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const uint8_t* a = abase + iss_k * 2;
+    const uint8_t* b = bbase + iss_k * 2;
+    uint8_t* dst = lds + iss_off;
 #pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
-      bf16x8 af[4], bfr[4];
+    for (int u = 0; u < R::LA; ++u)
+      __builtin_amdgcn_global_load_lds(a + aoff[u], &dst[(wave + 4 * u) * 1024], 16, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = wm * 64 + 16 * i + r16;
-        af[i] = *reinterpret_cast<const bf16x8*>(&base[R::off(r, 4 * ks + g4)]);
-      }
+    for (int u = 0; u < R::LB; ++u)
+      __builtin_amdgcn_global_load_lds(b + boff[u], &dst[R::ABYTES + (wave + 4 * u) * 1024], 16, 0, 0);
+#endif
+    iss_k += BK;
+    iss_off += R::STAGE;
+    if (iss_off == USED) iss_off = 0;
+    ++issued;
+  }
+  static __device__ __forceinline__ int next_slot(int off) {
+    off += R::STAGE;
+    return off == USED ? 0 : off;
+  }
+  __device__ __forceinline__ void read_frags(int slot, int ks, bf16x8 (&fa)[4], bf16x8 (&fb)[4]) {
+    const uint8_t* pa = lds + slot + rd_a[ks];
+    const uint8_t* pb = lds + slot + rd_b[ks];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = wn * 64 + 16 * j + r16;
-        bfr[j] = *reinterpret_cast<const bf16x8*>(&base[R::ABYTES + R::off(r, 4 * ks + g4)]);
-      }
+    for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(pa + 16 * i * R::ROWB);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j) fb[j] = *reinterpret_cast<const bf16x8*>(pb + 16 * j * R::ROWB);
+  }
+  static __device__ __forceinline__ void mma(const bf16x8 (&fa)[4], const bf16x8 (&fb)[4], Acc& acc) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc.v[i][j] = mfma16(af[i], bfr[j], acc.v[i][j]);
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc.v[i][j] = mfma16(fa[i], fb[j], acc.v[i][j]);
+  }
+  // The first MFMA of a leaf: C is the +0 literal rather than a zeroed
+  // register set, so no zero set enters the accumulator's loop phi (which
+  // made the register allocator rotate accumulators every iteration).
+  static __device__ __forceinline__ void mma_first(const bf16x8 (&fa)[4], const bf16x8 (&fb)[4], Acc& acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc.v[i][j] = mfma16(fa[i], fb[j], f32x4{0.f, 0.f, 0.f, 0.f});
+  }
+
+  // BK = 64 keeps the next k-substep's operand fragments in flight while the
+  // current substep's 16 MFMAs run: the ks = 0 fragments of a stage are read
+  // right after the barrier that publishes it, in the middle of the previous
+  // stage, so NS stages are in flight and no LDS read latency is exposed.
+  bf16x8 fa0[4], fb0[4];
+
+  __device__ __forceinline__ void prologue() {
+    if constexpr (BK == 64) {
+      for (int st = 0; st < R::NS; ++st)
+        if (issued < total) issue_next();
+      wait_vm_rem<R::LOADS, R::NS - 1>(total - 1);
+      block_barrier();
+      read_frags(rd_off, 0, fa0, fb0);
+    } else {
+      for (int st = 0; st < R::NS - 1; ++st)
+        if (issued < total) issue_next();
     }
   }
-  // One leaf: acc starts at +0 and takes the leaf's stages in ascending k.
+
+  // One stage of a leaf (BK = 64): ks = 0 from fa0/fb0, ks = 1 read here; in
+  // the middle, publish stage g+1 and prefetch its ks = 0 fragments.
+  template <bool FIRST>
+  __device__ __forceinline__ void stage64(Acc& acc) {
+    bf16x8 fa1[4], fb1[4];
+    read_frags(rd_off, 1, fa1, fb1);
+    if constexpr (FIRST) mma_first(fa0, fb0, acc);
+    else mma(fa0, fb0, acc);
+    // Stage g+1 is complete once at most the later stages are outstanding
+    // (after the last stage this waits for nothing and the read below
+    // fetches a stale slot that is never used: keeping this section
+    // unconditional leaves no control-flow merge that would make the
+    // compiler drain these reads before the MFMAs that follow).
+    wait_vm_rem<R::LOADS, R::NS - 2>(total - 2 - g);
+    block_barrier();  // stage g+1 visible; every wave's reads of stage g are done
+    rd_off = next_slot(rd_off);
+    read_frags(rd_off, 0, fa0, fb0);
+    // MFMAs of substep 1 with the loads of stage g+NS (into stage g's slot)
+    // spread between them
+    const bool more = issued < total;
+    static_assert(R::LOADS == 8, "interleave assumes 8 loads per stage");
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (more) issue_one(2 * i);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc.v[i][j] = mfma16(fa1[i], fb1[j], acc.v[i][j]);
+      if (more) issue_one(2 * i + 1);
+#pragma unroll
+      for (int j = 2; j < 4; ++j) acc.v[i][j] = mfma16(fa1[i], fb1[j], acc.v[i][j]);
+    }
+    if (more) issue_done();
+    ++g;
+  }
+  template <bool FIRST>
+  __device__ __forceinline__ void stage32(Acc& acc) {
+    // this thread's loads of stage g are done once at most the loads of
+    // the (up to NS-2) later stages already issued are outstanding
+    wait_vm_rem<R::LOADS, R::NS - 2>(total - 1 - g);
+    block_barrier();  // every wave's stage g is in LDS; stage g-1 reads are done
+    if (issued < total) issue_next();  // stage g+NS-1, into stage g-1's slot
+    bf16x8 fa[4], fb[4];
+    read_frags(rd_off, 0, fa, fb);
+    rd_off = next_slot(rd_off);
+    if constexpr (FIRST) mma_first(fa, fb, acc);
+    else mma(fa, fb, acc);
+    ++g;
+  }
+
+  // One leaf: the chain starts at +0 and takes the leaf's stages in
+  // ascending k, each stage as its 32-wide k substeps in ascending order.
   __device__ __forceinline__ void leaf(Acc& acc) {
-    acc_zero(acc);
-    for (int s = 0; s < spl; ++s) {
-      // this thread's loads of stage g are done once at most the loads of
-      // the (up to NS-2) later stages already issued are outstanding
-      wait_vm_rem<R::LOADS, R::NS - 2>(total - 1 - g);
-      block_barrier();  // every wave's stage g is in LDS; stage g-1 reads are done
-      if (g + R::NS - 1 < total) issue(g + R::NS - 1);
-      compute(g, acc);
-      ++g;
+    if constexpr (BK == 64) {
+      stage64<true>(acc);
+#pragma clang loop unroll(disable)
+      for (int s = 1; s < spl; ++s) stage64<false>(acc);
+    } else {
+      stage32<true>(acc);
+#pragma clang loop unroll(disable)
+      for (int s = 1; s < spl; ++s) stage32<false>(acc);
     }
   }
 };
@@ -268,36 +377,48 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(TileParams p) {
 
   Ctx c;
   c.lds = lds;
-  c.lane = lane;
-  c.wave = wave;
-  c.wm = wave >> 1;
-  c.wn = wave & 1;
-  c.kbase = (int64_t)leaf0 * p.kl;
+  c.wave = __builtin_amdgcn_readfirstlane(wave);
+  c.iss_k = (int64_t)leaf0 * p.kl;
+  c.iss_off = 0;
+  c.issued = 0;
+  c.rd_off = 0;
   c.spl = p.kl / BK;
   c.total = c.spl * NL;
   c.g = 0;
+  {
+    const int wm = c.wave >> 1, wn = c.wave & 1, g4 = lane >> 4, r16 = lane & 15;
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      c.rd_a[ks] = R::off(wm * 64 + r16, 4 * ks + g4);
+      c.rd_b[ks] = R::ABYTES + R::off(wn * 64 + r16, 4 * ks + g4);
+    }
+  }
+  // A rows: contiguous from m0, or gathered (offsets then from A itself)
+  const uint8_t* A8 = reinterpret_cast<const uint8_t*>(p.A);
+  c.abase = (GROUPED && p.rows) ? A8 : A8 + m0 * p.K * 2;
+  c.bbase = reinterpret_cast<const uint8_t*>(B + n0 * p.K);
 #pragma unroll
   for (int u = 0; u < R::LA; ++u) {
-    const int r = (wave + 4 * u) * R::RPL + lane / R::CPR;
+    const int r = (c.wave + 4 * u) * R::RPL + lane / R::CPR;
     const int chunk = R::slot(r, lane % R::CPR);  // the slot map is its own inverse
     int64_t row = min(m0 + r, m_end - 1);
+    int64_t rel = row - m0;
     if constexpr (GROUPED) {
       if (p.rows) {
         const int64_t gr = p.rows[row];
-        row = (gr >= 0 && gr < p.a_rows) ? gr : 0;
+        rel = (gr >= 0 && gr < p.a_rows) ? gr : 0;
       }
     }
-    c.asrc[u] = p.A + row * p.K + chunk * 8;
+    c.aoff[u] = (uint32_t)((rel * p.K + chunk * 8) * 2);
   }
 #pragma unroll
   for (int u = 0; u < R::LB; ++u) {
-    const int r = (wave + 4 * u) * R::RPL + lane / R::CPR;
+    const int r = (c.wave + 4 * u) * R::RPL + lane / R::CPR;
     const int chunk = R::slot(r, lane % R::CPR);
     const int64_t col = min(n0 + r, p.N - 1);
-    c.bsrc[u] = B + col * p.K + chunk * 8;
+    c.boff[u] = (uint32_t)(((col - n0) * p.K + chunk * 8) * 2);
   }
-  for (int st = 0; st < R::NS - 1; ++st)
-    if (st < c.total) c.issue(st);
+  c.prologue();
 
   typename Ctx::Acc acc;
   if constexpr (NL == 8) {
@@ -321,8 +442,8 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(TileParams p) {
   }
 
   // Epilogue: lane holds rows 4*(lane/16)+r of each 16x16 block, column lane%16.
-  const int64_t rbase = m0 + c.wm * 64 + 4 * (lane >> 4);
-  const int64_t cbase = n0 + c.wn * 64 + (lane & 15);
+  const int64_t rbase = m0 + (c.wave >> 1) * 64 + 4 * (lane >> 4);
+  const int64_t cbase = n0 + (c.wave & 1) * 64 + (lane & 15);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
