@@ -30,8 +30,9 @@
 // its visible keys and L: a decode row equals the same position's row in a
 // multi-row (prefill) launch. Scores are produced transposed (keys x heads):
 // each lane then holds the 8 probabilities of one head that the P.V MFMA
-// takes as its A operand; V is transposed through LDS so that the B operand
-// holds the same 8 keys in the same slots.
+// takes as its A operand. V rows go straight from HBM into LDS (direct
+// loads) and the P.V B operand is read back transposed with the gfx950
+// transpose read, holding the same 8 keys in the same slots.
 #include "common.h"
 #include "launch.h"
 
@@ -42,16 +43,38 @@ constexpr int kD = 128;
 
 template <int CH>
 struct AttnCfg {
-  static constexpr int KB = CH / 16;     // 16-key blocks per chunk
-  static constexpr int PV = CH / 32;     // 32-key MFMA steps per chunk
-  static constexpr int VT = CH + 4;      // LDS row stride (bf16) of V^T
-  static constexpr int VLOADS = CH * 16 / 64;  // 16-byte V loads per lane per chunk
+  static constexpr int KB = CH / 16;        // 16-key blocks per chunk
+  static constexpr int PV = CH / 32;        // 32-key MFMA steps per chunk
+  static constexpr int ROWB = kD * 2;       // bytes per staged V row (one key)
+  static constexpr int VDMA = CH / 4;       // 1 KB (4-key) direct loads per chunk
 };
+
+// V rows are staged in LDS in their own layout (key-major, d contiguous),
+// 16-byte chunk c of key k stored at chunk c ^ (2 * (k % 4)). The P.V MFMA
+// needs V transposed (keys along the operand's k slots); the gfx950
+// transpose read ds_read_b64_tr_b16 delivers that: within each 16-lane group
+// the 16 four-element reads are concatenated and lane l receives elements
+// l, l+16, l+32, l+48, so source lane q + 4m reading 8 bytes of key key0+m at
+// d = 16 db + 4q hands lane n the values V[key0 + m][16 db + n], m = 0..3.
+// With the swizzle the 16 lanes of a group touch 128 distinct bytes.
+__device__ __forceinline__ int vswz(int key, int chunk) { return chunk ^ ((key & 3) << 1); }
+
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)((__attribute__((address_space(3))) uint8_t*)p));
+#else
+  (void)p;
+  return s16x4{0, 0, 0, 0};
+#endif
+}
 
 template <int CH>
 __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a, float scale) {
   using Cfg = AttnCfg<CH>;
-  __shared__ __attribute__((aligned(16))) uint16_t vt[kD * Cfg::VT];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs[CH * Cfg::ROWB];
 
   const int lane = threadIdx.x;
   const int g4 = lane >> 4, c16 = lane & 15;
@@ -93,7 +116,7 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a, float scal
 
   const uint16_t* Q = static_cast<const uint16_t*>(a.q);
   const uint16_t* K = static_cast<const uint16_t*>(a.k);
-  const uint16_t* Vg = static_cast<const uint16_t*>(a.v);
+  const uint8_t* Vb = static_cast<const uint8_t*>(a.v);
   const int64_t kv_row = (int64_t)a.Hkv * kD;  // elements between consecutive keys
 
   // Q^T as the B operand: column = head c16 of the group, k = d.
@@ -108,6 +131,8 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a, float scal
       qf[ds] = __builtin_bit_cast(bf16x8, v);
     }
   }
+  // transpose-read lane roles: source lane s = q + 4m of each 16-lane group
+  const int tr_m = (lane & 15) >> 2, tr_q = lane & 3;
 
   float m_run = -INFINITY, l_run = 0.0f;  // per head c16 (identical in the 4 lanes of a head)
   f32x4 o[8];
@@ -116,7 +141,7 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a, float scal
 
   for (int64_t c = c0; c < c1; ++c) {
     const int64_t kbase = c * CH;  // position of the chunk's first key
-    // ---- loads: K fragments (A operand: key rows, k = d) and V rows
+    // ---- K fragments (A operand: key rows, k = d)
     bf16x8 kf[Cfg::KB][4];
 #pragma unroll
     for (int kb = 0; kb < Cfg::KB; ++kb) {
@@ -130,16 +155,18 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a, float scal
         kf[kb][ds] = __builtin_bit_cast(bf16x8, v);
       }
     }
-    u32x4 vv[Cfg::VLOADS];
+    // ---- V rows straight into LDS (keys past L load a clamped valid key:
+    //      their p is exactly 0, and the key's values are finite cache data)
+#if defined(__HIP_DEVICE_COMPILE__)
 #pragma unroll
-    for (int i = 0; i < Cfg::VLOADS; ++i) {
-      const int key = 4 * i + g4;  // 16 lanes share a key: 16 x 16 B = one 128-d row
-      const int64_t pos = kbase + key;
-      const bool ok = pos < L;
-      u32x4 v = *reinterpret_cast<const u32x4*>(Vg + (start + (ok ? pos : 0)) * kv_row + (int64_t)kvh * kD + 8 * c16);
-      if (!ok) v = u32x4{0u, 0u, 0u, 0u};
-      vv[i] = v;
+    for (int i = 0; i < Cfg::VDMA; ++i) {
+      const int key = 4 * i + (lane >> 4);
+      const int slot = lane & 15;
+      const int64_t pos = min(kbase + key, L - 1);
+      const uint8_t* src = Vb + ((start + pos) * kv_row + (int64_t)kvh * kD) * 2 + vswz(key, slot) * 16;
+      __builtin_amdgcn_global_load_lds(src, &vs[i * 1024], 16, 0, 0);
     }
+#endif
     // ---- S^T = K Q^T: lane holds keys kb*16 + 4*g4 + r for head c16
     f32x4 st[Cfg::KB];
 #pragma unroll
@@ -187,19 +214,6 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a, float scal
     l_run = l_run * alpha + psum;
     m_run = m_new;
 
-    // ---- V^T into LDS: vt[d][key]
-#pragma unroll
-    for (int i = 0; i < Cfg::VLOADS; ++i) {
-      const int key = 4 * i + g4;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int d = 8 * c16 + 2 * q;
-        vt[d * Cfg::VT + key] = (uint16_t)(vv[i][q] & 0xffffu);
-        vt[(d + 1) * Cfg::VT + key] = (uint16_t)(vv[i][q] >> 16);
-      }
-    }
-    __syncthreads();
-
     // ---- o = P V, started from o * alpha. Output rows = heads 4*g4 + r.
     float al[4];
 #pragma unroll
@@ -208,6 +222,7 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a, float scal
     for (int db = 0; db < 8; ++db)
 #pragma unroll
       for (int r = 0; r < 4; ++r) o[db][r] = o[db][r] * al[r];
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's V rows are in LDS
 #pragma unroll
     for (int t = 0; t < Cfg::PV; ++t) {
       // A operand: head c16, keys {32t + 4 g4 + e} (e < 4) and {32t + 16 + 4 g4 + e - 4}
@@ -222,22 +237,24 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a, float scal
       pb[3] = pl[2 * t + 1][1];
       const bf16x8 pf = __builtin_bit_cast(bf16x8, pa);
       const bf16x8 pfl = __builtin_bit_cast(bf16x8, pb);
+      // B operand: the same keys for d = 16 db + c16, by two transpose reads
+      const int k0 = 32 * t + 4 * g4 + tr_m, k1 = k0 + 16;
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        const uint16_t* vrow = vt + (db * 16 + c16) * Cfg::VT + 32 * t + 4 * g4;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
+        const int ch = 2 * db + (tr_q >> 1), byte = (tr_q & 1) * 8;
+        const s16x4 lo = lds_read_tr16(&vs[k0 * Cfg::ROWB + vswz(k0, ch) * 16 + byte]);
+        const s16x4 hi = lds_read_tr16(&vs[k1 * Cfg::ROWB + vswz(k1, ch) * 16 + byte]);
         u32x4 vb;
-        vb[0] = lo.x;
-        vb[1] = lo.y;
-        vb[2] = hi.x;
-        vb[3] = hi.y;
+        vb[0] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1));
+        vb[1] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3));
+        vb[2] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1));
+        vb[3] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3));
         const bf16x8 vf = __builtin_bit_cast(bf16x8, vb);
         o[db] = mfma16(pf, vf, o[db]);   // high parts first,
         o[db] = mfma16(pfl, vf, o[db]);  // then the low parts, in this fixed order
       }
     }
-    __syncthreads();  // vt is rewritten by the next chunk
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // V reads done before the next chunk's loads land
   }
 
   // ---- split state: o (rows = heads 4 g4 + r, col d = 16 db + c16), m, l (head c16)
