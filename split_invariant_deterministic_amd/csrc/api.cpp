@@ -409,7 +409,9 @@ inv_status inv_moe_gemm(const inv_contract* c, const void* X, int64_t x_rows, co
   if (s != INV_OK) return s;
   if (c->ranks != 1) return INV_E_TOPOLOGY;
   if (R < 0 || N < 0 || E <= 0 || x_rows < 0) return INV_E_ARG;
-  if (E > 65536) return INV_E_UNSUPPORTED;
+  if (E > 65536 || R > ((int64_t)1 << 31) - 1) return INV_E_UNSUPPORTED;
+  // gathered rows are addressed by 32-bit byte offsets from the start of X
+  if (rows && x_rows * K * 2 > ((int64_t)1 << 32) - 1) return INV_E_UNSUPPORTED;
   if (R == 0 || N == 0) return INV_OK;
   if (!X || !offsets || !W || !Y) return INV_E_ARG;
   if (!rows && x_rows < R) return INV_E_ARG;

@@ -334,22 +334,39 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(TileParams p) {
     // row tiles, in expert order; every row tile spans all column tiles
     const int t = (int)(blockIdx.x / tiles_n);
     n0 = (int64_t)(blockIdx.x % tiles_n) * R::BN;
-    int e = 0, tstart = 0;
-    int64_t r0 = 0, r1 = 0;
-    bool found = false;
-    for (; e < p.E; ++e) {
-      // offsets come from device memory: clamp so a malformed table can
-      // never address rows outside [0, M)
-      r0 = min(max((int64_t)p.offsets[e], (int64_t)0), p.M);
-      r1 = min(max((int64_t)p.offsets[e + 1], r0), p.M);
-      const int nt = (int)((r1 - r0 + R::BM - 1) / R::BM);
-      if (t < tstart + nt) {
-        found = true;
-        break;
+    // The tile counts are prefix-summed 64 experts at a time across the
+    // wave (two loads per lane, integer shuffles) and the owner found by a
+    // ballot, instead of a serial walk over every expert's offsets.
+    // Offsets come from device memory: clamp so a malformed table can never
+    // address rows outside [0, M).
+    int e = -1, tstart = 0, r0 = 0, r1 = 0, running = 0;
+    for (int cbase = 0; cbase < p.E && e < 0; cbase += 64) {
+      const int ee = cbase + lane;
+      int a0 = 0, a1 = 0, nt = 0;
+      if (ee < p.E) {
+        a0 = (int)min(max((int64_t)p.offsets[ee], (int64_t)0), p.M);
+        a1 = (int)min(max((int64_t)p.offsets[ee + 1], (int64_t)a0), p.M);
+        nt = (a1 - a0 + R::BM - 1) / R::BM;
       }
-      tstart += nt;
+      int incl = nt;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += v;
+      }
+      incl += running;
+      const uint64_t hit = __ballot(ee < p.E && t < incl);
+      if (hit) {  // wave-uniform
+        const int f = __ffsll((unsigned long long)hit) - 1;
+        e = cbase + f;
+        tstart = __shfl(incl - nt, f, 64);
+        r0 = __shfl(a0, f, 64);
+        r1 = __shfl(a1, f, 64);
+      } else {
+        running = __shfl(incl, 63, 64);
+      }
     }
-    if (!found) return;  // slot past the last tile: uniform exit before any barrier
+    if (e < 0) return;  // slot past the last tile: uniform exit before any barrier
     m0 = r0 + (int64_t)(t - tstart) * R::BM;
     m_end = r1;
     B += (int64_t)e * p.b_expert_stride;

@@ -111,21 +111,42 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict_
 //   count  : block e counts pairs with id e -> offsets[e+1]; block 0 also
 //            marks pairs with an id outside [0, E) as slot -1;
 //   scan   : offsets[0] = 0, offsets[e+1] += offsets[e] (one thread);
-//   scatter: block e walks the pairs in ascending p, 1024 per round, and
-//            gives its pairs consecutive grouped rows from offsets[e].
+//   scatter: block (e, s) owns slice s of the pairs; it counts expert e's
+//            pairs in the earlier slices (its base), each wave counts its
+//            quarter of the slice, and the waves then hand out consecutive
+//            grouped rows in ascending p with ballots.
+
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __builtin_amdgcn_ds_bpermute(((threadIdx.x & 63) ^ off) << 2, v);
+  return v;
+}
+
+// Matches of id e in pairs [lo, hi), summed over the calling threads
+// (stride = number of threads taking part, t = this thread's index).
+__device__ __forceinline__ int count_matches(const int32_t* __restrict__ ids, int64_t lo, int64_t hi, int e, int t,
+                                             int stride) {
+  int cnt = 0;
+  int64_t p = lo + t;
+  // bulk: 4 independent loads in flight per thread
+  for (; p + 3 * (int64_t)stride < hi; p += 4 * (int64_t)stride) {
+    const int32_t a = ids[p], b = ids[p + stride], c = ids[p + 2 * stride], d = ids[p + 3 * stride];
+    cnt += (a == e) + (b == e) + (c == e) + (d == e);
+  }
+  for (; p < hi; p += stride) cnt += (ids[p] == e);
+  return cnt;
+}
 
 __global__ __launch_bounds__(256) void moe_count_kernel(const int32_t* __restrict__ ids, int32_t* __restrict__ offsets,
                                                         int32_t* __restrict__ slot, int64_t P, int E) {
   __shared__ int part[4];
   const int e = blockIdx.x;
-  int cnt = 0;
-  for (int64_t p = threadIdx.x; p < P; p += 256) {
-    const int32_t id = ids[p];
-    cnt += (id == e);
-    if (e == 0 && (id < 0 || id >= E)) slot[p] = -1;
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) cnt += __builtin_amdgcn_ds_bpermute(((threadIdx.x & 63) ^ off) << 2, cnt);
+  if (e == 0)
+    for (int64_t p = threadIdx.x; p < P; p += 256) {
+      const int32_t id = ids[p];
+      if (id < 0 || id >= E) slot[p] = -1;
+    }
+  const int cnt = wave_sum_int(count_matches(ids, 0, P, e, threadIdx.x, 256));
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = cnt;
   __syncthreads();
   if (threadIdx.x == 0) offsets[e + 1] = part[0] + part[1] + part[2] + part[3];
@@ -137,45 +158,47 @@ __global__ void moe_scan_kernel(int32_t* __restrict__ offsets, int E) {
   for (int e = 0; e < E; ++e) offsets[e + 1] += offsets[e];
 }
 
+constexpr int kScatterSlices = 8;
+
 __global__ __launch_bounds__(256) void moe_scatter_kernel(const int32_t* __restrict__ ids,
                                                           const int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ rows, int32_t* __restrict__ slot,
                                                           int64_t P, int k) {
-  __shared__ int scan[256];
-  const int e = blockIdx.x;
-  const int tid = threadIdx.x;
-  int64_t next = offsets[e];
-  for (int64_t base = 0; base < P; base += 1024) {
-    bool f[4];
-    int c = 0;
+  __shared__ int part[2][4];
+  const int e = blockIdx.x, sidx = blockIdx.y;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t s0 = (P * sidx) / kScatterSlices, s1 = (P * (sidx + 1)) / kScatterSlices;
+  const int64_t q0 = s0 + ((s1 - s0) * w) / 4, q1 = s0 + ((s1 - s0) * (w + 1)) / 4;  // this wave's quarter
+  // expert e's pairs before this slice, and in this wave's quarter
+  const int before = wave_sum_int(count_matches(ids, 0, s0, e, threadIdx.x, 256));
+  const int mine = wave_sum_int(count_matches(ids, q0, q1, e, lane, 64));
+  if (lane == 0) {
+    part[0][w] = before;
+    part[1][w] = mine;
+  }
+  __syncthreads();
+  int next = offsets[e] + part[0][0] + part[0][1] + part[0][2] + part[0][3];
+  for (int v = 0; v < w; ++v) next += part[1][v];
+  const uint64_t lt = (1ull << lane) - 1ull;
+  for (int64_t base = q0; base < q1; base += 256) {
+    int32_t id[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t p = base + 4 * tid + u;
-      f[u] = p < P && ids[p] == e;
-      c += f[u];
+    for (int j = 0; j < 4; ++j) {
+      const int64_t p = base + 64 * j + lane;
+      id[j] = p < q1 ? ids[p] : -1;
     }
-    // inclusive Hillis-Steele scan of the per-thread counts (integers: exact)
-    scan[tid] = c;
-    __syncthreads();
 #pragma unroll
-    for (int off = 1; off < 256; off <<= 1) {
-      const int v = tid >= off ? scan[tid - off] : 0;
-      __syncthreads();
-      scan[tid] += v;
-      __syncthreads();
-    }
-    int r = (int)next + scan[tid] - c;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (f[u]) {
-        const int64_t p = base + 4 * tid + u;
+    for (int j = 0; j < 4; ++j) {
+      const int64_t p = base + 64 * j + lane;
+      const bool f = id[j] == e;
+      const uint64_t bal = __ballot(f);
+      if (f) {
+        const int r = next + __popcll(bal & lt);
         rows[r] = (int32_t)(p / k);
         slot[p] = r;
-        ++r;
       }
+      next += __popcll(bal);
     }
-    next += scan[255];
-    __syncthreads();  // scan[] is rewritten next round
   }
 }
 
@@ -183,6 +206,14 @@ __global__ __launch_bounds__(256) void moe_scatter_kernel(const int32_t* __restr
 //
 // a = bf16( silu(g) * u ), silu(g) = g / (1 + exp(-g)), g and u the bf16
 // halves of a packed [gate | up] row, math in fp32 (exp as exp2(-g*log2e)).
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  const float t = -g * kLog2e;
+  const float den = 1.0f + exp2_hw(t);
+  const float s = g / den;
+  return s * u;
+}
+
+// Scalar form (any F).
 __global__ __launch_bounds__(256) void swiglu_kernel(const uint16_t* __restrict__ gu, uint16_t* __restrict__ a,
                                                      int64_t R, int64_t F) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -190,10 +221,23 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const uint16_t* __restrict_
   const int64_t r = i / F, f = i - r * F;
   const float g = bf16_bits_to_f32(gu[r * 2 * F + f]);
   const float u = bf16_bits_to_f32(gu[r * 2 * F + F + f]);
-  const float t = -g * kLog2e;
-  const float den = 1.0f + exp2_hw(t);
-  const float s = g / den;
-  a[i] = f32_to_bf16_bits(s * u);
+  a[i] = f32_to_bf16_bits(silu_mul(g, u));
+}
+
+// F % 8 == 0: 8 outputs per thread with 16-byte accesses (same per-element math).
+__global__ __launch_bounds__(256) void swiglu8_kernel(const uint16_t* __restrict__ gu, uint16_t* __restrict__ a,
+                                                      int64_t R, int64_t F) {
+  const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 8-element group
+  const int64_t F8 = F >> 3;
+  if (v >= R * F8) return;
+  const int64_t r = v / F8, f = (v - r * F8) * 8;
+  const u32x4 g = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(gu + r * 2 * F + f));
+  const u32x4 u = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(gu + r * 2 * F + F + f));
+  u32x4 o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    o[q] = pack_bf16x2(silu_mul(bf16_lo(g[q]), bf16_lo(u[q])), silu_mul(bf16_hi(g[q]), bf16_hi(u[q])));
+  __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(a + r * F + f));
 }
 
 // ----------------------------------------------------------------- combine
@@ -267,14 +311,22 @@ hipError_t launch_moe_permute(const int32_t* ids, int32_t* offsets, int32_t* row
   hipLaunchKernelGGL(moe_scan_kernel, dim3(1), dim3(64), 0, s, offsets, E);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (P == 0) return hipSuccess;
-  hipLaunchKernelGGL(moe_scatter_kernel, dim3((unsigned)E), dim3(256), 0, s, ids, offsets, rows, slot, P, k);
+  hipLaunchKernelGGL(moe_scatter_kernel, dim3((unsigned)E, kScatterSlices), dim3(256), 0, s, ids, offsets, rows, slot,
+                     P, k);
   return hipGetLastError();
 }
 
 hipError_t launch_swiglu(const void* gu, void* a, int64_t R, int64_t F, hipStream_t s) {
-  const int64_t n = R * F;
-  hipLaunchKernelGGL(swiglu_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                     static_cast<const uint16_t*>(gu), static_cast<uint16_t*>(a), R, F);
+  auto G = static_cast<const uint16_t*>(gu);
+  auto O = static_cast<uint16_t*>(a);
+  const bool vec = F % 8 == 0 && ((reinterpret_cast<uintptr_t>(gu) | reinterpret_cast<uintptr_t>(a)) & 15u) == 0;
+  if (vec) {
+    const int64_t n = R * (F / 8);
+    hipLaunchKernelGGL(swiglu8_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, G, O, R, F);
+  } else {
+    const int64_t n = R * F;
+    hipLaunchKernelGGL(swiglu_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, G, O, R, F);
+  }
   return hipGetLastError();
 }
 

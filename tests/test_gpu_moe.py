@@ -178,3 +178,23 @@ def test_grouped_gemm_rows_equal_plain_gemm(inv, moe_full):
             continue
         ref = inv.gemm(d["x"][rows[r0:r1].long()].contiguous(), d["W1"][e], c)
         assert bitwise_equal(GU[r0:r1], ref), e
+
+
+@pytest.mark.parametrize("R,F", [(37, 13), (5, 768), (130, 40)])
+def test_swiglu_against_oracle(inv, R, F):
+    """Both forms: 16-byte groups (F % 8 == 0) and the scalar form (any F)."""
+    gu = synth.randn((R, 2 * F), 31 + F, 2.0)
+    a = inv.swiglu(gu.to(DEV), inv.contract())
+    check_bf16(a, omoe.swiglu(_np(gu).astype(np.float64)), f"swiglu {R}x{F}")
+
+
+@pytest.mark.parametrize("T", [1, 3, 1000, 4099])
+def test_permute_small_and_ragged(inv, T):
+    logits = synth.randn((T, 128), 60 + T, dtype=torch.float32)
+    c = inv.contract(leaves=8)
+    ids, _ = inv.moe_route(logits.to(DEV), c)
+    offsets, rows, slot = inv.moe_permute(ids, 128, c)
+    o, r, s = _grouping(ids.cpu().numpy(), 128)
+    assert np.array_equal(offsets.cpu().numpy(), o)
+    assert np.array_equal(rows.cpu().numpy(), r)
+    assert np.array_equal(slot.cpu().numpy(), s)
