@@ -118,7 +118,8 @@ typedef enum inv_op {
 inv_status inv_contract_check(const inv_contract* c, int op, int64_t K);
 
 /* Workspace bytes `op` needs for the given sizes (0 if none):
- *   INV_OP_GEMM:        d0 = M, d1 = N, d2 = K  -> ranks*M*N*4 when ranks > 1
+ *   INV_OP_GEMM:        d0 = M, d1 = N, d2 = K  -> ranks*M*N*4 when ranks > 1;
+ *                       with ranks == 1 the optional leaf-group size (or 0)
  *   INV_OP_DECODE_ATTN: d0 = Tq, d1 = Hq, d2 = D -> Tq*Hq*split_kv*(D+2)*4
  * Returns (size_t)-1 if the contract is invalid. Host only. */
 size_t inv_workspace_bytes(const inv_contract* c, int op, int64_t d0, int64_t d1, int64_t d2);
@@ -146,6 +147,11 @@ const char* inv_status_string(inv_status s);
  * partials (ws_bytes >= inv_workspace_bytes(INV_OP_GEMM)), and the top
  * log2(R) tree levels finish the sum. The result is bitwise identical for
  * every proven R. tree must be BALANCED.
+ * ranks == 1: the workspace is optional. For 64 < M with too few 128 x 128
+ * output tiles to fill the chip (tiles * G <= 256), inv_workspace_bytes
+ * reports G*M*N*4 bytes; given that much, G aligned subtrees are reduced in
+ * parallel and combined by the same tree (bitwise the same result as without
+ * the workspace).
  * ------------------------------------------------------------------------ */
 inv_status inv_gemm(const inv_contract* c, const void* A, const void* B, void* C,
                     int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes,

@@ -67,6 +67,22 @@ inv_status check_logprob_contract(const inv_contract* c, int64_t V) {
 
 bool out_is_bf16(const inv_contract* c) { return c->out_dtype == INV_BF16; }
 
+// Leaf groups for the single-rank GEMM when 128 x 128 tiles alone leave
+// compute units idle (64 < M): G aligned subtrees of L/G leaves each are
+// reduced by separate workgroups into a workspace and the top log2(G) tree
+// levels finish the sum. Every subtree is a node of the same balanced tree,
+// so the bits equal the single-pass kernel's. A tile's time is set by its K
+// chain, so G is the largest power of two with tiles * G <= 256 (one
+// workgroup per compute unit on MI355X); measured best on 4096-12288 wide
+// projections.
+int gemm_split_groups(const inv_contract* c, int64_t M, int64_t N) {
+  if (c->ranks != 1 || M <= 64) return 1;
+  const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+  int G = 1;
+  while (G < (int)c->leaves && tiles * G * 2 <= 256) G *= 2;
+  return G;
+}
+
 }  // namespace
 
 extern "C" {
@@ -116,9 +132,12 @@ inv_status inv_contract_check(const inv_contract* c, int op, int64_t K) {
 size_t inv_workspace_bytes(const inv_contract* c, int op, int64_t d0, int64_t d1, int64_t d2) {
   if (d0 < 0 || d1 < 0 || d2 < 0) return (size_t)-1;
   switch (op) {
-    case INV_OP_GEMM:
+    case INV_OP_GEMM: {
       if (check_gemm_contract(c, d2) != INV_OK) return (size_t)-1;
-      return c->ranks > 1 ? (size_t)c->ranks * (size_t)d0 * (size_t)d1 * sizeof(float) : 0;
+      if (c->ranks > 1) return (size_t)c->ranks * (size_t)d0 * (size_t)d1 * sizeof(float);
+      const int G = gemm_split_groups(c, d0, d1);
+      return G > 1 ? (size_t)G * (size_t)d0 * (size_t)d1 * sizeof(float) : 0;
+    }
     case INV_OP_DECODE_ATTN:
       if (check_attn_contract(c) != INV_OK) return (size_t)-1;
       return (size_t)d0 * (size_t)d1 * (size_t)c->split_kv * (size_t)(d2 + 2) * sizeof(float);
@@ -184,7 +203,16 @@ inv_status inv_gemm(const inv_contract* c, const void* A, const void* B, void* C
   if (M == 0 || N == 0) return INV_OK;
   const int L = (int)c->leaves, R = (int)c->ranks;
   const int kl = (int)(K / L);
-  if (R == 1) return hip_status(inv::launch_gemm(gemm_launch(A, B, C, M, N, K, kl, 0, L, 1, out_is_bf16(c)), stream));
+  if (R == 1) {
+    const int G = gemm_split_groups(c, M, N);
+    const size_t need_g = (size_t)G * (size_t)M * (size_t)N * sizeof(float);
+    if (G == 1 || !ws || ws_bytes < need_g)  // the workspace is optional here
+      return hip_status(inv::launch_gemm(gemm_launch(A, B, C, M, N, K, kl, 0, L, 1, out_is_bf16(c)), stream));
+    hipError_t e = inv::launch_gemm(gemm_launch(A, B, ws, M, N, K, kl, 0, L / G, G, false), stream);
+    if (e != hipSuccess) return INV_E_HIP;
+    return hip_status(inv::launch_tree_combine(static_cast<const float*>(ws), G, M * N, C, out_is_bf16(c), false,
+                                               stream));
+  }
   const size_t need = (size_t)R * (size_t)M * (size_t)N * sizeof(float);
   if (!ws || ws_bytes < need) return INV_E_WORKSPACE;
   // every emulated rank reduces its aligned subtree into its own fp32 plane ...

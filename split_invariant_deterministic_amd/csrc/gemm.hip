@@ -12,7 +12,7 @@
 //            P_l = v_mfma_f32_16x16x32_bf16(A block, B block, P_l)
 //   C   = balanced fp32 tree over the leaves, then one cast.
 // Row m of the MFMA output depends only on row m of its A operand, so the
-// kernels are free to choose tiles by M; padding rows are zero-filled.
+// kernels are free to choose tiles by M; padding rows never reach C.
 //
 // Kernels
 //   gemm_ring_kernel    large M: 128 x 128 tile per workgroup, operands
@@ -494,48 +494,77 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(TileParams p) {
 template <int FM>
 struct StreamCtx {
   using Acc = AccT<FM, 1>;
-  const uint16_t* arow[FM];  // this lane's A row per m block (clamped)
-  bool avalid[FM];
-  const uint16_t* brow;
-  bool bvalid;
-  int64_t k;    // next k to load for this wave
-  int spl;
-  int lane;
+  // Operands through buffer descriptors: ra covers the tile's valid A rows,
+  // rb its valid B rows. A lane's row offset (voa, vob) is fixed; the k
+  // position is a wave-uniform byte offset, so a ring slot costs no address
+  // registers. Rows past M (columns past N) are clamped to the tile's first
+  // row: output element (i, j) depends only on A row i and B row j, and such
+  // rows and columns are never stored. No select on loaded data, so loads
+  // stay in flight.
+  buf_rsrc ra, rb;
+  uint32_t voa[FM];
+  uint32_t vob;
+  uint32_t kb;  // byte offset of this wave's leaf start (wave-uniform)
+  int spl;      // 32-k blocks per leaf
 
-  __device__ __forceinline__ void load(int64_t kk, bf16x8 (&a)[FM], bf16x8& b) {
-    const int off = 8 * (lane >> 4);
+  // blocks `base` (uniform, runtime) + d (compile time) of the leaf
+  __device__ __forceinline__ void load(uint32_t base, int d, bf16x8 (&a)[FM], bf16x8& b) {
+    const uint32_t soff = kb + 64u * base;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      u32x4 v = *reinterpret_cast<const u32x4*>(arow[i] + kk + off);
-      if (!avalid[i]) v = u32x4{0u, 0u, 0u, 0u};
-      a[i] = __builtin_bit_cast(bf16x8, v);
-    }
-    u32x4 v = *reinterpret_cast<const u32x4*>(brow + kk + off);
-    if (!bvalid) v = u32x4{0u, 0u, 0u, 0u};
-    b = __builtin_bit_cast(bf16x8, v);
+    for (int i = 0; i < FM; ++i) a[i] = __builtin_bit_cast(bf16x8, buf_load16(ra, voa[i] + 64u * d, soff));
+    b = __builtin_bit_cast(bf16x8, buf_load16(rb, vob + 64u * d, soff));
   }
   __device__ __forceinline__ void mma(const bf16x8 (&a)[FM], const bf16x8& b, Acc& acc) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) acc.v[i][0] = mfma16(a[i], b, acc.v[i][0]);
   }
-  // One leaf of spl 32-k blocks, two blocks per iteration so the next loads
-  // are in flight while the current MFMAs run.
+  __device__ __forceinline__ void mma_first(const bf16x8 (&a)[FM], const bf16x8& b, Acc& acc) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) acc.v[i][0] = mfma16(a[i], b, f32x4{0.f, 0.f, 0.f, 0.f});
+  }
+  // One leaf, spl a multiple of DD: a ring of DD blocks in registers, each
+  // slot refilled right after its MFMA. Slots are static and the loop body
+  // has no branches, so DD blocks stay in flight. The chain is the plain
+  // ascending k of the leaf whatever DD is.
+  template <int DD>
+  __device__ __forceinline__ void leaf_ring(Acc& acc) {
+    bf16x8 a[DD][FM], b[DD];
+#pragma unroll
+    for (int d = 0; d < DD; ++d) load(0, d, a[d], b[d]);
+    if (spl == DD) {
+      mma_first(a[0], b[0], acc);
+#pragma unroll
+      for (int d = 1; d < DD; ++d) mma(a[d], b[d], acc);
+      return;
+    }
+    mma_first(a[0], b[0], acc);
+    load(DD, 0, a[0], b[0]);
+#pragma unroll
+    for (int d = 1; d < DD; ++d) {
+      mma(a[d], b[d], acc);
+      load(DD, d, a[d], b[d]);
+    }
+#pragma clang loop unroll(disable)
+    for (int s = DD; s + DD < spl; s += DD) {
+#pragma unroll
+      for (int d = 0; d < DD; ++d) {
+        mma(a[d], b[d], acc);
+        load((uint32_t)(s + DD), d, a[d], b[d]);
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < DD; ++d) mma(a[d], b[d], acc);
+  }
+  // Ring depth: the weight bytes in flight over the grid are
+  // N/16 * leaves * depth KiB whatever FM is, so the ring is as deep as the
+  // registers allow: up to 8 blocks for 16-32 rows, 4 for 48-64, the largest
+  // power of two that divides spl.
+  static constexpr int D = FM <= 2 ? 8 : 4;
   __device__ __forceinline__ void leaf(Acc& acc) {
-    acc_zero(acc);
-    bf16x8 a0[FM], a1[FM], b0, b1;
-    load(k, a0, b0);
-    int s = 0;
-    for (; s + 2 <= spl; s += 2) {
-      load(k + 32, a1, b1);
-      mma(a0, b0, acc);
-      if (s + 2 < spl) load(k + 64, a0, b0);
-      mma(a1, b1, acc);
-      k += 64;
-    }
-    if (s < spl) {  // odd block count
-      mma(a0, b0, acc);
-      k += 32;
-    }
+    if (D >= 8 && spl % 8 == 0) leaf_ring<(D >= 8 ? 8 : 1)>(acc);
+    else if (D >= 4 && spl % 4 == 0) leaf_ring<(D >= 4 ? 4 : 1)>(acc);
+    else if (spl % 2 == 0) leaf_ring<2>(acc);
+    else leaf_ring<1>(acc);
   }
 };
 
@@ -549,20 +578,24 @@ __global__ __launch_bounds__(64 * NW) void gemm_stream_kernel(TileParams p) {
   const int z = blockIdx.z;
   const int leaf = p.leaf_lo + z * NW + w;  // one leaf per wave
 
+  // Launch guarantees 16 * FM * K * 2 < 2^32, so every byte offset below
+  // fits the 32-bit buffer range.
   Ctx c;
-  c.lane = lane;
   c.spl = p.kl / 32;
-  c.k = (int64_t)leaf * p.kl;
+  c.kb = (uint32_t)__builtin_amdgcn_readfirstlane(leaf) * (uint32_t)p.kl * 2u;
+  const int64_t arows = p.M - m0 < 16 * FM ? p.M - m0 : 16 * FM;
+  const int64_t brows = p.N - n0 < 16 ? p.N - n0 : 16;
+  c.ra = make_rsrc(p.A + m0 * p.K, (uint32_t)(arows * p.K * 2));
+  c.rb = make_rsrc(p.B + n0 * p.K, (uint32_t)(brows * p.K * 2));
+  const uint32_t kq = 16u * (uint32_t)(lane >> 4);  // this lane's 8 k values
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
-    const int64_t row = m0 + 16 * i + (lane & 15);
-    c.avalid[i] = row < p.M;
-    c.arow[i] = p.A + (c.avalid[i] ? row : 0) * p.K;
+    const int r = 16 * i + (lane & 15);
+    c.voa[i] = (uint32_t)(r < arows ? r : 0) * (uint32_t)p.K * 2u + kq;
   }
   {
-    const int64_t col = n0 + (lane & 15);
-    c.bvalid = col < p.N;
-    c.brow = p.B + (c.bvalid ? col : 0) * p.K;
+    const int r = lane & 15;
+    c.vob = (uint32_t)(r < brows ? r : 0) * (uint32_t)p.K * 2u + kq;
   }
   typename Ctx::Acc acc;
   c.leaf(acc);
@@ -722,7 +755,7 @@ hipError_t launch_gemm(const GemmLaunch& g, hipStream_t s) {
     dim3 grid((unsigned)(slots * tiles_n), 1u, (unsigned)g.groups);
     return g.out_bf16 ? ring_dispatch<true, true>(p, grid, g.nl, s) : ring_dispatch<false, true>(p, grid, g.nl, s);
   }
-  if (g.M <= 64) {
+  if (g.M <= 64 && g.K < (int64_t{1} << 25)) {  // stream kernel: 32-bit buffer offsets
     const int fm = (int)((g.M + 15) / 16);
     // each wave owns one leaf; groups of nl leaves become nl waves per WG
     dim3 grid((unsigned)((g.N + 15) / 16), 1u, (unsigned)g.groups);

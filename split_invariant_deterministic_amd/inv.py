@@ -166,8 +166,11 @@ def _out_torch_dtype(c):
 
 # ------------------------------------------------------------------ GEMM
 
-def gemm(A, B, c, out=None, ws=None):
-    """C [M,N] = tree over K leaves of A [M,K] . B[N,K]^T (inv_gemm)."""
+def gemm(A, B, c, out=None, ws=None, use_ws=True):
+    """C [M,N] = tree over K leaves of A [M,K] . B[N,K]^T (inv_gemm).
+
+    The workspace the library asks for is allocated unless ``ws`` is given;
+    with ranks == 1 it is optional (``use_ws=False`` runs without it)."""
     _need(A, torch.bfloat16, "A", 2)
     _need(B, torch.bfloat16, "B", 2)
     M, K = A.shape
@@ -179,11 +182,9 @@ def gemm(A, B, c, out=None, ws=None):
     _need(out, _out_torch_dtype(c), "out", 2)
     if tuple(out.shape) != (M, N):
         raise ValueError("out has the wrong shape")
-    nbytes = 0
-    if c.ranks > 1:
-        nbytes = workspace_bytes(c, OP_GEMM, M, N, K)
-        if ws is None:
-            ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=A.device)
+    nbytes = workspace_bytes(c, OP_GEMM, M, N, K)
+    if ws is None and nbytes > 0 and (use_ws or c.ranks > 1):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=A.device)
     wsz = ws.numel() * ws.element_size() if ws is not None else 0
     _call("inv_gemm", ctypes.byref(c), _ptr(A), _ptr(B), _ptr(out), M, N, K, _ptr(ws), wsz, _stream())
     return out

@@ -77,6 +77,12 @@ def test_contract_violations():
 def test_workspace_sizes():
     inv = _inv()
     assert inv.workspace_bytes(inv.contract(ranks=1), inv.OP_GEMM, 64, 128, 4096) == 0
+    assert inv.workspace_bytes(inv.contract(ranks=1), inv.OP_GEMM, 4096, 12288, 4096) == 0
+    # few 128x128 tiles: optional leaf groups (32 tiles x 8 groups at M=128, N=4096)
+    assert inv.workspace_bytes(inv.contract(ranks=1), inv.OP_GEMM, 128, 4096, 12288) == 8 * 128 * 4096 * 4
+    assert inv.workspace_bytes(inv.contract(ranks=1), inv.OP_GEMM, 512, 4096, 4096) == 2 * 512 * 4096 * 4
+    assert inv.workspace_bytes(inv.contract(ranks=1), inv.OP_GEMM, 512, 12288, 4096) == 0  # 384 tiles
+    assert inv.workspace_bytes(inv.contract(leaves=2), inv.OP_GEMM, 128, 1024, 4096) == 2 * 128 * 1024 * 4
     assert inv.workspace_bytes(inv.contract(ranks=4), inv.OP_GEMM, 64, 128, 4096) == 4 * 64 * 128 * 4
     assert inv.workspace_bytes(inv.contract(), inv.OP_DECODE_ATTN, 3, 32, 128) == 3 * 32 * 16 * 130 * 4
     assert inv.workspace_bytes(inv.contract(ranks=3), inv.OP_GEMM, 64, 128, 4096) == ctypes.c_size_t(-1).value

@@ -127,10 +127,12 @@ def test_dense_batch_invariance_and_sampled_oracle(inv, dense_inputs, K, N):
     X, W = dense_inputs[(K, N)]
     c = inv.contract(leaves=8)
     full = inv.gemm(X, W, c)
-    for M in (1, 7, 64, 512):
+    for M in (1, 7, 16, 17, 63, 64, 65, 128, 200, 512):
         part = inv.gemm(X[:M].contiguous(), W, c)
         n, bad, dmax = mismatch_report(part, full[:M])
         assert bad == 0, f"M={M}: {bad}/{n} mismatches, max {dmax}"
+        # without the optional workspace: the single-pass kernel, same bits
+        assert bitwise_equal(inv.gemm(X[:M].contiguous(), W, c, use_ws=False), part), M
     # rows in another order give the same rows
     perm = torch.randperm(512, generator=torch.Generator().manual_seed(3)).to(DEV)
     pm = inv.gemm(X[perm].contiguous(), W, c)
