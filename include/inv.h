@@ -128,6 +128,72 @@ size_t inv_workspace_bytes(const inv_contract* c, int op, int64_t d0, int64_t d1
 const char* inv_status_string(inv_status s);
 
 /* ------------------------------------------------------------------------
+ * Serialized contract and identity digests ([IsoExec] "Unified execution
+ * contract": cases, a composition mapping each region to an implementation
+ * and its pinned constants, claims of the proven parallel sizes, and SHA-256
+ * identities -- semantic (the logical model), numerical_policy (every choice
+ * that can move a bit) and deployment (settings proven not to move bits).
+ * Two runtimes exchange the digests and refuse to run on a mismatch of the
+ * semantic or numerical_policy digest). Host only; nothing is launched.
+ * ------------------------------------------------------------------------ */
+
+/* Regions of the forward path a composition can pin. */
+typedef enum inv_region {
+  INV_REGION_NORM = 1,        /* RMSNorm                                   */
+  INV_REGION_LINEAR = 2,      /* dense projections (inv_gemm)              */
+  INV_REGION_LM_HEAD = 3,     /* LM-head logits (inv_gemm, fp32 boundary)  */
+  INV_REGION_LOGPROB = 4,     /* selected-token log-softmax                */
+  INV_REGION_ATTENTION = 5,   /* split-KV attention                        */
+  INV_REGION_MOE_ROUTE = 6,   /* top-k routing                             */
+  INV_REGION_MOE_EXPERTS = 7, /* grouped expert GEMMs                      */
+  INV_REGION_MOE_COMBINE = 8  /* fixed-order combine                       */
+} inv_region;
+
+/* One composition entry: a region and the contract pinned for it. */
+typedef struct inv_region_contract {
+  int32_t region;       /* inv_region                                        */
+  uint32_t reserved;    /* must be 0                                         */
+  inv_contract contract;
+} inv_region_contract;
+
+typedef enum inv_digest_kind {
+  INV_DIGEST_SEMANTIC = 1,
+  INV_DIGEST_NUMERICAL_POLICY = 2,
+  INV_DIGEST_DEPLOYMENT = 3
+} inv_digest_kind;
+
+/* Canonical JSON of a composition of n entries (each region at most once, in
+ * any order; written sorted by region): compact, fixed key order, integers
+ * and ASCII strings only, floats as IEEE-754 bit patterns, so one
+ * composition has one byte sequence. Layout:
+ *   {"ExecutionContract":{"cases":[..],"composition":[..],"claims":{..},
+ *    "semantic":{..},"deployment":{..},"identities":{"semantic":hex,
+ *    "numerical_policy":hex,"deployment":hex}}}
+ * The digests are SHA-256 of: the "semantic" value; the text
+ * {"cases":..,"composition":..,"claims":..}; the "deployment" value.
+ * Ranks are deployment (each proven rank count gives the same bits); leaves,
+ * chunks, splits, tree, dtypes and implementation ids are numerical policy;
+ * the region set, RMSNorm eps and the MoE top-k are semantic.
+ * *len receives the text length without the terminating NUL. buf == NULL is
+ * a size query; cap < *len + 1 returns INV_E_ARG and writes nothing. Each
+ * entry's contract is validated as its entry point would (INV_E_CONTRACT /
+ * INV_E_TOPOLOGY); an unknown or repeated region is INV_E_ARG. */
+inv_status inv_contract_json(const inv_region_contract* entries, size_t n, char* buf, size_t cap,
+                             size_t* len);
+
+/* The SHA-256 digest `kind` of the composition into digest[32]. */
+inv_status inv_contract_digest(const inv_region_contract* entries, size_t n, int kind,
+                               uint8_t digest[32]);
+
+/* INV_OK if the composition's digest `kind` equals expected[32] (a peer's),
+ * INV_E_CONTRACT if it differs: the caller refuses to run. */
+inv_status inv_contract_verify(const inv_region_contract* entries, size_t n, int kind,
+                               const uint8_t expected[32]);
+
+/* SHA-256 (FIPS 180-4) of `bytes` bytes of host memory. */
+inv_status inv_sha256(const void* data, size_t bytes, uint8_t digest[32]);
+
+/* ------------------------------------------------------------------------
  * GEMM with K leaves  ([IsoExec] "Parallelism-invariant kernels";
  * [NovaSky] "Making kernels parallelism-invariant"; [RLK] section 7, GEMM
  * merged in FP32 then written as BF16)

@@ -99,7 +99,28 @@ _lib.inv_workspace_bytes.restype = _SZ
 _lib.inv_status_string.argtypes = [ctypes.c_int]
 _lib.inv_status_string.restype = ctypes.c_char_p
 
-EXPORTS = sorted(list(_SIGS) + ["inv_workspace_bytes", "inv_status_string"])
+
+class RegionContract(ctypes.Structure):
+    _fields_ = [("region", ctypes.c_int32), ("reserved", ctypes.c_uint32), ("contract", Contract)]
+
+
+REGIONS = {"norms.rms": 1, "linear": 2, "lm_head": 3, "logprob": 4, "attention": 5, "moe.route": 6,
+           "moe.experts": 7, "moe.combine": 8}
+DIGEST_SEMANTIC, DIGEST_NUMERICAL_POLICY, DIGEST_DEPLOYMENT = 1, 2, 3
+_RCP = ctypes.POINTER(RegionContract)
+_D32 = ctypes.c_uint8 * 32
+for _name, _args in {
+    "inv_contract_json": [_RCP, _SZ, ctypes.c_char_p, _SZ, ctypes.POINTER(_SZ)],
+    "inv_contract_digest": [_RCP, _SZ, ctypes.c_int, _D32],
+    "inv_contract_verify": [_RCP, _SZ, ctypes.c_int, _D32],
+    "inv_sha256": [ctypes.c_char_p, _SZ, _D32],
+}.items():
+    _f = getattr(_lib, _name)
+    _f.argtypes = _args
+    _f.restype = ctypes.c_int
+
+EXPORTS = sorted(list(_SIGS) + ["inv_workspace_bytes", "inv_status_string", "inv_contract_json",
+                                "inv_contract_digest", "inv_contract_verify", "inv_sha256"])
 
 
 def _call(name, *args):
@@ -134,6 +155,49 @@ def contract_check(c, op, K=0):
 
 def workspace_bytes(c, op, d0, d1, d2):
     return _lib.inv_workspace_bytes(ctypes.byref(c), op, d0, d1, d2)
+
+
+# ------------------------------------------------------------------ identities
+
+def composition(entries):
+    """A C array of inv_region_contract from {region name: Contract}."""
+    arr = (RegionContract * len(entries))()
+    for i, (name, c) in enumerate(entries.items()):
+        arr[i].region = REGIONS[name] if isinstance(name, str) else int(name)
+        arr[i].contract = c
+    return arr
+
+
+def contract_json(entries):
+    """Canonical JSON text of the composition (inv_contract_json)."""
+    arr = composition(entries)
+    n = _SZ(0)
+    _call("inv_contract_json", arr, len(arr), None, 0, ctypes.byref(n))
+    buf = ctypes.create_string_buffer(n.value + 1)
+    _call("inv_contract_json", arr, len(arr), buf, n.value + 1, ctypes.byref(n))
+    return buf.value.decode("ascii")
+
+
+def contract_digest(entries, kind):
+    """32-byte SHA-256 identity `kind` of the composition (inv_contract_digest)."""
+    arr = composition(entries)
+    d = _D32()
+    _call("inv_contract_digest", arr, len(arr), kind, d)
+    return bytes(d)
+
+
+def contract_verify(entries, kind, expected):
+    """Raises InvError (status E_CONTRACT) if the peer's digest differs."""
+    arr = composition(entries)
+    if len(expected) != 32:
+        raise ValueError("a digest is 32 bytes")
+    _call("inv_contract_verify", arr, len(arr), kind, _D32(*expected))
+
+
+def sha256(data):
+    d = _D32()
+    _call("inv_sha256", bytes(data), len(data), d)
+    return bytes(d)
 
 
 # ------------------------------------------------------------------ helpers
