@@ -292,7 +292,7 @@ def main():
         result["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                               "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                               "traffic": recorded_traffic(),
-                              "kernel": "inv_gemm (gemm_tile_kernel), 4096x12288x4096 + 4096x4096x12288, "
+                              "kernel": "inv_gemm (gemm_ring_kernel<8, 64, bf16>), 4096x12288x4096 + 4096x4096x12288, "
                                         "2*M*N*K flops per launch over the mean launch time"}
         result["rmsnorm_gbs"] = round(2 * 2 * M * Hd / (ms["rmsnorm"] * 1e-3) / 1e9, 1)
     if "lmhead" in stages:
