@@ -13,7 +13,9 @@ synthetic input, every stage in the library's HIP kernels:
   moe     8192 tokens, hidden 2048, 128 experts, top-8, expert FFN
           2048->768->2048 with 8 K-leaves, fixed expert-order combine
   lmhead  RMSNorm -> invariant GEMM 4096->151936 (fp32 logits) -> 64-chunk
-          selected-token logprob, 4096 tokens
+          selected-token logprob, 4096 tokens; the fused LM head (logprob
+          from 16-column blocks in the GEMM epilogue, no stored logits) is
+          timed beside the step, not inside it
 
 Inputs are resident in HBM before the timed region. ``value`` is the
 invariant GEMM throughput of the dense stage (its FLOPs over the time of its
@@ -235,6 +237,27 @@ def main():
     ms_step = wall * 1e3 / args.steps
     log(f"timed steps done: {ms_step:.2f} ms/step")
 
+    # ------------------------------------------------------------ fused LM head (outside the step)
+    # The same LM head with the logprob reduced in the GEMM epilogue (16-column
+    # vocabulary blocks, logits never stored): timed beside the step's unfused
+    # GEMM + logprob, not added to it.
+    if "lmhead" in stages:
+        V = lm["W"].shape[0]
+        lm_ws = inv.block16_workspace(M, V, dev)
+        hn = inv.rmsnorm(lm["h"], gamma, cn)
+        Tx = Timer(torch)
+        for i in range(max(3, min(args.steps, 10)) + 2):
+            if i == 2:
+                torch.cuda.synchronize()
+                Tx.reset()
+            Tx.start("lmhead_fused")
+            inv.lmhead_logprob(hn, lm["W"], lm["targets"], c8f, ws=lm_ws)
+            Tx.stop("lmhead_fused")
+        torch.cuda.synchronize()
+        ms["lmhead_fused"] = Tx.mean_ms("lmhead_fused")
+        del lm_ws
+        log("fused LM head timed")
+
     # ------------------------------------------------------------ fast paths
     Tf = Timer(torch)
     fast = {}
@@ -303,6 +326,9 @@ def main():
         lm_ms = ms["lm_rmsnorm"] + ms["gemm_lmhead"] + ms["logprob"]
         result["lmhead_logprob_tokens_per_s"] = round(M / (lm_ms * 1e-3), 1)
         result["gemm_lmhead_tflops"] = round(2.0 * M * V * Hd / (ms["gemm_lmhead"] * 1e-3) / 1e12, 2)
+        fused_ms = ms["lm_rmsnorm"] + ms["lmhead_fused"]
+        result["lmhead_fused_logprob_tokens_per_s"] = round(M / (fused_ms * 1e-3), 1)
+        result["lmhead_fused_speedup"] = round(lm_ms / fused_ms, 3)
     if "attn" in stages:
         result["attn_gbs"] = round(4096.0 * sumL / (ms["attn"] * 1e-3) / 1e9, 1)
     if "moe" in stages:
@@ -326,6 +352,8 @@ def main():
     if "lmhead" in stages:
         add("inv_gemm lm head", "mfma", 2.0 * M * V * Hd, ms["gemm_lmhead"], PEAK_BF16_TFLOPS, "TFLOP/s")
         add("inv_logprob 4096x151936", "hbm", 4.0 * V * M, ms["logprob"], PEAK_HBM_GBS, "GB/s")
+        add("inv_lmhead_logprob (fused) 4096x151936x4096", "mfma", 2.0 * M * V * Hd, ms["lmhead_fused"],
+            PEAK_BF16_TFLOPS, "TFLOP/s")
     if "attn" in stages:
         add("inv_decode_attn B=256", "hbm", 4096.0 * sumL, ms["attn"], PEAK_HBM_GBS, "GB/s")
     if "moe" in stages:

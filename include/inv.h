@@ -110,7 +110,9 @@ typedef enum inv_op {
   INV_OP_DECODE_ATTN = 5,
   INV_OP_MOE_ROUTE = 6,
   INV_OP_MOE_GEMM = 7,
-  INV_OP_MOE_COMBINE = 8
+  INV_OP_MOE_COMBINE = 8,
+  INV_OP_LMHEAD_LOGPROB = 9,
+  INV_OP_LOGPROB_BLOCK16 = 10
 } inv_op;
 
 /* Host-only contract validation for `op`; the same check every entry point
@@ -121,6 +123,8 @@ inv_status inv_contract_check(const inv_contract* c, int op, int64_t K);
  *   INV_OP_GEMM:        d0 = M, d1 = N, d2 = K  -> ranks*M*N*4 when ranks > 1;
  *                       with ranks == 1 the optional leaf-group size (or 0)
  *   INV_OP_DECODE_ATTN: d0 = Tq, d1 = Hq, d2 = D -> Tq*Hq*split_kv*(D+2)*4
+ *   INV_OP_LMHEAD_LOGPROB, INV_OP_LOGPROB_BLOCK16: d0 = M, d1 = V, d2 = K
+ *                       -> M*ceil(V/16)*8 + M*4
  * Returns (size_t)-1 if the contract is invalid. Host only. */
 size_t inv_workspace_bytes(const inv_contract* c, int op, int64_t d0, int64_t d1, int64_t d2);
 
@@ -146,7 +150,8 @@ typedef enum inv_region {
   INV_REGION_ATTENTION = 5,   /* split-KV attention                        */
   INV_REGION_MOE_ROUTE = 6,   /* top-k routing                             */
   INV_REGION_MOE_EXPERTS = 7, /* grouped expert GEMMs                      */
-  INV_REGION_MOE_COMBINE = 8  /* fixed-order combine                       */
+  INV_REGION_MOE_COMBINE = 8, /* fixed-order combine                       */
+  INV_REGION_LMHEAD_LOGPROB = 9 /* fused LM head + logprob (16-col blocks) */
 } inv_region;
 
 /* One composition entry: a region and the contract pinned for it. */
@@ -364,6 +369,47 @@ inv_status inv_moe_route(const inv_contract* c, const float* logits, int32_t* id
 inv_status inv_moe_permute(const inv_contract* c, const int32_t* ids, int32_t* offsets,
                            int32_t* rows, int32_t* slot, int64_t T, int32_t E,
                            hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Fused LM head + selected-token log-probability.
+ *
+ * [RLK] section 4: the log-probability of the selected token is its logit
+ * minus the LSE over the vocabulary, and vocabulary blocks carry local
+ * (m_j, s_j) statistics merged in an order the contract fixes; section 7:
+ * logits stay fp32. Here the vocabulary block is 16 columns -- the columns
+ * of one 16x16 MFMA output block -- so the GEMM reduces each block while the
+ * fp32 logits are still in registers and never writes the [M, V] logits.
+ *   block b = columns [16b, min(16b+16, V)), nb = ceil(V/16);
+ *   m_b = max over the block; s_b = sum of exp2((x - m_b) * log2e) by the
+ *     xor butterfly 1, 2, 4, 8 over the 16 columns (a balanced tree over the
+ *     column index; columns past V contribute nothing);
+ *   (m, s) = balanced tree over b, padded with (-inf, 0) to a power of two
+ *     (the merge of the pages, exact on the padding);
+ *   LSE = m + log2(s) * ln2; lp = x[t] - LSE, NaN when t is outside [0, V).
+ * The logits x are bitwise inv_gemm's fp32 output, so the fused result is
+ * bitwise inv_logprob_block16 applied to inv_gemm's logits, for every M.
+ * This schedule differs from inv_logprob's C-chunk schedule (a separate
+ * contract: same mathematics, other rounding).
+ * ------------------------------------------------------------------------ */
+
+/* out[m] = lp of target[m] for rows h [M, K] bf16 against W [V, K] bf16
+ * (logits = inv_gemm with c->leaves K-leaves and fp32 boundary dtype:
+ * c->out_dtype must be INV_FP32, c->tree BALANCED, c->ranks 1).
+ * target [M] int32, out [M] fp32. Workspace: ws_bytes >=
+ * inv_workspace_bytes(INV_OP_LMHEAD_LOGPROB, M, V, K), 8-byte aligned; on
+ * return it holds the block statistics [M, nb, 2] fp32 followed by the
+ * target logits [M]. V <= 262144. */
+inv_status inv_lmhead_logprob(const inv_contract* c, const void* h, const void* W, const int32_t* target,
+                              float* out, int64_t M, int64_t V, int64_t K, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
+
+/* The same 16-column block schedule from stored fp32 logits [M, ldl]
+ * (ldl >= V): the unfused counterpart of inv_lmhead_logprob. c->tree may be
+ * LEFT_FOLD (the merge over blocks left to right) as the contrasting
+ * schedule. Workspace and layout as for inv_lmhead_logprob. */
+inv_status inv_logprob_block16(const inv_contract* c, const float* logits, int64_t ldl, const int32_t* target,
+                               float* out, int64_t M, int64_t V, void* ws, size_t ws_bytes,
+                               hipStream_t stream);
 
 /* Grouped GEMM: for expert e, grouped rows r in [offsets[e], offsets[e+1]):
  * Y[r, :] = inv_gemm row of A = X[rows[r], :] (or X[r, :] if rows is NULL)

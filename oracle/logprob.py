@@ -17,6 +17,13 @@ Readings taken: C chunks with chunk j = [floor(j V / C), floor((j+1) V / C));
 the merge order is the balanced tree over chunks; a target id outside
 [0, V) yields NaN.
 
+LM-head schedule (the fused GEMM + logprob): blocks of a fixed width of 16
+columns, block b = [16 b, min(16 b + 16, V)), merged by the balanced tree
+over the block index after padding the block list with the identity
+(-inf, 0) to a power of two (for a power-of-two count this is the same tree
+as ``merge_tree``; for other counts the padding fixes where the short
+subtree sits). ``block_stats`` and ``merge_tree_padded`` write it out.
+
 ``logprob`` is the plain definition in float64. ``chunk_stats`` and
 ``merge_tree`` evaluate the chunked form in float64 (equal to the plain form
 up to float64 rounding); they localise errors and pin the merge formula.
@@ -83,3 +90,49 @@ def merge_tree(ms, ss, schedule=BALANCED):
     items = [(ms[:, j], ss[:, j]) for j in range(ms.shape[1])]
     m, s = combine(items, merge, schedule)
     return m + np.log(s)
+
+
+def block_bounds(V, width=16):
+    """Fixed-width vocabulary blocks [w b, min(w b + w, V))."""
+    return [(a, min(a + width, V)) for a in range(0, V, width)]
+
+
+def block_stats(logits, width=16):
+    """(m_b, s_b) per row and fixed-width block in float64, arrays [M, nb]."""
+    x = np.asarray(logits, dtype=np.float64)
+    M, V = x.shape
+    bounds = block_bounds(V, width)
+    ms = np.empty((M, len(bounds)))
+    ss = np.empty((M, len(bounds)))
+    for j, (a, b) in enumerate(bounds):
+        blk = x[:, a:b]
+        ms[:, j] = blk.max(axis=1)
+        ss[:, j] = np.sum(np.exp(blk - ms[:, j:j + 1]), axis=1)
+    return ms, ss
+
+
+def pad_pow2(items, identity):
+    """items followed by copies of identity up to the next power of two."""
+    P = 1
+    while P < len(items):
+        P *= 2
+    return list(items) + [identity] * (P - len(items))
+
+
+def merge_tree_padded(ms, ss):
+    """LSE per row: balanced tree over the blocks padded with (-inf, 0) to 2^k."""
+    M, n = ms.shape
+    items = pad_pow2([(ms[:, j], ss[:, j]) for j in range(n)], (np.full(M, -np.inf), np.zeros(M)))
+    m, s = combine(items, merge, BALANCED)
+    return m + np.log(s)
+
+
+def logprob_blocks(logits, target, width=16):
+    """lp through the block schedule, float64 (equals ``logprob`` up to rounding)."""
+    x = np.asarray(logits, dtype=np.float64)
+    t = np.asarray(target).astype(np.int64)
+    M, V = x.shape
+    lse_ = merge_tree_padded(*block_stats(x, width))
+    ok = (t >= 0) & (t < V)
+    tl = np.where(ok, x[np.arange(M), np.clip(t, 0, V - 1)], np.nan)
+    return tl - lse_

@@ -124,6 +124,14 @@ inv_status inv_contract_check(const inv_contract* c, int op, int64_t K) {
       return check_logprob_contract(c, 0);
     case INV_OP_DECODE_ATTN:
       return check_attn_contract(c);
+    case INV_OP_LMHEAD_LOGPROB: {
+      inv_status s = check_gemm_contract(c, K);
+      if (s != INV_OK) return s;
+      if (c->out_dtype != INV_FP32) return INV_E_CONTRACT;
+      return c->ranks == 1 ? INV_OK : INV_E_UNSUPPORTED;
+    }
+    case INV_OP_LOGPROB_BLOCK16:
+      return check_contract(c);
     default:
       return INV_E_ARG;
   }
@@ -141,6 +149,10 @@ size_t inv_workspace_bytes(const inv_contract* c, int op, int64_t d0, int64_t d1
     case INV_OP_DECODE_ATTN:
       if (check_attn_contract(c) != INV_OK) return (size_t)-1;
       return (size_t)d0 * (size_t)d1 * (size_t)c->split_kv * (size_t)(d2 + 2) * sizeof(float);
+    case INV_OP_LMHEAD_LOGPROB:
+    case INV_OP_LOGPROB_BLOCK16:
+      if (inv_contract_check(c, op, d2) != INV_OK || d1 <= 0 || (d1 + 15) / 16 > 16384) return (size_t)-1;
+      return (size_t)d0 * (size_t)((d1 + 15) / 16) * 8u + (size_t)d0 * 4u;
     default:
       if (inv_contract_check(c, op, d2) != INV_OK) return (size_t)-1;
       return 0;
@@ -294,6 +306,64 @@ inv_status inv_logprob(const inv_contract* c, const float* logits, int64_t ldl, 
   if (!logits || !target || !out) return INV_E_ARG;
   return hip_status(inv::launch_logprob(logits, ldl, target, out, nullptr, nullptr, M, V, (int)c->leaves, 0,
                                         (int)c->leaves, c->tree == INV_TREE_LEFT_FOLD, false, stream));
+}
+
+// ------------------------------------------------------- LM head + logprob
+
+namespace {
+constexpr int64_t kMaxBlocks16 = 16384;  // 16-column blocks per row: V <= 262144
+
+size_t block16_ws_bytes(int64_t M, int64_t V) {
+  const int64_t nb = (V + 15) / 16;
+  return (size_t)M * (size_t)nb * 8u + (size_t)M * 4u;
+}
+
+inv_status check_block16(const inv_contract* c, int64_t M, int64_t V, void* ws, size_t ws_bytes) {
+  if (M < 0 || V <= 0) return INV_E_ARG;
+  if ((V + 15) / 16 > kMaxBlocks16 || M > (int64_t)1 << 31) return INV_E_UNSUPPORTED;
+  if (M > 0 && (!ws || ws_bytes < block16_ws_bytes(M, V))) return INV_E_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) & 7u) return INV_E_ARG;  // (m, s) pairs are read as float2
+  (void)c;
+  return INV_OK;
+}
+}  // namespace
+
+inv_status inv_lmhead_logprob(const inv_contract* c, const void* h, const void* W, const int32_t* target,
+                              float* out, int64_t M, int64_t V, int64_t K, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+  inv_status s = check_gemm_contract(c, K);
+  if (s != INV_OK) return s;
+  if (c->out_dtype != INV_FP32) return INV_E_CONTRACT;  // logits are never rounded below fp32
+  if (c->ranks != 1) return INV_E_UNSUPPORTED;
+  if ((s = gemm_shape_check(h, W, out, M, V, K)) != INV_OK) return s;
+  if ((s = check_block16(c, M, V, ws, ws_bytes)) != INV_OK) return s;
+  if (M == 0) return INV_OK;
+  if (!target) return INV_E_ARG;
+  float* stats = static_cast<float*>(ws);
+  float* tlogit = stats + 2 * M * ((V + 15) / 16);
+  inv::GemmLaunch g = gemm_launch(h, W, nullptr, M, V, K, (int)(K / c->leaves), 0, (int)c->leaves, 1, false);
+  g.lp_stats = stats;
+  g.lp_tlogit = tlogit;
+  g.lp_target = target;
+  hipError_t e = inv::launch_gemm(g, stream);
+  if (e != hipSuccess) return INV_E_HIP;
+  return hip_status(inv::launch_block16_merge(stats, tlogit, target, out, M, V, false, stream));
+}
+
+inv_status inv_logprob_block16(const inv_contract* c, const float* logits, int64_t ldl, const int32_t* target,
+                               float* out, int64_t M, int64_t V, void* ws, size_t ws_bytes, hipStream_t stream) {
+  inv_status s = check_contract(c);
+  if (s != INV_OK) return s;
+  if (ldl < V) return INV_E_ARG;
+  if ((s = check_block16(c, M, V, ws, ws_bytes)) != INV_OK) return s;
+  if (M == 0) return INV_OK;
+  if (!logits || !target || !out) return INV_E_ARG;
+  float* stats = static_cast<float*>(ws);
+  float* tlogit = stats + 2 * M * ((V + 15) / 16);
+  hipError_t e = inv::launch_block16_stats(logits, ldl, target, stats, tlogit, M, V, stream);
+  if (e != hipSuccess) return INV_E_HIP;
+  return hip_status(
+      inv::launch_block16_merge(stats, tlogit, target, out, M, V, c->tree == INV_TREE_LEFT_FOLD, stream));
 }
 
 inv_status inv_logprob_partials(const inv_contract* c, const float* logits, int64_t ldl, const int32_t* target,

@@ -110,4 +110,25 @@ __device__ __forceinline__ MS lse_merge(MS a, MS b) {
   return MS{m, s};
 }
 
+// Statistics of one 16-column vocabulary block held by one lane (v[c] is
+// column c of the block; columns c >= nvalid lie past the vocabulary):
+// m = max over the valid columns (exact); s = sum of exp2((v[c] - m) * log2e)
+// over them by the balanced tree over the column index, adjacent pairs first:
+// ((e0+e1)+(e2+e3))+((e4+e5)+(e6+e7)) + (the same over columns 8..15).
+// Columns past the vocabulary contribute +0. A NaN logit makes s NaN.
+__device__ __forceinline__ MS block16_stats(const float (&v)[16], int nvalid) {
+  float m = -INFINITY;
+#pragma unroll
+  for (int c = 0; c < 16; ++c)
+    if (c < nvalid) m = fmaxf(m, v[c]);
+  float e[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) e[c] = (c < nvalid && v[c] != -INFINITY) ? exp_shifted(v[c], m) : 0.0f;
+#pragma unroll
+  for (int w = 16; w > 1; w /= 2)
+#pragma unroll
+    for (int k = 0; k < w / 2; ++k) e[k] = e[2 * k] + e[2 * k + 1];
+  return MS{m, e[0]};
+}
+
 }  // namespace inv

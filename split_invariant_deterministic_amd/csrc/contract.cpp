@@ -167,6 +167,7 @@ const RegionInfo kRegions[] = {
     {INV_REGION_MOE_ROUTE, "moe.route", INV_OP_MOE_ROUTE, "topk_softmax_lower_id_ties", 1},
     {INV_REGION_MOE_EXPERTS, "moe.experts", INV_OP_MOE_GEMM, "grouped_k_leaf_mfma_tree", 1},
     {INV_REGION_MOE_COMBINE, "moe.combine", INV_OP_MOE_COMBINE, "expert_id_leaf_tree", 1},
+    {INV_REGION_LMHEAD_LOGPROB, "lm_head_logprob", INV_OP_LMHEAD_LOGPROB, "k_leaf_mfma_tree_block16_epilogue", 1},
 };
 
 const RegionInfo* region_info(int region) {
@@ -210,6 +211,12 @@ std::string constants(const RegionInfo& r, const inv_contract& c) {
              q(tree_name(c.tree)) + acc + ",\"p_operand\":\"bf16 hi + bf16 lo\",\"out_dtype\":\"bf16\"}";
     case INV_REGION_MOE_ROUTE:
       return "{\"weights\":\"fp32 softmax over the top k\",\"ties\":\"lower expert id\"}";
+    case INV_REGION_LMHEAD_LOGPROB:
+      return "{\"leaves\":" + u(c.leaves) + ",\"tree\":" + q(tree_name(c.tree)) + acc +
+             ",\"leaf_dtype\":" + q(dtype_name(c.leaf_dtype)) + ",\"logits_dtype\":\"fp32\"" +
+             ",\"leaf_chain\":\"v_mfma_f32_16x16x32_bf16, ascending k from +0\"" +
+             ",\"vocab_block\":16,\"block_sum\":\"balanced over the column index\"" +
+             ",\"block_merge\":\"balanced, padded with (-inf, 0) to a power of two\"}";
     case INV_REGION_MOE_COMBINE:
       return "{\"leaves\":" + u(c.leaves) + ",\"tree\":" + q(tree_name(c.tree)) + acc +
              ",\"leaf_order\":\"ascending expert id\",\"out_dtype\":\"bf16\"}";
@@ -240,7 +247,8 @@ inv_status build(const inv_region_contract* e, size_t n, Sections& out) {
     if (sorted[i]->reserved != 0) return INV_E_ARG;
     const RegionInfo& r = *region_info(sorted[i]->region);
     const inv_contract& c = sorted[i]->contract;
-    const int64_t K = (r.op == INV_OP_GEMM || r.op == INV_OP_MOE_GEMM) ? (int64_t)c.leaves * 32 : 0;
+    const int64_t K =
+        (r.op == INV_OP_GEMM || r.op == INV_OP_MOE_GEMM || r.op == INV_OP_LMHEAD_LOGPROB) ? (int64_t)c.leaves * 32 : 0;
     const inv_status s = inv_contract_check(&c, r.op, K);
     if (s != INV_OK) return s;
   }
@@ -254,7 +262,9 @@ inv_status build(const inv_region_contract* e, size_t n, Sections& out) {
     comp += sep + "{\"region\":" + q(r.name) + ",\"cases\":" + kCases + ",\"impl\":{\"id\":" + q(r.impl) +
             ",\"version\":" + u(r.version) + ",\"arch\":\"gfx950\"},\"constants\":" + constants(r, c) + "}";
     topo += sep + q(r.name) + ":{\"proven_ranks\":" +
-            (r.region == INV_REGION_MOE_EXPERTS ? std::string("[1]") : proven(c.leaves)) + "}";
+            (r.region == INV_REGION_MOE_EXPERTS || r.region == INV_REGION_LMHEAD_LOGPROB ? std::string("[1]")
+                                                                                        : proven(c.leaves)) +
+            "}";
     ranks += sep + q(r.name) + ":" + u(c.ranks);
     if (r.region == INV_REGION_NORM) {
       uint32_t bits;

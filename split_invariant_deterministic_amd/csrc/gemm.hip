@@ -80,7 +80,54 @@ struct TileParams {
   int E;
   int64_t a_rows;
   int64_t b_expert_stride;
+  // logprob-statistics output mode (kOutLP): per row and 16-column block
+  float* lp_stats;           // [M, ceil(N/16)] (m, s) pairs
+  float* lp_tlogit;          // [M] logit of the row's target column
+  const int32_t* lp_target;  // [M]
 };
+
+// Output modes of the GEMM kernels: fp32 C, bf16 C, or (LM head) no C at all
+// but the vocabulary-block statistics of each row and its target's logit.
+constexpr int kOutF32 = 0, kOutBF16 = 1, kOutLP = 2;
+
+// kOutLP epilogue. A wave's fp32 result block (rows x 16*cols, in the MFMA
+// output layout) is transposed through LDS so that lane l holds row l's
+// columns; the lane then reduces each 16-column vocabulary block in
+// registers (block16_stats) and writes its (m, s), and the target's logit if
+// the row's target falls in these columns. t: this wave's LDS scratch of
+// rows x kLpStride floats; the row stride of 68 floats keeps both the
+// transposing writes and the 16-byte row reads free of bank conflicts.
+constexpr int kLpStride = 68;
+
+template <int NB>  // 16-column blocks per row held by the wave
+__device__ __forceinline__ void lp_rows_epilogue(const TileParams& p, const float* t, int64_t row, bool row_ok,
+                                                 int64_t col0, int lane) {
+  const float* mine = t + lane * kLpStride;
+  const int64_t nb = (p.N + 15) / 16;
+  const int32_t tgt = row_ok ? p.lp_target[row] : -1;
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int64_t c0 = col0 + 16 * j;
+    float v[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 f = *reinterpret_cast<const float4*>(mine + 16 * j + 4 * q);
+      v[4 * q] = f.x;
+      v[4 * q + 1] = f.y;
+      v[4 * q + 2] = f.z;
+      v[4 * q + 3] = f.w;
+    }
+    const int nvalid = (int)min(max(p.N - c0, (int64_t)0), (int64_t)16);
+    const MS st = block16_stats(v, nvalid);
+    if (row_ok && nvalid > 0) {
+      float* d = p.lp_stats + 2 * (row * nb + c0 / 16);
+      d[0] = st.m;
+      d[1] = st.s;
+    }
+  }
+  if (row_ok && (int64_t)tgt >= col0 && (int64_t)tgt < col0 + 16 * NB && (int64_t)tgt < p.N)
+    p.lp_tlogit[row] = mine[tgt - col0];
+}
 
 // ---------------------------------------------------------------- ring kernel
 //
@@ -316,7 +363,7 @@ struct RingCtx {
 template <int NL>
 constexpr int ring_bytes() { return NL == 8 ? 98304 : 131072; }
 
-template <int NL, int BK, bool OUT_BF16, bool GROUPED>
+template <int NL, int BK, int OUTM, bool GROUPED>
 __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(TileParams p) {
   constexpr int RING = ring_bytes<NL>();
   constexpr int SPILL = NL == 8 ? 65536 : 0;
@@ -461,6 +508,21 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(TileParams p) {
   // Epilogue: lane holds rows 4*(lane/16)+r of each 16x16 block, column lane%16.
   const int64_t rbase = m0 + (c.wave >> 1) * 64 + 4 * (lane >> 4);
   const int64_t cbase = n0 + (c.wave & 1) * 64 + (lane & 15);
+  if constexpr (OUTM == kOutLP) {
+    static_assert(4 * 64 * kLpStride * 4 <= RING, "the transposed tile reuses the ring");
+    block_barrier();  // every wave has consumed its last ring stage
+    float* t = reinterpret_cast<float*>(lds) + wave * 64 * kLpStride;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) t[(16 * i + 4 * (lane >> 4) + r) * kLpStride + 16 * j + (lane & 15)] = acc.v[i][j][r];
+    // the wave reads back only what it wrote; its LDS accesses complete in order
+    const int64_t row = m0 + (c.wave >> 1) * 64 + lane;
+    lp_rows_epilogue<4>(p, t, row, row < m_end, n0 + (c.wave & 1) * 64, lane);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -480,7 +542,7 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(TileParams p) {
         if (col < p.N) {
           const int64_t off = (int64_t)z * p.c_group_stride + row * p.N + col;
           const float v = bad ? __builtin_nanf("") : acc.v[i][j][r];
-          if constexpr (OUT_BF16)
+          if constexpr (OUTM == kOutBF16)
             reinterpret_cast<uint16_t*>(p.C)[off] = f32_to_bf16_bits(v);
           else
             reinterpret_cast<float*>(p.C)[off] = v;
@@ -568,10 +630,11 @@ struct StreamCtx {
   }
 };
 
-template <int FM, int NW, bool OUT_BF16>
+template <int FM, int NW, int OUTM>
 __global__ __launch_bounds__(64 * NW) void gemm_stream_kernel(TileParams p) {
   using Ctx = StreamCtx<FM>;
   __shared__ float xch[NW > 1 ? NW : 1][FM * 4 * 64];
+  __shared__ __attribute__((aligned(16))) float lp_buf[OUTM == kOutLP ? 64 * kLpStride : 4];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t n0 = (int64_t)blockIdx.x * 16;
   const int64_t m0 = (int64_t)blockIdx.y * 16 * FM;
@@ -620,6 +683,18 @@ __global__ __launch_bounds__(64 * NW) void gemm_stream_kernel(TileParams p) {
   }
   if (w != 0) return;
   const int64_t col = n0 + (lane & 15);
+  if constexpr (OUTM == kOutLP) {
+    // wave 0 alone from here on: the 16*FM x 16 block transposed through
+    // LDS, lane l < 16*FM owns row l (the other lanes' results are dropped)
+    float* t = lp_buf;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) t[(16 * i + 4 * (lane >> 4) + r) * kLpStride + (lane & 15)] = acc.v[i][0][r];
+    const int64_t row = m0 + lane;
+    lp_rows_epilogue<1>(p, t, row, lane < 16 * FM && row < p.M, n0, lane);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -627,7 +702,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_stream_kernel(TileParams p) {
       const int64_t row = m0 + 16 * i + 4 * (lane >> 4) + r;
       if (row < p.M && col < p.N) {
         const int64_t off = (int64_t)z * p.c_group_stride + row * p.N + col;
-        if constexpr (OUT_BF16)
+        if constexpr (OUTM == kOutBF16)
           reinterpret_cast<uint16_t*>(p.C)[off] = f32_to_bf16_bits(acc.v[i][0][r]);
         else
           reinterpret_cast<float*>(p.C)[off] = acc.v[i][0][r];
@@ -672,10 +747,10 @@ __global__ __launch_bounds__(256) void cast_bf16_kernel(const float* __restrict_
 // ------------------------------------------------------------------ dispatch
 
 #define INV_RING_CASE(NL_, BK_)                                                                              \
-  hipLaunchKernelGGL((gemm_ring_kernel<NL_, BK_, OUT_BF16, GROUPED>), grid, dim3(256), 0, s, p);             \
+  hipLaunchKernelGGL((gemm_ring_kernel<NL_, BK_, OUTM, GROUPED>), grid, dim3(256), 0, s, p);                 \
   break;
 
-template <bool OUT_BF16, bool GROUPED>
+template <int OUTM, bool GROUPED>
 hipError_t ring_dispatch(const TileParams& p, dim3 grid, int nl, hipStream_t s) {
   const bool bk64 = p.kl % 64 == 0;  // else the leaf is an odd multiple of 32
   switch (nl * 2 + (bk64 ? 1 : 0)) {
@@ -693,25 +768,25 @@ hipError_t ring_dispatch(const TileParams& p, dim3 grid, int nl, hipStream_t s) 
 }
 #undef INV_RING_CASE
 
-template <int FM, bool OUT_BF16>
+template <int FM, int OUTM>
 hipError_t stream_dispatch_nw(const TileParams& p, dim3 grid, int nw, hipStream_t s) {
   switch (nw) {
-    case 1: hipLaunchKernelGGL((gemm_stream_kernel<FM, 1, OUT_BF16>), grid, dim3(64), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((gemm_stream_kernel<FM, 2, OUT_BF16>), grid, dim3(128), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((gemm_stream_kernel<FM, 4, OUT_BF16>), grid, dim3(256), 0, s, p); break;
-    case 8: hipLaunchKernelGGL((gemm_stream_kernel<FM, 8, OUT_BF16>), grid, dim3(512), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((gemm_stream_kernel<FM, 1, OUTM>), grid, dim3(64), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((gemm_stream_kernel<FM, 2, OUTM>), grid, dim3(128), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((gemm_stream_kernel<FM, 4, OUTM>), grid, dim3(256), 0, s, p); break;
+    case 8: hipLaunchKernelGGL((gemm_stream_kernel<FM, 8, OUTM>), grid, dim3(512), 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <bool OUT_BF16>
+template <int OUTM>
 hipError_t stream_dispatch(const TileParams& p, int fm, dim3 grid, int nw, hipStream_t s) {
   switch (fm) {
-    case 1: return stream_dispatch_nw<1, OUT_BF16>(p, grid, nw, s);
-    case 2: return stream_dispatch_nw<2, OUT_BF16>(p, grid, nw, s);
-    case 3: return stream_dispatch_nw<3, OUT_BF16>(p, grid, nw, s);
-    case 4: return stream_dispatch_nw<4, OUT_BF16>(p, grid, nw, s);
+    case 1: return stream_dispatch_nw<1, OUTM>(p, grid, nw, s);
+    case 2: return stream_dispatch_nw<2, OUTM>(p, grid, nw, s);
+    case 3: return stream_dispatch_nw<3, OUTM>(p, grid, nw, s);
+    case 4: return stream_dispatch_nw<4, OUTM>(p, grid, nw, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -748,22 +823,30 @@ hipError_t launch_gemm(const GemmLaunch& g, hipStream_t s) {
   p.E = g.E;
   p.a_rows = g.a_rows;
   p.b_expert_stride = g.b_expert_stride;
+  p.lp_stats = g.lp_stats;
+  p.lp_tlogit = g.lp_tlogit;
+  p.lp_target = g.lp_target;
+  const bool lp = g.lp_stats != nullptr;
+  if (lp && (g.offsets || g.groups != 1)) return hipErrorInvalidValue;  // statistics need whole trees
 
   if (g.offsets) {  // grouped: row-tile slots = an upper bound on sum_e ceil(count_e / 128)
     const int64_t slots = g.M / 128 + g.E;
     const int64_t tiles_n = (g.N + 127) / 128;
     dim3 grid((unsigned)(slots * tiles_n), 1u, (unsigned)g.groups);
-    return g.out_bf16 ? ring_dispatch<true, true>(p, grid, g.nl, s) : ring_dispatch<false, true>(p, grid, g.nl, s);
+    return g.out_bf16 ? ring_dispatch<kOutBF16, true>(p, grid, g.nl, s)
+                      : ring_dispatch<kOutF32, true>(p, grid, g.nl, s);
   }
   if (g.M <= 64 && g.K < (int64_t{1} << 25)) {  // stream kernel: 32-bit buffer offsets
     const int fm = (int)((g.M + 15) / 16);
     // each wave owns one leaf; groups of nl leaves become nl waves per WG
     dim3 grid((unsigned)((g.N + 15) / 16), 1u, (unsigned)g.groups);
-    return g.out_bf16 ? stream_dispatch<true>(p, fm, grid, g.nl, s) : stream_dispatch<false>(p, fm, grid, g.nl, s);
+    if (lp) return stream_dispatch<kOutLP>(p, fm, grid, g.nl, s);
+    return g.out_bf16 ? stream_dispatch<kOutBF16>(p, fm, grid, g.nl, s) : stream_dispatch<kOutF32>(p, fm, grid, g.nl, s);
   }
   const int64_t tiles = ((g.M + 127) / 128) * ((g.N + 127) / 128);
   dim3 grid((unsigned)tiles, 1u, (unsigned)g.groups);
-  return g.out_bf16 ? ring_dispatch<true, false>(p, grid, g.nl, s) : ring_dispatch<false, false>(p, grid, g.nl, s);
+  if (lp) return ring_dispatch<kOutLP, false>(p, grid, g.nl, s);
+  return g.out_bf16 ? ring_dispatch<kOutBF16, false>(p, grid, g.nl, s) : ring_dispatch<kOutF32, false>(p, grid, g.nl, s);
 }
 
 hipError_t launch_tree_combine(const float* P, int count, int64_t plane, void* C, bool out_bf16, bool left_fold,

@@ -28,6 +28,12 @@ struct GemmLaunch {
   int E;
   int64_t a_rows;          // rows of A (gathered indices outside [0, a_rows) read as zero rows)
   int64_t b_expert_stride; // elements between experts' B
+  // LM-head statistics mode (lp_stats != nullptr, groups == 1, not grouped):
+  // C is not written; per row and 16-column vocabulary block the (m, s) pair
+  // goes to lp_stats [M, ceil(N/16), 2] and the target's logit to lp_tlogit.
+  float* lp_stats = nullptr;
+  float* lp_tlogit = nullptr;
+  const int32_t* lp_target = nullptr;
 };
 hipError_t launch_gemm(const GemmLaunch& g, hipStream_t s);
 
@@ -46,6 +52,14 @@ hipError_t launch_rmsnorm(const void* x, const void* gamma, void* y, int64_t M, 
 hipError_t launch_logprob(const float* logits, int64_t ldl, const int32_t* target, float* out,
                           float* stats, float* tlogit, int64_t M, int64_t V, int C, int chunk_lo,
                           int chunk_hi, bool left_fold, bool partial, hipStream_t s);
+// LM-head logprob from 16-column block statistics: per row, the balanced
+// tree (or left fold) over ceil(V/16) blocks padded with (-inf, 0) to a power
+// of two, then lp = tlogit - LSE. stats [M, nb, 2], nb = ceil(V/16).
+hipError_t launch_block16_merge(const float* stats, const float* tlogit, const int32_t* target, float* out,
+                                int64_t M, int64_t V, bool left_fold, hipStream_t s);
+// The same block statistics computed from stored fp32 logits [M, ldl].
+hipError_t launch_block16_stats(const float* logits, int64_t ldl, const int32_t* target, float* stats,
+                                float* tlogit, int64_t M, int64_t V, hipStream_t s);
 hipError_t launch_logprob_combine(const float* stats, const float* tlogit, const int32_t* target,
                                   float* out, int64_t M, int64_t V, int C, bool left_fold,
                                   hipStream_t s);

@@ -27,7 +27,7 @@ OK, E_ARG, E_CONTRACT, E_TOPOLOGY, E_UNSUPPORTED, E_HIP, E_WORKSPACE = range(7)
 BF16, FP32 = 1, 2
 BALANCED, LEFT_FOLD = 1, 2
 OP_GEMM, OP_TREE_COMBINE, OP_RMSNORM, OP_LOGPROB, OP_DECODE_ATTN, OP_MOE_ROUTE, OP_MOE_GEMM, \
-    OP_MOE_COMBINE = range(1, 9)
+    OP_MOE_COMBINE, OP_LMHEAD_LOGPROB, OP_LOGPROB_BLOCK16 = range(1, 11)
 ABI_VERSION = 1
 
 _DT = {"bf16": BF16, "fp32": FP32, BF16: BF16, FP32: FP32}
@@ -89,6 +89,8 @@ _SIGS = {
     "inv_moe_gemm": [_CP, _P, _I64, _P, _P, _P, _P, _I64, _I32, _I64, _I64, _P],
     "inv_swiglu": [_CP, _P, _P, _I64, _I64, _P],
     "inv_moe_combine": [_CP, _P, _P, _P, _I64, _P, _I64, _I64, _P],
+    "inv_lmhead_logprob": [_CP, _P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P],
+    "inv_logprob_block16": [_CP, _P, _I64, _P, _P, _I64, _I64, _P, _SZ, _P],
 }
 for _name, _args in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -105,7 +107,7 @@ class RegionContract(ctypes.Structure):
 
 
 REGIONS = {"norms.rms": 1, "linear": 2, "lm_head": 3, "logprob": 4, "attention": 5, "moe.route": 6,
-           "moe.experts": 7, "moe.combine": 8}
+           "moe.experts": 7, "moe.combine": 8, "lm_head_logprob": 9}
 DIGEST_SEMANTIC, DIGEST_NUMERICAL_POLICY, DIGEST_DEPLOYMENT = 1, 2, 3
 _RCP = ctypes.POINTER(RegionContract)
 _D32 = ctypes.c_uint8 * 32
@@ -365,6 +367,50 @@ def logprob_combine(stats, tlogit, target, V, c, out=None):
 
 
 # ------------------------------------------------------------------ attention
+
+def block16_workspace(M, V, device):
+    """Workspace of the 16-column block schedule: stats [M, nb, 2] then tlogit [M]."""
+    nb = (V + 15) // 16
+    return torch.empty(M * nb * 2 + M, dtype=torch.float32, device=device)
+
+
+def block16_views(ws, M, V):
+    """(stats [M, nb, 2], tlogit [M]) views of a block16 workspace."""
+    nb = (V + 15) // 16
+    return ws[:M * nb * 2].view(M, nb, 2), ws[M * nb * 2:M * nb * 2 + M]
+
+
+def lmhead_logprob(h, W, target, c, out=None, ws=None):
+    """Fused LM head + selected-token logprob (inv_lmhead_logprob): lp [M] fp32."""
+    _need(h, torch.bfloat16, "h", 2)
+    _need(W, torch.bfloat16, "W", 2)
+    _need(target, torch.int32, "target", 1)
+    M, K = h.shape
+    V = W.shape[0]
+    if W.shape[1] != K or target.shape[0] != M:
+        raise ValueError("h, W and target disagree")
+    if out is None:
+        out = torch.empty(M, dtype=torch.float32, device=h.device)
+    if ws is None:
+        ws = block16_workspace(M, V, h.device)
+    _call("inv_lmhead_logprob", ctypes.byref(c), _ptr(h), _ptr(W), _ptr(target), _ptr(out), M, V, K, _ptr(ws),
+          ws.numel() * ws.element_size(), _stream())
+    return out
+
+
+def logprob_block16(logits, target, c, out=None, ws=None):
+    """The 16-column block schedule from stored fp32 logits (inv_logprob_block16)."""
+    _need(target, torch.int32, "target", 1)
+    ldl = _logits_ld(logits)
+    M, V = logits.shape
+    if out is None:
+        out = torch.empty(M, dtype=torch.float32, device=logits.device)
+    if ws is None:
+        ws = block16_workspace(M, V, logits.device)
+    _call("inv_logprob_block16", ctypes.byref(c), _ptr(logits), ldl, _ptr(target), _ptr(out), M, V, _ptr(ws),
+          ws.numel() * ws.element_size(), _stream())
+    return out
+
 
 def _attn_args(q, k, v, cu_seqlens, q_seq, q_pos):
     _need(q, torch.bfloat16, "q", 3)

@@ -86,6 +86,10 @@ def test_workspace_sizes():
     assert inv.workspace_bytes(inv.contract(ranks=4), inv.OP_GEMM, 64, 128, 4096) == 4 * 64 * 128 * 4
     assert inv.workspace_bytes(inv.contract(), inv.OP_DECODE_ATTN, 3, 32, 128) == 3 * 32 * 16 * 130 * 4
     assert inv.workspace_bytes(inv.contract(ranks=3), inv.OP_GEMM, 64, 128, 4096) == ctypes.c_size_t(-1).value
+    c32 = inv.contract(leaves=8, out="fp32")
+    assert inv.workspace_bytes(c32, inv.OP_LMHEAD_LOGPROB, 4096, 151936, 4096) == 4096 * 9496 * 8 + 4096 * 4
+    assert inv.workspace_bytes(c32, inv.OP_LOGPROB_BLOCK16, 3, 17, 0) == 3 * 2 * 8 + 3 * 4
+    assert inv.workspace_bytes(inv.contract(), inv.OP_LMHEAD_LOGPROB, 8, 512, 256) == ctypes.c_size_t(-1).value
 
 
 def test_entry_points_reject_before_any_launch():
@@ -130,6 +134,22 @@ def test_entry_points_reject_before_any_launch():
     assert lib.inv_moe_gemm(by(inv.contract(ranks=2)), fake, 4, fake, fake, fake, fake, 4, 2, 64, 4096,
                             null) == inv.E_TOPOLOGY
     assert lib.inv_moe_combine(by(cm), null, null, null, 0, null, 0, 2048, null) == inv.OK
+    # fused LM head + logprob: fp32 logits, one rank, V <= 262144, enough aligned workspace
+    cl = inv.contract(leaves=8, out="fp32")
+    big = 1 << 30
+    assert lib.inv_lmhead_logprob(by(inv.contract(leaves=8)), fake, fake, fake, fake, 4, 512, 256, fake, big,
+                                  null) == inv.E_CONTRACT
+    assert lib.inv_lmhead_logprob(by(inv.contract(leaves=8, ranks=2, out="fp32")), fake, fake, fake, fake, 4, 512,
+                                  256, fake, big, null) == inv.E_UNSUPPORTED
+    assert lib.inv_lmhead_logprob(by(cl), fake, fake, fake, fake, 4, 262160, 256, fake, big, null) \
+        == inv.E_UNSUPPORTED
+    assert lib.inv_lmhead_logprob(by(cl), fake, fake, fake, fake, 4, 512, 256, fake, 4 * 32 * 8, null) \
+        == inv.E_WORKSPACE
+    assert lib.inv_lmhead_logprob(by(cl), fake, fake, fake, fake, 4, 512, 256, ctypes.c_void_p((1 << 20) + 4),
+                                  big, null) == inv.E_ARG
+    assert lib.inv_lmhead_logprob(by(cl), fake, fake, fake, fake, 0, 512, 256, null, 0, null) == inv.OK
+    assert lib.inv_logprob_block16(by(cl), fake, 10, fake, fake, 4, 16, fake, big, null) == inv.E_ARG  # ldl < V
+    assert lib.inv_logprob_block16(by(cl), fake, 16, fake, fake, 4, 16, null, 0, null) == inv.E_WORKSPACE
 
 
 def test_status_strings():

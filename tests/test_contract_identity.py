@@ -39,6 +39,7 @@ def path_composition(inv, **over):
         "moe.route": inv.contract(leaves=8),
         "moe.experts": inv.contract(leaves=8),
         "moe.combine": inv.contract(leaves=8),
+        "lm_head_logprob": inv.contract(leaves=8, out="fp32"),
     }
     e.update(over)
     return e
@@ -71,6 +72,10 @@ def test_sha256_against_hashlib_at_padding_boundaries(inv):
 
 # ------------------------------------------------------------------ JSON and digests
 
+def by_region(d):
+    return {c["region"]: c for c in d["composition"]}
+
+
 def _sections(text):
     d = json.loads(text)["ExecutionContract"]
     dump = lambda o: json.dumps(o, separators=(",", ":"), ensure_ascii=True).encode()
@@ -89,7 +94,8 @@ def test_json_layout_and_identities(inv):
     assert json.dumps(json.loads(text), separators=(",", ":")) == text
     regions = [c["region"] for c in d["composition"]]
     assert regions == ["norms.rms", "linear", "lm_head", "logprob", "attention", "moe.route",
-                       "moe.experts", "moe.combine"]
+                       "moe.experts", "moe.combine", "lm_head_logprob"]
+    assert by_region(d)["lm_head_logprob"]["constants"]["vocab_block"] == 16
     by = {c["region"]: c for c in d["composition"]}
     assert by["linear"]["constants"]["leaves"] == 8 and by["lm_head"]["constants"]["out_dtype"] == "fp32"
     assert by["logprob"]["constants"]["chunks"] == 64
@@ -125,6 +131,7 @@ def _digests(inv, e):
     ({"logprob": dict(leaves=64, tree="left_fold")}, "policy"),
     ({"attention": dict(split_kv=8)}, "policy"),
     ({"attention": dict(kv_chunk=128)}, "policy"),
+    ({"lm_head_logprob": dict(leaves=4, out="fp32")}, "policy"),
     ({"linear": dict(leaves=8, ranks=4)}, "deployment"),   # a proven rank count: same bits
     ({"logprob": dict(leaves=64, ranks=2)}, "deployment"),
     ({"norms.rms": dict(eps=1e-5)}, "semantic"),           # a different model
@@ -166,6 +173,9 @@ def test_invalid_compositions_are_rejected(inv):
     assert ex.value.status == inv.E_TOPOLOGY
     with pytest.raises(inv.InvError) as ex:
         inv.contract_json({"linear": inv.contract(tree="left_fold")})  # the GEMM tree is balanced only
+    assert ex.value.status == inv.E_CONTRACT
+    with pytest.raises(inv.InvError) as ex:
+        inv.contract_json({"lm_head_logprob": inv.contract(leaves=8)})  # logits must stay fp32
     assert ex.value.status == inv.E_CONTRACT
     with pytest.raises(inv.InvError) as ex:
         inv.contract_json({99: inv.contract()})

@@ -201,6 +201,37 @@ def test_logprob_chunked_tree_equals_plain_lse():
             assert np.allclose(olp.merge_tree(ms, ss, sch), olp.lse(x), rtol=0, atol=1e-12)
 
 
+def test_block_schedule_partitions_and_equals_plain_lse():
+    """The 16-column block schedule of the fused LM head: blocks tile [0, V),
+    and block statistics merged over the padded tree give the plain LSE."""
+    rng = np.random.default_rng(14)
+    for V in (1, 15, 16, 17, 100, 1000, 2374 * 3 + 5):
+        b = olp.block_bounds(V)
+        assert b[0][0] == 0 and b[-1][1] == V
+        assert all(hi - lo == 16 for lo, hi in b[:-1]) and 1 <= b[-1][1] - b[-1][0] <= 16
+        assert all(b[i][1] == b[i + 1][0] for i in range(len(b) - 1))
+        x = rng.normal(size=(3, V)) * 3
+        assert np.allclose(olp.merge_tree_padded(*olp.block_stats(x)), olp.lse(x), rtol=0, atol=1e-12)
+        t = np.array([0, V - 1, V])
+        lp = olp.logprob_blocks(x, t)
+        assert np.allclose(lp[:2], olp.logprob(x, t)[:2], rtol=0, atol=1e-12) and np.isnan(lp[2])
+
+
+def test_padded_tree_shape():
+    """Padding to a power of two fixes the tree for any block count: five
+    blocks pair as ((0,1),(2,3)),(4,pad) -- not the ceil-halving tree
+    ((0,1),2),(3,4) -- and the padding merges away exactly."""
+    cat = lambda a, b: f"({a}{b})"
+    assert otree.combine(olp.pad_pow2(list("abcde"), "_"), cat) == "(((ab)(cd))((e_)(__)))"
+    assert otree.combine(list("abcde"), cat) == "(((ab)c)(de))"
+    assert olp.pad_pow2(list("abcd"), "_") == list("abcd")
+    # the identity is exact in the merge, so a padded tree equals its unpadded twin
+    rng = np.random.default_rng(15)
+    ms, ss = rng.normal(size=(2, 8)), rng.uniform(1, 16, size=(2, 8))
+    full = olp.merge_tree(ms, ss)
+    assert np.array_equal(olp.merge_tree_padded(ms, ss), full)
+
+
 def test_lse_merge_identity_and_halves():
     m, s = np.array([0.7]), np.array([3.25])
     mi, si = olp.merge((np.array([-np.inf]), np.array([0.0])), (m, s))
