@@ -17,6 +17,7 @@ import pytest
 import torch
 
 from oracle import attention as oatt
+from oracle import gdn as ogdn
 from oracle import gemm as ogemm
 from oracle import logprob as olp
 from oracle import moe as omoe
@@ -351,6 +352,77 @@ def test_moe_identical_experts_equal_one_expert():
     assert np.all(w == 0.125) and ids.tolist() == [list(range(8))] * T
     single = numerics.to_bf16(omoe.expert_ffn(x, W1, W2).astype(np.float64))
     assert np.array_equal(out, single)
+
+
+# ---------------------------------------------------------------- Gated DeltaNet (CPR)
+
+def _gdn_case(L, dk=16, dv=12, seed=0, gscale=0.2):
+    rng = np.random.default_rng(seed)
+    q = rng.normal(size=(L, dk))
+    k = rng.normal(size=(L, dk))
+    v = rng.normal(size=(L, dv))
+    g = -gscale * rng.uniform(size=L)
+    beta = rng.uniform(size=L)
+    qh, kh, alpha = ogdn.prep(q, k, g)
+    return qh, kh, v, alpha, beta
+
+
+def test_gdn_chunk_closed_form_equals_the_recurrence():
+    """The boundary-state closed form is the recurrence unrolled over a chunk."""
+    for C, seed in ((1, 1), (2, 2), (5, 3), (16, 4), (64, 5)):
+        qh, kh, v, alpha, beta = _gdn_case(C, seed=seed)
+        S0 = np.random.default_rng(seed + 10).normal(size=(16, 12))
+        _, S = ogdn.recurrent(qh, kh, v, alpha, beta, S0)
+        assert np.allclose(ogdn.chunk_update(S0, kh, v, alpha, beta), S, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("L,C", [(1, 4), (7, 4), (64, 16), (100, 16), (130, 64)])
+def test_gdn_cpr_equals_the_recurrence(L, C):
+    qh, kh, v, alpha, beta = _gdn_case(L, seed=L)
+    o_ref, S_ref = ogdn.recurrent(qh, kh, v, alpha, beta)
+    o, b, run = ogdn.cpr(qh, kh, v, alpha, beta, C)
+    assert b.shape[0] == L // C + 1 and not b[0].any()
+    assert np.allclose(o, o_ref, rtol=0, atol=1e-12)
+    assert np.allclose(run, S_ref, rtol=0, atol=1e-12)
+    for j in range(1, L // C + 1):   # every boundary is the recurrence's state there
+        _, Sj = ogdn.recurrent(qh[:j * C], kh[:j * C], v[:j * C], alpha[:j * C], beta[:j * C])
+        assert np.allclose(b[j], Sj, rtol=0, atol=1e-12)
+
+
+def test_gdn_delta_rule_closed_forms():
+    dk, dv = 8, 5
+    rng = np.random.default_rng(9)
+    vals = rng.normal(size=(dk, dv))
+    eye = np.eye(dk)
+    # beta = 1, no decay, orthonormal keys: each write stores its value exactly
+    kh, alpha, beta = eye, np.ones(dk), np.ones(dk)
+    _, S = ogdn.recurrent(np.zeros((dk, dk)), kh, vals, alpha, beta)
+    assert np.allclose(S, vals, rtol=0, atol=1e-15)
+    # a second write to the same unit key replaces the first (the delta rule); with a key of
+    # squared norm n the old value survives as (1 - n) n v1 (what l2norm's eps leaves)
+    k1 = rng.normal(size=dk)
+    k1 = k1 / np.linalg.norm(k1)
+    v1, v2 = rng.normal(size=dv), rng.normal(size=dv)
+    _, S = ogdn.recurrent(np.zeros((2, dk)), np.stack([k1, k1]), np.stack([v1, v2]), np.ones(2), np.ones(2))
+    assert np.allclose(S.T @ k1, v2, rtol=0, atol=1e-12)
+    k2 = ogdn.l2norm(rng.normal(size=(1, dk)))[0]
+    n = k2 @ k2
+    _, S = ogdn.recurrent(np.zeros((2, dk)), np.stack([k2, k2]), np.stack([v1, v2]), np.ones(2), np.ones(2))
+    assert np.allclose(S.T @ k2, n * v2 + (1 - n) * n * v1, rtol=0, atol=1e-14) and n < 1
+    # beta = 0: nothing is written, the zero state stays zero and outputs are exact zeros
+    qh, kh, v, alpha, _ = _gdn_case(20)
+    o, S = ogdn.recurrent(qh, kh, v, alpha, np.zeros(20))
+    assert not o.any() and not S.any()
+    # pure decay of one write: S_t = (prod alpha) k v^T
+    a = np.array([1.0, 0.5, 0.25, 0.8])
+    _, S = ogdn.recurrent(np.zeros((4, dk)), np.stack([eye[2]] * 4), np.stack([vals[0]] + [np.zeros(dv)] * 3), a,
+                          np.array([1.0, 0.0, 0.0, 0.0]))
+    assert np.allclose(S, 0.5 * 0.25 * 0.8 * np.outer(eye[2], vals[0]), rtol=0, atol=1e-15)
+    # the l2 norm and the query scale
+    q = np.array([[3.0, 4.0] + [0.0] * 6])
+    qh, kh, _ = ogdn.prep(q, q, np.zeros(1))
+    assert np.allclose(kh[0, :2], [3 / math.sqrt(25 + 1e-6), 4 / math.sqrt(25 + 1e-6)], rtol=1e-15)
+    assert np.allclose(qh, kh / math.sqrt(8), rtol=1e-15)
 
 
 # ---------------------------------------------------------------- generator
