@@ -38,6 +38,8 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector, published (packed fp32; without packed ops, which
+                            # this library never emits, the ceiling is 78.6)
 
 
 def parse():
@@ -46,8 +48,8 @@ def parse():
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--stages", default="dense,norm,attn,moe,lmhead",
-                   help="comma list of dense,norm,attn,moe,lmhead (the whole path by default); "
+    p.add_argument("--stages", default="dense,norm,attn,moe,lmhead,gdn",
+                   help="comma list of dense,norm,attn,moe,lmhead,gdn (the whole path by default); "
                         "'copy' adds a plain 1 GiB device copy used only to calibrate traffic counters")
     return p.parse_args()
 
@@ -258,6 +260,41 @@ def main():
         del lm_ws
         log("fused LM head timed")
 
+    # ------------------------------------------------------------ CPR Gated DeltaNet (outside the step)
+    # Prefill of 5 sequences x 2048 tokens, 16 heads of width 128, chunk 64; one
+    # decode token for 256 sequences, once at a plain position and once at a
+    # position that closes a chunk (the boundary update and resynchronisation).
+    if "gdn" in stages:
+        cg = inv.contract(kv_chunk=64, out="bf16")
+        gd = synth.gdn([2048] * 5, H=16, seed=0, device=dev)
+        Tg = gd["q"].shape[0]
+        g_ws = torch.empty(inv.workspace_bytes(cg, inv.OP_GDN_PREFILL, Tg, 16, 5), dtype=torch.uint8, device=dev)
+        g_out = torch.empty((Tg, 16, 128), dtype=torch.bfloat16, device=dev)
+        dq = synth.gdn([1] * 256, H=16, seed=1, device=dev)
+        g_cache = inv.gdn_cache(cg, 256, 16, dev)
+        d_out = torch.empty((256, 16, 128), dtype=torch.bfloat16, device=dev)
+        pos_plain = torch.full((256,), 2048, dtype=torch.int32, device=dev)
+        pos_close = torch.full((256,), 2111, dtype=torch.int32, device=dev)
+        Tx = Timer(torch)
+        for i in range(max(3, min(args.steps, 10)) + 2):
+            if i == 2:
+                torch.cuda.synchronize()
+                Tx.reset()
+            Tx.start("gdn_prefill")
+            inv.gdn_prefill(gd["q"], gd["k"], gd["v"], gd["g"], gd["beta"], gd["cu_seqlens"], cg, out=g_out, ws=g_ws)
+            Tx.stop("gdn_prefill")
+            Tx.start("gdn_decode")
+            inv.gdn_decode(dq["q"], dq["k"], dq["v"], dq["g"], dq["beta"], pos_plain, g_cache, cg, out=d_out)
+            Tx.stop("gdn_decode")
+            Tx.start("gdn_decode_boundary")
+            inv.gdn_decode(dq["q"], dq["k"], dq["v"], dq["g"], dq["beta"], pos_close, g_cache, cg, out=d_out)
+            Tx.stop("gdn_decode_boundary")
+        torch.cuda.synchronize()
+        for k in ("gdn_prefill", "gdn_decode", "gdn_decode_boundary"):
+            ms[k] = Tx.mean_ms(k)
+        del g_ws, gd, g_cache
+        log("CPR Gated DeltaNet timed")
+
     # ------------------------------------------------------------ fast paths
     Tf = Timer(torch)
     fast = {}
@@ -331,6 +368,11 @@ def main():
         result["lmhead_fused_speedup"] = round(lm_ms / fused_ms, 3)
     if "attn" in stages:
         result["attn_gbs"] = round(4096.0 * sumL / (ms["attn"] * 1e-3) / 1e9, 1)
+    if "gdn" in stages:
+        result["gdn_prefill_tokens_per_s"] = round(10240 / (ms["gdn_prefill"] * 1e-3), 1)
+        result["gdn_prefill_ms"] = round(ms["gdn_prefill"], 4)
+        result["gdn_decode_ms"] = round(ms["gdn_decode"], 4)
+        result["gdn_decode_boundary_ms"] = round(ms["gdn_decode_boundary"], 4)
     if "moe" in stages:
         result["moe_tflops"] = round(2.0 * 8192 * 8 * (1536 * 2048 + 2048 * 768) / (ms["moe"] * 1e-3) / 1e12, 2)
     if "norm" in stages:
@@ -356,6 +398,16 @@ def main():
             PEAK_BF16_TFLOPS, "TFLOP/s")
     if "attn" in stages:
         add("inv_decode_attn B=256", "hbm", 4096.0 * sumL, ms["attn"], PEAK_HBM_GBS, "GB/s")
+    if "gdn" in stages:
+        # CPR flops per (token, head): the recurrence step 7*128^2 (S^T k, the
+        # rank-1 update with decay, S^T q) plus the chunk update amortised over
+        # C = 64 tokens, (4*128^2*C + 2*C*(C-1)*128) / C; fp32 vector ALU bound.
+        fl_tok = 7 * 128 * 128 + (4 * 128 * 128 * 64 + 2 * 64 * 63 * 128) / 64
+        add("gdn prefill 5x2048 tokens, 16 heads", "alu", fl_tok * 10240 * 16, ms["gdn_prefill"],
+            PEAK_FP32_TFLOPS, "TFLOP/s")
+        # decode: the running state read and written, 2 * 128^2 * 4 bytes per (sequence, head)
+        add("gdn decode 256 sequences, 16 heads", "hbm", 2 * 128 * 128 * 4 * 256 * 16, ms["gdn_decode"],
+            PEAK_HBM_GBS, "GB/s")
     if "moe" in stages:
         add("moe layer 8192 tokens", "mfma", 2.0 * 8192 * 8 * (1536 * 2048 + 2048 * 768), ms["moe"],
             PEAK_BF16_TFLOPS, "TFLOP/s")

@@ -112,7 +112,9 @@ typedef enum inv_op {
   INV_OP_MOE_GEMM = 7,
   INV_OP_MOE_COMBINE = 8,
   INV_OP_LMHEAD_LOGPROB = 9,
-  INV_OP_LOGPROB_BLOCK16 = 10
+  INV_OP_LOGPROB_BLOCK16 = 10,
+  INV_OP_GDN_PREFILL = 11,
+  INV_OP_GDN_DECODE = 12
 } inv_op;
 
 /* Host-only contract validation for `op`; the same check every entry point
@@ -125,6 +127,8 @@ inv_status inv_contract_check(const inv_contract* c, int op, int64_t K);
  *   INV_OP_DECODE_ATTN: d0 = Tq, d1 = Hq, d2 = D -> Tq*Hq*split_kv*(D+2)*4
  *   INV_OP_LMHEAD_LOGPROB, INV_OP_LOGPROB_BLOCK16: d0 = M, d1 = V, d2 = K
  *                       -> M*ceil(V/16)*8 + M*4
+ *   INV_OP_GDN_PREFILL: d0 = T tokens, d1 = H heads, d2 = S sequences
+ *                       -> (2*T*H*128 + T*H + (T/C + S)*H*128*128)*4 + 16
  * Returns (size_t)-1 if the contract is invalid. Host only. */
 size_t inv_workspace_bytes(const inv_contract* c, int op, int64_t d0, int64_t d1, int64_t d2);
 
@@ -410,6 +414,60 @@ inv_status inv_lmhead_logprob(const inv_contract* c, const void* h, const void* 
 inv_status inv_logprob_block16(const inv_contract* c, const float* logits, int64_t ldl, const int32_t* target,
                                float* out, int64_t M, int64_t V, void* ws, size_t ws_bytes,
                                hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Gated DeltaNet under the chunkwise-parallel recurrent (CPR) schedule.
+ *
+ * [IsoExec] "Chunkwise-parallel recurrent (CPR) GDN" ([NovaSky] "Solving the
+ * linear-attention headache"): the recurrence is the function; a first pass
+ * computes the state at every chunk boundary, a parallel pass runs the
+ * recurrence inside each chunk from its boundary state, and decode runs the
+ * recurrence but resynchronises to the boundary state every C tokens, so
+ * prefill, training forward and decode share one rounding schedule. The
+ * layer (the gated delta rule, restated; the pages give no formulas), per
+ * head with key and value width D = 128:
+ *   k^ = k / sqrt(sum k^2 + 1e-6), q^ = q / sqrt(sum q^2 + 1e-6) / sqrt(128)
+ *   alpha = exp(g) (g <= 0 the log-decay), beta in [0, 1]
+ *   S_t = alpha_t (S_{t-1} - beta_t k^_t (k^_t^T S_{t-1})) + beta_t k^_t v_t^T,
+ *   S_0 = 0, o_t = S_t^T q^_t   (S is D x D fp32)
+ * Boundaries at multiples of C = c->kv_chunk (32 or 64) from each sequence's
+ * first token; a boundary state is the previous one advanced by the
+ * chunkwise closed form of the recurrence (gamma = running product of alpha
+ * inside the chunk, w from the unit-lower-triangular solve, S_C = gamma_C S_0
+ * + sum_s (gamma_C / gamma_s) k^_s w_s^T); every output comes from the
+ * token-by-token recurrence started at its chunk's boundary state.
+ * The same device functions run in both entry points, so a sequence
+ * prefilled to any length and continued by decode gives, token for token,
+ * the bits of one prefill of the whole sequence. c->ranks must be 1;
+ * c->out_dtype is the output's dtype (bf16 or fp32).
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of one sequence's decode cache: the running state and the last
+ * boundary state [H][128][128] fp32 each, then the open chunk's k^ and v
+ * [C][H][128] fp32 and alpha, beta [C][H] fp32. A fresh sequence's cache is
+ * all zeros. (size_t)-1 if the contract is invalid. */
+size_t inv_gdn_cache_bytes(const inv_contract* c, int32_t H);
+
+/* Prefill / training forward of S packed sequences (cu_seqlens [S+1] int32,
+ * T = cu_seqlens[S] tokens): q, k, v [T, H, D] bf16, g, beta [T, H] fp32,
+ * out [T, H, D] out_dtype. D must be 128. If cache is not NULL it receives,
+ * per sequence, the decode cache after the sequence's last token (cache
+ * [S] x inv_gdn_cache_bytes). Workspace: ws_bytes >=
+ * inv_workspace_bytes(INV_OP_GDN_PREFILL, T, H, S), 16-byte aligned; it holds
+ * k^, q^, alpha and every boundary state. */
+inv_status inv_gdn_prefill(const inv_contract* c, const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, const int32_t* cu_seqlens, int32_t S, int64_t T, int32_t H,
+                           int32_t D, void* out, void* cache, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* One decode token for each of B sequences: q, k, v [B, H, D] bf16, g, beta
+ * [B, H] fp32, pos [B] int32 = the number of tokens the sequence already has
+ * (this token's position), out [B, H, D] out_dtype, cache [B] decode caches
+ * (updated in place: the token joins the open chunk; when it closes the
+ * chunk, the boundary state advances and the running state resynchronises
+ * to it). The caller advances pos. */
+inv_status inv_gdn_decode(const inv_contract* c, const void* q, const void* k, const void* v, const float* g,
+                          const float* beta, const int32_t* pos, int32_t B, int32_t H, int32_t D, void* out,
+                          void* cache, hipStream_t stream);
 
 /* Grouped GEMM: for expert e, grouped rows r in [offsets[e], offsets[e+1]):
  * Y[r, :] = inv_gemm row of A = X[rows[r], :] (or X[r, :] if rows is NULL)

@@ -57,6 +57,20 @@ inv_status check_attn_contract(const inv_contract* c) {
   return INV_OK;
 }
 
+inv_status check_gdn_contract(const inv_contract* c) {
+  inv_status s = check_contract(c);
+  if (s != INV_OK) return s;
+  if (c->kv_chunk != 32 && c->kv_chunk != 64) return INV_E_CONTRACT;
+  if (c->ranks != 1) return INV_E_UNSUPPORTED;
+  return INV_OK;
+}
+
+size_t gdn_prefill_ws_bytes(int64_t T, int64_t H, int64_t S, int64_t C) {
+  return ((size_t)2 * T * H * 128 + (size_t)T * H + (size_t)(T / C + S) * H * 128 * 128) * sizeof(float);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
 inv_status check_logprob_contract(const inv_contract* c, int64_t V) {
   inv_status s = check_contract(c);
   if (s != INV_OK) return s;
@@ -132,6 +146,9 @@ inv_status inv_contract_check(const inv_contract* c, int op, int64_t K) {
     }
     case INV_OP_LOGPROB_BLOCK16:
       return check_contract(c);
+    case INV_OP_GDN_PREFILL:
+    case INV_OP_GDN_DECODE:
+      return check_gdn_contract(c);
     default:
       return INV_E_ARG;
   }
@@ -149,6 +166,9 @@ size_t inv_workspace_bytes(const inv_contract* c, int op, int64_t d0, int64_t d1
     case INV_OP_DECODE_ATTN:
       if (check_attn_contract(c) != INV_OK) return (size_t)-1;
       return (size_t)d0 * (size_t)d1 * (size_t)c->split_kv * (size_t)(d2 + 2) * sizeof(float);
+    case INV_OP_GDN_PREFILL:
+      if (check_gdn_contract(c) != INV_OK || d1 < 1 || d2 < 1) return (size_t)-1;
+      return gdn_prefill_ws_bytes(d0, d1, d2, c->kv_chunk) + 16;
     case INV_OP_LMHEAD_LOGPROB:
     case INV_OP_LOGPROB_BLOCK16:
       if (inv_contract_check(c, op, d2) != INV_OK || d1 <= 0 || (d1 + 15) / 16 > 16384) return (size_t)-1;
@@ -306,6 +326,75 @@ inv_status inv_logprob(const inv_contract* c, const float* logits, int64_t ldl, 
   if (!logits || !target || !out) return INV_E_ARG;
   return hip_status(inv::launch_logprob(logits, ldl, target, out, nullptr, nullptr, M, V, (int)c->leaves, 0,
                                         (int)c->leaves, c->tree == INV_TREE_LEFT_FOLD, false, stream));
+}
+
+// ------------------------------------------------------- Gated DeltaNet (CPR)
+
+size_t inv_gdn_cache_bytes(const inv_contract* c, int32_t H) {
+  if (check_gdn_contract(c) != INV_OK || H <= 0) return (size_t)-1;
+  return (size_t)inv::gdn_cache_floats(H, (int)c->kv_chunk) * sizeof(float);
+}
+
+inv_status inv_gdn_prefill(const inv_contract* c, const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, const int32_t* cu_seqlens, int32_t S, int64_t T, int32_t H, int32_t D,
+                           void* out, void* cache, void* ws, size_t ws_bytes, hipStream_t stream) {
+  inv_status s = check_gdn_contract(c);
+  if (s != INV_OK) return s;
+  if (D != 128) return INV_E_UNSUPPORTED;
+  if (S < 1 || T < 0 || H < 1) return INV_E_ARG;
+  if (T / (int64_t)c->kv_chunk + S > ((int64_t)1 << 31) - 1 || H > 65535) return INV_E_UNSUPPORTED;
+  if (!cu_seqlens) return INV_E_ARG;
+  if (T > 0 && (!q || !k || !v || !g || !beta || !out)) return INV_E_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(cache) || !aligned16(ws))
+    return INV_E_ARG;
+  const size_t need = gdn_prefill_ws_bytes(T, H, S, c->kv_chunk);
+  if (!ws || ws_bytes < need) return INV_E_WORKSPACE;
+  inv::GdnArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.g = g;
+  a.beta = beta;
+  a.cu = cu_seqlens;
+  a.S = S;
+  a.T = T;
+  a.H = H;
+  a.out = out;
+  a.cache = cache;
+  float* w = static_cast<float*>(ws);
+  a.qh = w;
+  a.kh = w + T * H * 128;
+  a.alpha = w + 2 * T * H * 128;
+  // boundary states start on a 16-byte boundary
+  a.bstates = w + ((2 * T * H * 128 + T * H + 3) / 4) * 4;
+  if (reinterpret_cast<char*>(a.bstates + (T / c->kv_chunk + S) * H * 128 * 128) >
+      static_cast<char*>(ws) + ws_bytes)
+    return INV_E_WORKSPACE;
+  return hip_status(inv::launch_gdn_prefill(a, (int)c->kv_chunk, out_is_bf16(c), stream));
+}
+
+inv_status inv_gdn_decode(const inv_contract* c, const void* q, const void* k, const void* v, const float* g,
+                          const float* beta, const int32_t* pos, int32_t B, int32_t H, int32_t D, void* out,
+                          void* cache, hipStream_t stream) {
+  inv_status s = check_gdn_contract(c);
+  if (s != INV_OK) return s;
+  if (D != 128) return INV_E_UNSUPPORTED;
+  if (B < 0 || H < 1 || H > 65535) return INV_E_ARG;
+  if (B == 0) return INV_OK;
+  if (!q || !k || !v || !g || !beta || !pos || !out || !cache) return INV_E_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(cache)) return INV_E_ARG;
+  inv::GdnDecodeArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.g = g;
+  a.beta = beta;
+  a.pos = pos;
+  a.B = B;
+  a.H = H;
+  a.out = out;
+  a.cache = cache;
+  return hip_status(inv::launch_gdn_decode(a, (int)c->kv_chunk, out_is_bf16(c), stream));
 }
 
 // ------------------------------------------------------- LM head + logprob

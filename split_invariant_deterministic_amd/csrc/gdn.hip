@@ -1,0 +1,636 @@
+// Gated DeltaNet under the chunkwise-parallel recurrent (CPR) schedule, gfx950.
+//
+// IsoExec blog, "Chunkwise-parallel recurrent (CPR) GDN" (and the NovaSky
+// write-up, "Solving the linear-attention headache"): the recurrence is the
+// function; a first pass computes the state at every chunk boundary, a
+// parallel pass runs the recurrence inside every chunk from its boundary
+// state, and decode runs the recurrence but resynchronises to the boundary
+// state every C tokens. Prefill and decode therefore share one rounding
+// schedule: the same two device functions below (rec_step for a token,
+// chunk_update for a boundary), on the same thread layout, in both.
+//
+// Layer (gated delta rule, one head, width 128, restated):
+//   k^ = k / sqrt(sum k^2 + eps), q^ = q / sqrt(sum q^2 + eps) * 128^(-1/2)
+//   alpha = exp(g); S_t = alpha (S - beta k^ (k^T S)) + beta k^ v^T; o_t = S_t^T q^
+// Boundary states use the chunkwise closed form of the same recurrence:
+//   gamma_t = alpha_0 ... alpha_t (running product inside the chunk)
+//   w_t = beta_t (v_t - gamma_t S0^T k^_t - sum_{s<t} (gamma_t/gamma_s)(k^_s.k^_t) w_s)
+//   S_C = gamma_{C-1} S0 + sum_s (gamma_{C-1}/gamma_s) k^_s w_s^T
+//
+// Thread layout (256 threads): for the recurrence, thread (ti, tj),
+// ti = lane % 16, tj = 4 * wave + lane / 16, holds S[8ti .. 8ti+8)[8tj .. 8tj+8)
+// in registers; a chunk update splits the 128 value columns into 4 blocks of
+// 32, one workgroup each, thread (ti, tc) holding rows 8ti .. 8ti+8 of two
+// columns. Either way a reduction over the state rows (S^T x) is, per column,
+// a sequential fma chain over 8 rows, then a balanced tree over the 16 row
+// groups: the 16 lanes of a DPP row share the column, so that tree is an
+// in-register butterfly. Columns never mix, so the bits of a column do not
+// depend on which block or thread holds it.
+#include "common.h"
+#include "launch.h"
+
+namespace inv {
+namespace {
+
+constexpr int kD = 128;              // key = value width
+constexpr float kGdnEps = 1e-6f;
+constexpr float kInvSqrtD = 0.08838834764831845f;  // fp32(128^-1/2)
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF,
+                                                               true));
+}
+
+// Sum over the 16 lanes of a DPP row, pairing xor 1, 2, 4, 8 (a balanced tree
+// over the lane index). 0xB1 / 0x4E: quad_perm [1,0,3,2] / [2,3,0,1]; after
+// two steps a quad is uniform, so row_half_mirror (0x141) reads the xor-4
+// partner's value, and then row_mirror (0x140) the xor-8 partner's.
+__device__ __forceinline__ float row16_sum(float v) {
+  v = v + dpp<0xB1>(v);
+  v = v + dpp<0x4E>(v);
+  v = v + dpp<0x141>(v);
+  v = v + dpp<0x140>(v);
+  return v;
+}
+
+struct Tl {
+  int tid, lane, ti, tj;
+};
+__device__ __forceinline__ Tl thread_layout() {
+  Tl t;
+  t.tid = threadIdx.x;
+  t.lane = t.tid & 63;
+  t.ti = t.lane & 15;
+  t.tj = 4 * (t.tid >> 6) + (t.lane >> 4);
+  return t;
+}
+
+// norms.l2 + gating for one (token, head), one wave: lane l holds elements 2l
+// and 2l+1 of q and k (bf16 pairs). Sum of squares: a*a then fma(b, b, .) per
+// lane, then the xor butterfly 32..1.
+__device__ __forceinline__ float2 l2norm_pair(uint32_t bits, float scale) {
+  const float a = bf16_lo(bits), b = bf16_hi(bits);
+  float ss = a * a;
+  ss = __builtin_fmaf(b, b, ss);
+  ss = wave_sum_butterfly(ss);
+  const float r = 1.0f / __builtin_sqrtf(ss + kGdnEps);
+  return make_float2((a * r) * scale, (b * r) * scale);
+}
+
+__device__ __forceinline__ float gate_alpha(float g) { return exp2_hw(g * kLog2e); }
+
+// One token of the recurrence on the thread's 8x8 block. k8 / q8: the
+// thread's 8 rows of k^ and q^; v8: its 8 columns of v.
+__device__ __forceinline__ void rec_step(float (&S)[8][8], const float (&k8)[8], const float (&q8)[8],
+                                         const float (&v8)[8], float a, float b, float (&o8)[8]) {
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    float u = 0.0f;
+#pragma unroll
+    for (int ii = 0; ii < 8; ++ii) u = __builtin_fmaf(S[ii][jj], k8[ii], u);
+    u = row16_sum(u);
+    const float d = b * (v8[jj] - a * u);
+#pragma unroll
+    for (int ii = 0; ii < 8; ++ii) S[ii][jj] = __builtin_fmaf(k8[ii], d, a * S[ii][jj]);
+  }
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    float o = 0.0f;
+#pragma unroll
+    for (int ii = 0; ii < 8; ++ii) o = __builtin_fmaf(S[ii][jj], q8[ii], o);
+    o8[jj] = row16_sum(o);
+  }
+}
+
+// Chunk updates run on column blocks. Every value column of the state evolves
+// on its own (the recurrence mixes rows, never columns), so a workgroup of
+// 256 threads owns kCB = 32 columns: thread (ti, tc), ti = lane % 16,
+// tc = 4 * wave + lane / 16, holds rows 8ti .. 8ti+8 of columns 32 cb + 2 tc
+// and + 1. Each column's arithmetic is the same whichever block holds it.
+constexpr int kCB = 32;
+constexpr int kKStride = kD + 1;  // odd row stride: lanes reading different rows hit different banks
+
+struct Tc {
+  int tid, lane, ti, tc;
+};
+__device__ __forceinline__ Tc col_layout() {
+  Tc t;
+  t.tid = threadIdx.x;
+  t.lane = t.tid & 63;
+  t.ti = t.lane & 15;
+  t.tc = 4 * (t.tid >> 6) + (t.lane >> 4);
+  return t;
+}
+
+// LDS of one chunk update of one column block: inputs K (k^, all 128 rows),
+// V (the block's 32 columns of v, fp32), alpha, beta; scratch P (then W, in
+// place), A, gamma, c.
+template <int C>
+struct alignas(16) ChunkLds {
+  float K[C][kKStride];
+  float V[C][kCB];
+  float PW[C][kCB];
+  float A[C][C];
+  float alpha[C], beta[C], gamma[C], cf[C];
+};
+
+// S (registers, the block of boundary state b_j on entry) becomes b_{j+1}.
+// The chunk's inputs are in L.K / L.V / L.alpha / L.beta, visible to all.
+template <int C>
+__device__ void chunk_update(float (&S)[8][2], ChunkLds<C>& L, const Tc& T) {
+  // running products of the gates (one thread, ascending; the gates read
+  // into registers first so the chain does not wait on LDS)
+  if (T.tid == 0) {
+    float gm = 1.0f;  // 1 * alpha_0 = alpha_0 exactly
+#pragma unroll
+    for (int t0 = 0; t0 < C; t0 += 16) {
+      float al[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) al[q] = L.alpha[t0 + q];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        gm = gm * al[q];
+        L.gamma[t0 + q] = gm;
+      }
+    }
+  }
+  // P[t][j] = sum_i k^_t[i] S0[i][j]: the thread's 8 rows as one fma chain,
+  // then the balanced tree over the 16 row groups (a DPP row butterfly)
+  for (int t = 0; t < C; ++t) {
+    float k8[8];
+#pragma unroll
+    for (int ii = 0; ii < 8; ++ii) k8[ii] = L.K[t][8 * T.ti + ii];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      float u = 0.0f;
+#pragma unroll
+      for (int ii = 0; ii < 8; ++ii) u = __builtin_fmaf(S[ii][jj], k8[ii], u);
+      u = row16_sum(u);
+      if (T.ti == 0) L.PW[t][2 * T.tc + jj] = u;
+    }
+  }
+  __syncthreads();
+  if (T.tid < C) L.cf[T.tid] = L.gamma[C - 1] / L.gamma[T.tid];  // gamma_last / gamma_s
+  // A[t][s] = (gamma_t / gamma_s) * (k^_t . k^_s), s < t; each dot a sequential
+  // fma over the width in ascending order. Register tiles of 4 x 4 entries:
+  // per step a thread reads 4 + 4 values and issues 16 fmas.
+  static_assert(C % 16 == 0 && (C / 4) * (C / 4) <= 256, "chunk shape");
+  if (T.tid < (C / 4) * (C / 4)) {
+    const int t0 = 4 * (T.tid / (C / 4)), s0 = 4 * (T.tid % (C / 4));
+    if (s0 <= t0) {  // tiles that touch the strict lower triangle
+      float dot[4][4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) dot[a][b] = 0.0f;
+      for (int i = 0; i < kD; ++i) {
+        float kt[4], ks[4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) kt[a] = L.K[t0 + a][i];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) ks[b] = L.K[s0 + b][i];
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) dot[a][b] = __builtin_fmaf(kt[a], ks[b], dot[a][b]);
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          if (s0 + b < t0 + a) L.A[t0 + a][s0 + b] = (L.gamma[t0 + a] / L.gamma[s0 + b]) * dot[a][b];
+    }
+  }
+  __syncthreads();
+  // forward substitution, one column per thread, the column's w in registers:
+  // w_t = beta_t (v_t - gamma_t P_t - sum_{s<t} A[t][s] w_s), s ascending.
+  // Rows go in blocks of 16: the block's 16 sums over the earlier blocks run
+  // as independent interleaved chains (A read four entries at a time), then
+  // the in-block terms in order; every w_t keeps its single ascending-s chain.
+  if (T.tid < kCB) {
+    const int j = T.tid;
+    float w[C];
+#pragma unroll
+    for (int b0 = 0; b0 < C; b0 += 16) {
+      float acc[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[q] = L.V[b0 + q][j] - L.gamma[b0 + q] * L.PW[b0 + q][j];
+#pragma unroll
+      for (int s4 = 0; s4 < b0; s4 += 4)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const float4 a4 = *reinterpret_cast<const float4*>(&L.A[b0 + q][s4]);
+          acc[q] = __builtin_fmaf(-a4.x, w[s4], acc[q]);
+          acc[q] = __builtin_fmaf(-a4.y, w[s4 + 1], acc[q]);
+          acc[q] = __builtin_fmaf(-a4.z, w[s4 + 2], acc[q]);
+          acc[q] = __builtin_fmaf(-a4.w, w[s4 + 3], acc[q]);
+        }
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+#pragma unroll
+        for (int s = b0; s < b0 + q; ++s) acc[q] = __builtin_fmaf(-L.A[b0 + q][s], w[s], acc[q]);
+        w[b0 + q] = L.beta[b0 + q] * acc[q];
+        L.PW[b0 + q][j] = w[b0 + q];
+      }
+    }
+  }
+  __syncthreads();
+  // k^_s scaled by gamma_last / gamma_s, in place
+  for (int e = T.tid; e < C * kD; e += 256) L.K[e / kD][e % kD] = L.cf[e / kD] * L.K[e / kD][e % kD];
+  __syncthreads();
+  // S_C = gamma_last S0 + sum_s (c_s k^_s) w_s^T, s ascending
+  const float gl = L.gamma[C - 1];
+#pragma unroll
+  for (int ii = 0; ii < 8; ++ii)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) S[ii][jj] = gl * S[ii][jj];
+  for (int s = 0; s < C; ++s) {
+    float kc[8];
+#pragma unroll
+    for (int ii = 0; ii < 8; ++ii) kc[ii] = L.K[s][8 * T.ti + ii];
+    const float2 w2 = *reinterpret_cast<const float2*>(&L.PW[s][2 * T.tc]);
+#pragma unroll
+    for (int ii = 0; ii < 8; ++ii) {
+      S[ii][0] = __builtin_fmaf(kc[ii], w2.x, S[ii][0]);
+      S[ii][1] = __builtin_fmaf(kc[ii], w2.y, S[ii][1]);
+    }
+  }
+  __syncthreads();  // LDS free for the next chunk
+}
+
+// The chunk's inputs into LDS: every global load issued before the first LDS
+// write, so the memory latency is paid once. K: all 128 rows of k^ for the
+// chunk's C tokens; V: the block's 32 columns.
+template <int C, typename KAt, typename VAt, typename GAt>
+__device__ __forceinline__ void fill_chunk(ChunkLds<C>& L, const Tc& T, KAt kat, VAt vat, GAt gat) {
+  constexpr int PK = C * kD / 256, PV = C * kCB / 256;
+  float kr[PK], vr[PV];
+#pragma unroll
+  for (int u = 0; u < PK; ++u) {
+    const int e = T.tid + 256 * u;
+    kr[u] = kat(e / kD, e % kD);
+  }
+#pragma unroll
+  for (int u = 0; u < PV; ++u) {
+    const int e = T.tid + 256 * u;
+    vr[u] = vat(e / kCB, e % kCB);
+  }
+  float al = 0.0f, be = 0.0f;
+  if (T.tid < C) gat(T.tid, al, be);
+#pragma unroll
+  for (int u = 0; u < PK; ++u) {
+    const int e = T.tid + 256 * u;
+    L.K[e / kD][e % kD] = kr[u];
+  }
+#pragma unroll
+  for (int u = 0; u < PV; ++u) {
+    const int e = T.tid + 256 * u;
+    L.V[e / kCB][e % kCB] = vr[u];
+  }
+  if (T.tid < C) {
+    L.alpha[T.tid] = al;
+    L.beta[T.tid] = be;
+  }
+  __syncthreads();
+}
+
+// Column block <-> global state [128][128] fp32 (row-major).
+__device__ __forceinline__ void load_block(float (&S)[8][2], const float* __restrict__ g, int cb, const Tc& T) {
+#pragma unroll
+  for (int ii = 0; ii < 8; ++ii) {
+    const float2 x = *reinterpret_cast<const float2*>(g + (8 * T.ti + ii) * kD + kCB * cb + 2 * T.tc);
+    S[ii][0] = x.x;
+    S[ii][1] = x.y;
+  }
+}
+__device__ __forceinline__ void store_block(const float (&S)[8][2], float* __restrict__ g, int cb, const Tc& T) {
+#pragma unroll
+  for (int ii = 0; ii < 8; ++ii)
+    *reinterpret_cast<float2*>(g + (8 * T.ti + ii) * kD + kCB * cb + 2 * T.tc) = make_float2(S[ii][0], S[ii][1]);
+}
+
+// State block <-> global [128][128] fp32 (row-major), thread's 8x8 block.
+__device__ __forceinline__ void load_state(float (&S)[8][8], const float* __restrict__ g, const Tl& T) {
+#pragma unroll
+  for (int ii = 0; ii < 8; ++ii) {
+    const float4* r = reinterpret_cast<const float4*>(g + (8 * T.ti + ii) * kD + 8 * T.tj);
+    const float4 x = r[0], y = r[1];
+    S[ii][0] = x.x; S[ii][1] = x.y; S[ii][2] = x.z; S[ii][3] = x.w;
+    S[ii][4] = y.x; S[ii][5] = y.y; S[ii][6] = y.z; S[ii][7] = y.w;
+  }
+}
+__device__ __forceinline__ void store_state(const float (&S)[8][8], float* __restrict__ g, const Tl& T) {
+#pragma unroll
+  for (int ii = 0; ii < 8; ++ii) {
+    float4* r = reinterpret_cast<float4*>(g + (8 * T.ti + ii) * kD + 8 * T.tj);
+    r[0] = make_float4(S[ii][0], S[ii][1], S[ii][2], S[ii][3]);
+    r[1] = make_float4(S[ii][4], S[ii][5], S[ii][6], S[ii][7]);
+  }
+}
+
+// Decode cache of one sequence (fp32): running state, last boundary state,
+// and the tokens of the open chunk (k^, v, alpha, beta per slot).
+struct CacheView {
+  float* srun;  // [H][128][128]
+  float* sb;    // [H][128][128]
+  float* kbuf;  // [C][H][128]
+  float* vbuf;  // [C][H][128]
+  float* abuf;  // [C][H]
+  float* bbuf;  // [C][H]
+};
+__device__ __forceinline__ CacheView cache_view(void* base, int64_t seq, int H, int C) {
+  const int64_t per = gdn_cache_floats(H, C);
+  float* p = static_cast<float*>(base) + seq * per;
+  CacheView v;
+  v.srun = p;
+  v.sb = p + (int64_t)H * kD * kD;
+  v.kbuf = v.sb + (int64_t)H * kD * kD;
+  v.vbuf = v.kbuf + (int64_t)C * H * kD;
+  v.abuf = v.vbuf + (int64_t)C * H * kD;
+  v.bbuf = v.abuf + (int64_t)C * H;
+  return v;
+}
+
+// ------------------------------------------------------------------ kernels
+
+// Prep: one wave per (token, head): k^, q^ (fp32) and alpha.
+__global__ __launch_bounds__(256) void gdn_prep_kernel(const uint32_t* __restrict__ q, const uint32_t* __restrict__ k,
+                                                       const float* __restrict__ g, float* __restrict__ qh,
+                                                       float* __restrict__ kh, float* __restrict__ alpha,
+                                                       int64_t TH) {
+  const int64_t th = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (th >= TH) return;  // uniform per wave; no block-wide barrier below
+  const float2 kk = l2norm_pair(k[th * 64 + lane], 1.0f);
+  const float2 qq = l2norm_pair(q[th * 64 + lane], kInvSqrtD);
+  reinterpret_cast<float2*>(kh)[th * 64 + lane] = kk;
+  reinterpret_cast<float2*>(qh)[th * 64 + lane] = qq;
+  if (lane == 0) alpha[th] = gate_alpha(g[th]);
+}
+
+// Sequence bounds from the device table, clamped to [0, T] so that a
+// malformed table can never address outside the buffers (its outputs are
+// then meaningless, but every index stays in range).
+__device__ __forceinline__ int64_t cu_at(const GdnArgs& a, int s) {
+  return min(max((int64_t)a.cu[s], (int64_t)0), a.T);
+}
+// First boundary-state slot of sequence s: floor(cu[s] / C) + s. Slot
+// base(s) + j holds boundary j of sequence s; slots never collide for a
+// well-formed table and stay below T/C + S for any table.
+__device__ __forceinline__ int64_t boundary_base(const GdnArgs& a, int s, int C) { return cu_at(a, s) / C + s; }
+
+// First pass: one workgroup per (sequence, head, column block), the chunks in
+// order.
+template <int C>
+__global__ __launch_bounds__(256, 2) void gdn_boundary_kernel(GdnArgs a) {
+  __shared__ ChunkLds<C> L;
+  const Tc T = col_layout();
+  const int s = blockIdx.x, h = blockIdx.y, cb = blockIdx.z;
+  const int64_t t0 = cu_at(a, s), len = max(cu_at(a, s + 1) - t0, (int64_t)0);
+  const int64_t n = len / C;
+  const int64_t base = boundary_base(a, s, C);
+  const int64_t plane = (int64_t)kD * kD;
+  float S[8][2];
+#pragma unroll
+  for (int ii = 0; ii < 8; ++ii) S[ii][0] = S[ii][1] = 0.0f;
+  store_block(S, a.bstates + (base * a.H + h) * plane, cb, T);
+  for (int64_t j = 0; j < n; ++j) {
+    const int64_t tc0 = t0 + j * C;
+    fill_chunk<C>(
+        L, T, [&](int t, int i) { return a.kh[((tc0 + t) * a.H + h) * kD + i]; },
+        [&](int t, int c) { return bf16_bits_to_f32(a.v[((tc0 + t) * a.H + h) * kD + kCB * cb + c]); },
+        [&](int t, float& al, float& be) {
+          al = a.alpha[(tc0 + t) * a.H + h];
+          be = a.beta[(tc0 + t) * a.H + h];
+        });
+    chunk_update<C>(S, L, T);
+    store_block(S, a.bstates + ((base + j + 1) * a.H + h) * plane, cb, T);
+  }
+  if (a.cache) {
+    const CacheView cv = cache_view(a.cache, s, a.H, C);
+    store_block(S, cv.sb + h * plane, cb, T);
+    if (len % C == 0) store_block(S, cv.srun + h * plane, cb, T);
+  }
+}
+
+// One token's inputs for the thread: k^ and q^ rows, v columns, gates.
+struct TokIn {
+  float k8[8], q8[8], v8[8], a, b;
+};
+__device__ __forceinline__ void load_tok(TokIn& x, const GdnArgs& a, int64_t tok, int h, const Tl& T) {
+  const int64_t r = (tok * a.H + h) * kD;
+  const float4* kp = reinterpret_cast<const float4*>(a.kh + r + 8 * T.ti);
+  const float4* qp = reinterpret_cast<const float4*>(a.qh + r + 8 * T.ti);
+  const float4 k0 = kp[0], k1 = kp[1], q0 = qp[0], q1 = qp[1];
+  x.k8[0] = k0.x; x.k8[1] = k0.y; x.k8[2] = k0.z; x.k8[3] = k0.w;
+  x.k8[4] = k1.x; x.k8[5] = k1.y; x.k8[6] = k1.z; x.k8[7] = k1.w;
+  x.q8[0] = q0.x; x.q8[1] = q0.y; x.q8[2] = q0.z; x.q8[3] = q0.w;
+  x.q8[4] = q1.x; x.q8[5] = q1.y; x.q8[6] = q1.z; x.q8[7] = q1.w;
+  const u32x4 vv = *reinterpret_cast<const u32x4*>(a.v + r + 8 * T.tj);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x.v8[2 * e] = bf16_lo(vv[e]);
+    x.v8[2 * e + 1] = bf16_hi(vv[e]);
+  }
+  x.a = a.alpha[tok * a.H + h];
+  x.b = a.beta[tok * a.H + h];
+}
+
+template <bool OUT_BF16>
+__device__ __forceinline__ void store_out(void* out, int64_t row, const float (&o8)[8], const Tl& T) {
+  if (T.ti != 0) return;
+  if constexpr (OUT_BF16) {
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(o8[2 * e], o8[2 * e + 1]);
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + row + 8 * T.tj) = u32x4{w[0], w[1], w[2], w[3]};
+  } else {
+    float4* p = reinterpret_cast<float4*>(static_cast<float*>(out) + row + 8 * T.tj);
+    p[0] = make_float4(o8[0], o8[1], o8[2], o8[3]);
+    p[1] = make_float4(o8[4], o8[5], o8[6], o8[7]);
+  }
+}
+
+// Second pass: one workgroup per (chunk slot, head); chunk slot c of sequence
+// s is c - boundary_base(s). Runs the recurrence from the chunk's boundary.
+template <int C, bool OUT_BF16>
+__global__ __launch_bounds__(256) void gdn_output_kernel(GdnArgs a) {
+  const Tl T = thread_layout();
+  const int64_t c = blockIdx.x;
+  const int h = blockIdx.y;
+  // the sequence owning slot c: largest s with base(s) <= c (uniform search)
+  int lo = 0, hi = a.S - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (boundary_base(a, mid, C) <= c) lo = mid;
+    else hi = mid - 1;
+  }
+  const int s = lo;
+  const int64_t t0 = cu_at(a, s), len = max(cu_at(a, s + 1) - t0, (int64_t)0);
+  const int64_t j = c - boundary_base(a, s, C);
+  if (j < 0 || j * C >= len) return;  // a slot with no tokens
+  const int64_t plane = (int64_t)kD * kD;
+  float S[8][8];
+  load_state(S, a.bstates + (c * a.H + h) * plane, T);
+  const int64_t ta = t0 + j * C, tb = min(t0 + (j + 1) * C, t0 + len);
+  TokIn cur, nxt;
+  load_tok(cur, a, ta, h, T);
+  for (int64_t t = ta; t < tb; ++t) {
+    if (t + 1 < tb) load_tok(nxt, a, t + 1, h, T);
+    float o8[8];
+    rec_step(S, cur.k8, cur.q8, cur.v8, cur.a, cur.b, o8);
+    store_out<OUT_BF16>(a.out, (t * a.H + h) * kD, o8, T);
+    if (t + 1 < tb) cur = nxt;
+  }
+  // the open chunk of the last slot continues in decode
+  if (a.cache && tb == t0 + len && len % C != 0) {
+    const CacheView cv = cache_view(a.cache, s, a.H, C);
+    store_state(S, cv.srun + h * plane, T);
+    for (int64_t t = ta; t < tb; ++t) {
+      const int slot = (int)(t - ta);
+      const int64_t r = (t * a.H + h) * kD;
+      for (int e = T.tid; e < kD; e += 256) {
+        cv.kbuf[((int64_t)slot * a.H + h) * kD + e] = a.kh[r + e];
+        cv.vbuf[((int64_t)slot * a.H + h) * kD + e] = bf16_bits_to_f32(a.v[r + e]);
+      }
+      if (T.tid == 0) {
+        cv.abuf[(int64_t)slot * a.H + h] = a.alpha[t * a.H + h];
+        cv.bbuf[(int64_t)slot * a.H + h] = a.beta[t * a.H + h];
+      }
+    }
+  }
+}
+
+// Decode, part 1: one token per sequence, one workgroup per (sequence, head).
+// Wave 0 prepares the token exactly as gdn_prep_kernel does; the recurrence
+// step then runs from the cached running state. The token joins the open
+// chunk's buffer at slot pos % C.
+template <int C, bool OUT_BF16>
+__global__ __launch_bounds__(256) void gdn_decode_step_kernel(GdnDecodeArgs a) {
+  __shared__ float kq[2][kD];
+  __shared__ float ab[2];
+  const Tl T = thread_layout();
+  const int bseq = blockIdx.x, h = blockIdx.y;
+  const int64_t pos = a.pos[bseq];
+  const int64_t r = ((int64_t)bseq * a.H + h) * kD;
+  if (pos < 0) {  // a data error: NaN output, the cache untouched (uniform exit)
+    const float nan8[8] = {__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                           __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+    store_out<OUT_BF16>(a.out, r, nan8, T);
+    return;
+  }
+  const int slot = (int)(pos % C);
+  const CacheView cv = cache_view(a.cache, bseq, a.H, C);
+  if (T.tid < 64) {
+    const float2 kk = l2norm_pair(reinterpret_cast<const uint32_t*>(a.k)[r / 2 + T.lane], 1.0f);
+    const float2 qq = l2norm_pair(reinterpret_cast<const uint32_t*>(a.q)[r / 2 + T.lane], kInvSqrtD);
+    kq[0][2 * T.lane] = kk.x;
+    kq[0][2 * T.lane + 1] = kk.y;
+    kq[1][2 * T.lane] = qq.x;
+    kq[1][2 * T.lane + 1] = qq.y;
+    if (T.lane == 0) {
+      ab[0] = gate_alpha(a.g[(int64_t)bseq * a.H + h]);
+      ab[1] = a.beta[(int64_t)bseq * a.H + h];
+    }
+  }
+  __syncthreads();
+  const int64_t plane = (int64_t)kD * kD;
+  float S[8][8];
+  load_state(S, cv.srun + h * plane, T);
+  float k8[8], q8[8], v8[8], o8[8];
+#pragma unroll
+  for (int ii = 0; ii < 8; ++ii) {
+    k8[ii] = kq[0][8 * T.ti + ii];
+    q8[ii] = kq[1][8 * T.ti + ii];
+  }
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) v8[jj] = bf16_bits_to_f32(a.v[r + 8 * T.tj + jj]);
+  rec_step(S, k8, q8, v8, ab[0], ab[1], o8);
+  store_out<OUT_BF16>(a.out, r, o8, T);
+  store_state(S, cv.srun + h * plane, T);
+  for (int e = T.tid; e < kD; e += 256) {
+    cv.kbuf[((int64_t)slot * a.H + h) * kD + e] = kq[0][e];
+    cv.vbuf[((int64_t)slot * a.H + h) * kD + e] = bf16_bits_to_f32(a.v[r + e]);
+  }
+  if (T.tid == 0) {
+    cv.abuf[(int64_t)slot * a.H + h] = ab[0];
+    cv.bbuf[(int64_t)slot * a.H + h] = ab[1];
+  }
+}
+
+// Decode, part 2: where the token closed a chunk, the boundary state is
+// advanced by the same chunk update as the first pass (one workgroup per
+// column block), and the running state resynchronises to it.
+template <int C>
+__global__ __launch_bounds__(256, 2) void gdn_decode_resync_kernel(GdnDecodeArgs a) {
+  __shared__ ChunkLds<C> L;
+  const Tc T = col_layout();
+  const int bseq = blockIdx.x, h = blockIdx.y, cb = blockIdx.z;
+  const int64_t pos = a.pos[bseq];
+  if (pos < 0 || (pos + 1) % C != 0) return;  // uniform
+  const CacheView cv = cache_view(a.cache, bseq, a.H, C);
+  fill_chunk<C>(
+      L, T, [&](int t, int i) { return cv.kbuf[((int64_t)t * a.H + h) * kD + i]; },
+      [&](int t, int c) { return cv.vbuf[((int64_t)t * a.H + h) * kD + kCB * cb + c]; },
+      [&](int t, float& al, float& be) {
+        al = cv.abuf[(int64_t)t * a.H + h];
+        be = cv.bbuf[(int64_t)t * a.H + h];
+      });
+  const int64_t plane = (int64_t)kD * kD;
+  float S[8][2];
+  load_block(S, cv.sb + h * plane, cb, T);
+  chunk_update<C>(S, L, T);
+  store_block(S, cv.sb + h * plane, cb, T);
+  store_block(S, cv.srun + h * plane, cb, T);
+}
+
+}  // namespace
+
+hipError_t launch_gdn_prefill(const GdnArgs& a, int C, bool out_bf16, hipStream_t s) {
+  const int64_t TH = a.T * a.H;
+  if (TH > 0) {
+    hipLaunchKernelGGL(gdn_prep_kernel, dim3((unsigned)((TH + 3) / 4)), dim3(256), 0, s,
+                       reinterpret_cast<const uint32_t*>(a.q), reinterpret_cast<const uint32_t*>(a.k), a.g, a.qh, a.kh,
+                       a.alpha, TH);
+  }
+  const dim3 gb((unsigned)a.S, (unsigned)a.H, (unsigned)(kD / kCB));
+  const dim3 go((unsigned)(a.T / C + a.S), (unsigned)a.H);
+  switch (C) {
+    case 32:
+      hipLaunchKernelGGL(gdn_boundary_kernel<32>, gb, dim3(256), 0, s, a);
+      if (out_bf16) hipLaunchKernelGGL((gdn_output_kernel<32, true>), go, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((gdn_output_kernel<32, false>), go, dim3(256), 0, s, a);
+      break;
+    case 64:
+      hipLaunchKernelGGL(gdn_boundary_kernel<64>, gb, dim3(256), 0, s, a);
+      if (out_bf16) hipLaunchKernelGGL((gdn_output_kernel<64, true>), go, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((gdn_output_kernel<64, false>), go, dim3(256), 0, s, a);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gdn_decode(const GdnDecodeArgs& a, int C, bool out_bf16, hipStream_t s) {
+  const dim3 grid((unsigned)a.B, (unsigned)a.H);
+  const dim3 grid_r((unsigned)a.B, (unsigned)a.H, (unsigned)(kD / kCB));
+  switch (C) {
+    case 32:
+      if (out_bf16) hipLaunchKernelGGL((gdn_decode_step_kernel<32, true>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((gdn_decode_step_kernel<32, false>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL(gdn_decode_resync_kernel<32>, grid_r, dim3(256), 0, s, a);
+      break;
+    case 64:
+      if (out_bf16) hipLaunchKernelGGL((gdn_decode_step_kernel<64, true>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((gdn_decode_step_kernel<64, false>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL(gdn_decode_resync_kernel<64>, grid_r, dim3(256), 0, s, a);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace inv

@@ -83,6 +83,45 @@ hipError_t launch_attn_splits(const AttnLaunch& a, hipStream_t s);
 hipError_t launch_attn_combine(const float* ws, void* out, int64_t Tq, int Hq, int D, int split_kv,
                                bool left_fold, hipStream_t s);
 
+// ---- Gated DeltaNet (CPR) ---------------------------------------------------
+// Floats of one sequence's decode cache: running state and last boundary
+// state [H][128][128] each, then the open chunk's k^, v [C][H][128] and
+// alpha, beta [C][H].
+__host__ __device__ inline int64_t gdn_cache_floats(int H, int C) {
+  return 2LL * H * 128 * 128 + (int64_t)C * H * (2 * 128 + 2);
+}
+struct GdnArgs {
+  const uint16_t* q;      // [T, H, 128] bf16
+  const uint16_t* k;
+  const uint16_t* v;
+  const float* g;         // [T, H] log-decay
+  const float* beta;      // [T, H]
+  const int32_t* cu;      // [S+1]
+  int S;
+  int64_t T;
+  int H;
+  void* out;              // [T, H, 128]
+  void* cache;            // [S] decode caches, nullable
+  float* qh;              // workspace: [T, H, 128]
+  float* kh;              // [T, H, 128]
+  float* alpha;           // [T, H]
+  float* bstates;         // [T/C + S, H, 128, 128] boundary states
+};
+struct GdnDecodeArgs {
+  const uint16_t* q;      // [B, H, 128] bf16
+  const uint16_t* k;
+  const uint16_t* v;
+  const float* g;         // [B, H]
+  const float* beta;
+  const int32_t* pos;     // [B] position of this token in its sequence
+  int B;
+  int H;
+  void* out;              // [B, H, 128]
+  void* cache;            // [B] decode caches
+};
+hipError_t launch_gdn_prefill(const GdnArgs& a, int C, bool out_bf16, hipStream_t s);
+hipError_t launch_gdn_decode(const GdnDecodeArgs& a, int C, bool out_bf16, hipStream_t s);
+
 // ---- MoE --------------------------------------------------------------------
 hipError_t launch_moe_route(const float* logits, int32_t* ids, float* w, int64_t T, int E, int k,
                             hipStream_t s);

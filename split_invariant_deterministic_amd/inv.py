@@ -27,7 +27,7 @@ OK, E_ARG, E_CONTRACT, E_TOPOLOGY, E_UNSUPPORTED, E_HIP, E_WORKSPACE = range(7)
 BF16, FP32 = 1, 2
 BALANCED, LEFT_FOLD = 1, 2
 OP_GEMM, OP_TREE_COMBINE, OP_RMSNORM, OP_LOGPROB, OP_DECODE_ATTN, OP_MOE_ROUTE, OP_MOE_GEMM, \
-    OP_MOE_COMBINE, OP_LMHEAD_LOGPROB, OP_LOGPROB_BLOCK16 = range(1, 11)
+    OP_MOE_COMBINE, OP_LMHEAD_LOGPROB, OP_LOGPROB_BLOCK16, OP_GDN_PREFILL, OP_GDN_DECODE = range(1, 13)
 ABI_VERSION = 1
 
 _DT = {"bf16": BF16, "fp32": FP32, BF16: BF16, FP32: FP32}
@@ -91,6 +91,8 @@ _SIGS = {
     "inv_moe_combine": [_CP, _P, _P, _P, _I64, _P, _I64, _I64, _P],
     "inv_lmhead_logprob": [_CP, _P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P],
     "inv_logprob_block16": [_CP, _P, _I64, _P, _P, _I64, _I64, _P, _SZ, _P],
+    "inv_gdn_prefill": [_CP, _P, _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _P, _P, _P, _SZ, _P],
+    "inv_gdn_decode": [_CP, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P],
 }
 for _name, _args in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -98,6 +100,8 @@ for _name, _args in _SIGS.items():
     _f.restype = ctypes.c_int
 _lib.inv_workspace_bytes.argtypes = [_CP, ctypes.c_int, _I64, _I64, _I64]
 _lib.inv_workspace_bytes.restype = _SZ
+_lib.inv_gdn_cache_bytes.argtypes = [_CP, _I32]
+_lib.inv_gdn_cache_bytes.restype = _SZ
 _lib.inv_status_string.argtypes = [ctypes.c_int]
 _lib.inv_status_string.restype = ctypes.c_char_p
 
@@ -121,7 +125,7 @@ for _name, _args in {
     _f.argtypes = _args
     _f.restype = ctypes.c_int
 
-EXPORTS = sorted(list(_SIGS) + ["inv_workspace_bytes", "inv_status_string", "inv_contract_json",
+EXPORTS = sorted(list(_SIGS) + ["inv_workspace_bytes", "inv_status_string", "inv_gdn_cache_bytes", "inv_contract_json",
                                 "inv_contract_digest", "inv_contract_verify", "inv_sha256"])
 
 
@@ -409,6 +413,47 @@ def logprob_block16(logits, target, c, out=None, ws=None):
         ws = block16_workspace(M, V, logits.device)
     _call("inv_logprob_block16", ctypes.byref(c), _ptr(logits), ldl, _ptr(target), _ptr(out), M, V, _ptr(ws),
           ws.numel() * ws.element_size(), _stream())
+    return out
+
+
+# ------------------------------------------------------------------ Gated DeltaNet (CPR)
+
+def gdn_cache(c, S, H, device):
+    """Zeroed decode caches for S sequences (the state of empty sequences)."""
+    n = _lib.inv_gdn_cache_bytes(ctypes.byref(c), H)
+    if n == ctypes.c_size_t(-1).value:
+        raise InvError(E_CONTRACT, "inv_gdn_cache_bytes")
+    return torch.zeros(S * n // 4, dtype=torch.float32, device=device)
+
+
+def gdn_prefill(q, k, v, g, beta, cu_seqlens, c, out=None, cache=None, ws=None):
+    """CPR Gated DeltaNet over packed sequences (inv_gdn_prefill): out [T, H, 128]."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, torch.bfloat16, n, 3)
+    _need(g, torch.float32, "g", 2)
+    _need(beta, torch.float32, "beta", 2)
+    _need(cu_seqlens, torch.int32, "cu_seqlens", 1)
+    T, H, D = q.shape
+    S = cu_seqlens.shape[0] - 1
+    if out is None:
+        out = torch.empty((T, H, D), dtype=_out_torch_dtype(c), device=q.device)
+    if ws is None:
+        ws = torch.empty(workspace_bytes(c, OP_GDN_PREFILL, T, H, S), dtype=torch.uint8, device=q.device)
+    _call("inv_gdn_prefill", ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), S,
+          T, H, D, _ptr(out), _ptr(cache), _ptr(ws), ws.numel() * ws.element_size(), _stream())
+    return out
+
+
+def gdn_decode(q, k, v, g, beta, pos, cache, c, out=None):
+    """One decode token per sequence (inv_gdn_decode); cache is updated in place."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, torch.bfloat16, n, 3)
+    _need(pos, torch.int32, "pos", 1)
+    B, H, D = q.shape
+    if out is None:
+        out = torch.empty((B, H, D), dtype=_out_torch_dtype(c), device=q.device)
+    _call("inv_gdn_decode", ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(pos), B, H, D,
+          _ptr(out), _ptr(cache), _stream())
     return out
 
 

@@ -27,6 +27,9 @@ synthetic draws stand in for the trained weights and prompts the pages use):
            K, V [sum L, 8, 128]
 * moe:     router logits [T, 128] fp32, x [T, 2048], W1 [128, 1536, 2048] *
            0.02, W2 [128, 2048, 768] * 0.02
+* gdn:     packed sequences of the given lengths, q, k, v [T, H, 128] bf16
+           N(0, 1), log-decay g [T, H] fp32 uniform in [-0.5, 0], writing
+           strength beta [T, H] fp32 uniform in [0, 1]
 """
 
 import torch
@@ -113,3 +116,14 @@ def moe(T=8192, H=2048, E=128, F=768, seed=0, device="cpu"):
         "W1": randn((E, 2 * F, H), s + 2, 0.02, device=device),
         "W2": randn((E, H, F), s + 3, 0.02, device=device),
     }
+
+
+def gdn(lengths, H=16, seed=0, device="cpu"):
+    s = seed * 1000 + 60
+    lengths = [int(x) for x in lengths]
+    T = sum(lengths)
+    cu = torch.tensor([0] + lengths, dtype=torch.int64).cumsum(0).to(torch.int32)
+    g = torch.rand((T, H), generator=_gen(s + 3, device), device=device) * -0.5
+    beta = torch.rand((T, H), generator=_gen(s + 4, device), device=device)
+    return {"q": randn((T, H, 128), s + 0, device=device), "k": randn((T, H, 128), s + 1, device=device),
+            "v": randn((T, H, 128), s + 2, device=device), "g": g, "beta": beta, "cu_seqlens": cu.to(device)}
