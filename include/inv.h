@@ -155,7 +155,8 @@ typedef enum inv_region {
   INV_REGION_MOE_ROUTE = 6,   /* top-k routing                             */
   INV_REGION_MOE_EXPERTS = 7, /* grouped expert GEMMs                      */
   INV_REGION_MOE_COMBINE = 8, /* fixed-order combine                       */
-  INV_REGION_LMHEAD_LOGPROB = 9 /* fused LM head + logprob (16-col blocks) */
+  INV_REGION_LMHEAD_LOGPROB = 9, /* fused LM head + logprob (16-col blocks) */
+  INV_REGION_GDN = 10            /* CPR Gated DeltaNet (gdn.core)         */
 } inv_region;
 
 /* One composition entry: a region and the contract pinned for it. */

@@ -168,6 +168,7 @@ const RegionInfo kRegions[] = {
     {INV_REGION_MOE_EXPERTS, "moe.experts", INV_OP_MOE_GEMM, "grouped_k_leaf_mfma_tree", 1},
     {INV_REGION_MOE_COMBINE, "moe.combine", INV_OP_MOE_COMBINE, "expert_id_leaf_tree", 1},
     {INV_REGION_LMHEAD_LOGPROB, "lm_head_logprob", INV_OP_LMHEAD_LOGPROB, "k_leaf_mfma_tree_block16_epilogue", 1},
+    {INV_REGION_GDN, "gdn.core", INV_OP_GDN_PREFILL, "cpr_boundary_closed_form_recurrent_scan", 1},
 };
 
 const RegionInfo* region_info(int region) {
@@ -217,6 +218,12 @@ std::string constants(const RegionInfo& r, const inv_contract& c) {
              ",\"leaf_chain\":\"v_mfma_f32_16x16x32_bf16, ascending k from +0\"" +
              ",\"vocab_block\":16,\"block_sum\":\"balanced over the column index\"" +
              ",\"block_merge\":\"balanced, padded with (-inf, 0) to a power of two\"}";
+    case INV_REGION_GDN:
+      return "{\"chunk\":" + u(c.kv_chunk) + acc + ",\"state_dtype\":\"fp32\",\"out_dtype\":" +
+             q(dtype_name(c.out_dtype)) +
+             ",\"boundary\":\"chunkwise closed form, unit-lower-triangular solve by forward substitution\"" +
+             ",\"outputs\":\"token recurrence from the chunk's boundary state\"" +
+             ",\"decode\":\"recurrence, resynchronised to the boundary state when a chunk closes\"}";
     case INV_REGION_MOE_COMBINE:
       return "{\"leaves\":" + u(c.leaves) + ",\"tree\":" + q(tree_name(c.tree)) + acc +
              ",\"leaf_order\":\"ascending expert id\",\"out_dtype\":\"bf16\"}";
@@ -262,7 +269,8 @@ inv_status build(const inv_region_contract* e, size_t n, Sections& out) {
     comp += sep + "{\"region\":" + q(r.name) + ",\"cases\":" + kCases + ",\"impl\":{\"id\":" + q(r.impl) +
             ",\"version\":" + u(r.version) + ",\"arch\":\"gfx950\"},\"constants\":" + constants(r, c) + "}";
     topo += sep + q(r.name) + ":{\"proven_ranks\":" +
-            (r.region == INV_REGION_MOE_EXPERTS || r.region == INV_REGION_LMHEAD_LOGPROB ? std::string("[1]")
+            (r.region == INV_REGION_MOE_EXPERTS || r.region == INV_REGION_LMHEAD_LOGPROB || r.region == INV_REGION_GDN
+                 ? std::string("[1]")
                                                                                         : proven(c.leaves)) +
             "}";
     ranks += sep + q(r.name) + ":" + u(c.ranks);
@@ -272,6 +280,9 @@ inv_status build(const inv_region_contract* e, size_t n, Sections& out) {
       char buf[16];
       std::snprintf(buf, sizeof(buf), "0x%08x", bits);
       sem_const += std::string(sem_const.size() > 1 ? "," : "") + q(r.name) + ":{\"eps_fp32_bits\":" + q(buf) + "}";
+    } else if (r.region == INV_REGION_GDN) {
+      sem_const += std::string(sem_const.size() > 1 ? "," : "") + q(r.name) +
+                   ":{\"head_width\":128,\"l2norm_eps_fp32_bits\":\"0x358637bd\",\"gate\":\"alpha = exp(g)\"}";
     } else if (r.region == INV_REGION_MOE_ROUTE || r.region == INV_REGION_MOE_COMBINE) {
       sem_const += std::string(sem_const.size() > 1 ? "," : "") + q(r.name) + ":{\"top_k\":" + u(c.leaves) + "}";
     }

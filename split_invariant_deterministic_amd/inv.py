@@ -111,7 +111,7 @@ class RegionContract(ctypes.Structure):
 
 
 REGIONS = {"norms.rms": 1, "linear": 2, "lm_head": 3, "logprob": 4, "attention": 5, "moe.route": 6,
-           "moe.experts": 7, "moe.combine": 8, "lm_head_logprob": 9}
+           "moe.experts": 7, "moe.combine": 8, "lm_head_logprob": 9, "gdn.core": 10}
 DIGEST_SEMANTIC, DIGEST_NUMERICAL_POLICY, DIGEST_DEPLOYMENT = 1, 2, 3
 _RCP = ctypes.POINTER(RegionContract)
 _D32 = ctypes.c_uint8 * 32

@@ -90,6 +90,11 @@ def test_workspace_sizes():
     assert inv.workspace_bytes(c32, inv.OP_LMHEAD_LOGPROB, 4096, 151936, 4096) == 4096 * 9496 * 8 + 4096 * 4
     assert inv.workspace_bytes(c32, inv.OP_LOGPROB_BLOCK16, 3, 17, 0) == 3 * 2 * 8 + 3 * 4
     assert inv.workspace_bytes(inv.contract(), inv.OP_LMHEAD_LOGPROB, 8, 512, 256) == ctypes.c_size_t(-1).value
+    cg = inv.contract(kv_chunk=64)
+    T, H, S = 10240, 16, 5
+    assert inv.workspace_bytes(cg, inv.OP_GDN_PREFILL, T, H, S) == \
+        (2 * T * H * 128 + T * H + (T // 64 + S) * H * 128 * 128) * 4 + 16
+    assert inv._lib.inv_gdn_cache_bytes(ctypes.byref(cg), 16) == (2 * 16 * 128 * 128 + 64 * 16 * 258) * 4
 
 
 def test_entry_points_reject_before_any_launch():
@@ -150,6 +155,19 @@ def test_entry_points_reject_before_any_launch():
     assert lib.inv_lmhead_logprob(by(cl), fake, fake, fake, fake, 0, 512, 256, null, 0, null) == inv.OK
     assert lib.inv_logprob_block16(by(cl), fake, 10, fake, fake, 4, 16, fake, big, null) == inv.E_ARG  # ldl < V
     assert lib.inv_logprob_block16(by(cl), fake, 16, fake, fake, 4, 16, null, 0, null) == inv.E_WORKSPACE
+    # CPR Gated DeltaNet: width 128, chunk 32 or 64, one rank, enough aligned workspace
+    cg = inv.contract(kv_chunk=64)
+    gp = lambda c, D, ws, nbytes, cache=null: lib.inv_gdn_prefill(by(c), fake, fake, fake, fake, fake, fake, 2, 256,
+                                                                   16, D, fake, cache, ws, nbytes, null)
+    assert gp(cg, 64, fake, big) == inv.E_UNSUPPORTED
+    assert gp(inv.contract(kv_chunk=128), 128, fake, big) == inv.E_CONTRACT
+    assert gp(inv.contract(kv_chunk=64, ranks=2), 128, fake, big) == inv.E_UNSUPPORTED
+    assert gp(cg, 128, fake, 1024) == inv.E_WORKSPACE
+    assert gp(cg, 128, ctypes.c_void_p((1 << 20) + 4), big) == inv.E_ARG
+    assert gp(cg, 128, fake, big, ctypes.c_void_p((1 << 20) + 8)) == inv.E_ARG  # misaligned cache
+    assert lib.inv_gdn_decode(by(cg), fake, fake, fake, fake, fake, fake, 0, 16, 128, fake, fake, null) == inv.OK
+    assert lib.inv_gdn_decode(by(cg), fake, fake, fake, fake, fake, fake, 4, 16, 128, fake, null, null) \
+        == inv.E_ARG
 
 
 def test_status_strings():

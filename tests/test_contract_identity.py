@@ -40,6 +40,7 @@ def path_composition(inv, **over):
         "moe.experts": inv.contract(leaves=8),
         "moe.combine": inv.contract(leaves=8),
         "lm_head_logprob": inv.contract(leaves=8, out="fp32"),
+        "gdn.core": inv.contract(kv_chunk=64),
     }
     e.update(over)
     return e
@@ -94,7 +95,7 @@ def test_json_layout_and_identities(inv):
     assert json.dumps(json.loads(text), separators=(",", ":")) == text
     regions = [c["region"] for c in d["composition"]]
     assert regions == ["norms.rms", "linear", "lm_head", "logprob", "attention", "moe.route",
-                       "moe.experts", "moe.combine", "lm_head_logprob"]
+                       "moe.experts", "moe.combine", "lm_head_logprob", "gdn.core"]
     assert by_region(d)["lm_head_logprob"]["constants"]["vocab_block"] == 16
     by = {c["region"]: c for c in d["composition"]}
     assert by["linear"]["constants"]["leaves"] == 8 and by["lm_head"]["constants"]["out_dtype"] == "fp32"
@@ -132,6 +133,7 @@ def _digests(inv, e):
     ({"attention": dict(split_kv=8)}, "policy"),
     ({"attention": dict(kv_chunk=128)}, "policy"),
     ({"lm_head_logprob": dict(leaves=4, out="fp32")}, "policy"),
+    ({"gdn.core": dict(kv_chunk=32)}, "policy"),
     ({"linear": dict(leaves=8, ranks=4)}, "deployment"),   # a proven rank count: same bits
     ({"logprob": dict(leaves=64, ranks=2)}, "deployment"),
     ({"norms.rms": dict(eps=1e-5)}, "semantic"),           # a different model
@@ -176,6 +178,9 @@ def test_invalid_compositions_are_rejected(inv):
     assert ex.value.status == inv.E_CONTRACT
     with pytest.raises(inv.InvError) as ex:
         inv.contract_json({"lm_head_logprob": inv.contract(leaves=8)})  # logits must stay fp32
+    assert ex.value.status == inv.E_CONTRACT
+    with pytest.raises(inv.InvError) as ex:
+        inv.contract_json({"gdn.core": inv.contract(kv_chunk=128)})  # chunks of 32 or 64
     assert ex.value.status == inv.E_CONTRACT
     with pytest.raises(inv.InvError) as ex:
         inv.contract_json({99: inv.contract()})
