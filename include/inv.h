@@ -128,7 +128,7 @@ inv_status inv_contract_check(const inv_contract* c, int op, int64_t K);
  *   INV_OP_LMHEAD_LOGPROB, INV_OP_LOGPROB_BLOCK16: d0 = M, d1 = V, d2 = K
  *                       -> M*ceil(V/16)*8 + M*4
  *   INV_OP_GDN_PREFILL: d0 = T tokens, d1 = H heads, d2 = S sequences
- *                       -> (2*T*H*128 + T*H + (T/C + S)*H*128*128)*4 + 16
+ *                       -> (2*T*H*128 + T*H + (T/C + S)*H*(128*128 + C*C + 2C))*4 + 16
  * Returns (size_t)-1 if the contract is invalid. Host only. */
 size_t inv_workspace_bytes(const inv_contract* c, int op, int64_t d0, int64_t d1, int64_t d2);
 
@@ -434,9 +434,11 @@ inv_status inv_logprob_block16(const inv_contract* c, const float* logits, int64
  * Boundaries at multiples of C = c->kv_chunk (32 or 64) from each sequence's
  * first token; a boundary state is the previous one advanced by the
  * chunkwise closed form of the recurrence (gamma = running product of alpha
- * inside the chunk, w from the unit-lower-triangular solve, S_C = gamma_C S_0
- * + sum_s (gamma_C / gamma_s) k^_s w_s^T); every output comes from the
- * token-by-token recurrence started at its chunk's boundary state.
+ * inside the chunk; w = M r with M = (I + diag(beta) A)^-1 diag(beta) by
+ * forward substitution, A[t][s] = (gamma_t/gamma_s)(k^_s . k^_t) for s < t,
+ * r_t = v_t - gamma_t S_0^T k^_t; S_C = gamma_C S_0 + sum_s (gamma_C /
+ * gamma_s) k^_s w_s^T); every output comes from the token-by-token
+ * recurrence started at its chunk's boundary state.
  * The same device functions run in both entry points, so a sequence
  * prefilled to any length and continued by decode gives, token for token,
  * the bits of one prefill of the whole sequence. c->ranks must be 1;
@@ -445,8 +447,9 @@ inv_status inv_logprob_block16(const inv_contract* c, const float* logits, int64
 
 /* Bytes of one sequence's decode cache: the running state and the last
  * boundary state [H][128][128] fp32 each, then the open chunk's k^ and v
- * [C][H][128] fp32 and alpha, beta [C][H] fp32. A fresh sequence's cache is
- * all zeros. (size_t)-1 if the contract is invalid. */
+ * [C][H][128] fp32 and alpha, beta [C][H] fp32, then [H][C*C + 2C] fp32 of
+ * scratch for the chunk-closing step. A fresh sequence's cache is all zeros.
+ * (size_t)-1 if the contract is invalid. */
 size_t inv_gdn_cache_bytes(const inv_contract* c, int32_t H);
 
 /* Prefill / training forward of S packed sequences (cu_seqlens [S+1] int32,
@@ -455,7 +458,8 @@ size_t inv_gdn_cache_bytes(const inv_contract* c, int32_t H);
  * per sequence, the decode cache after the sequence's last token (cache
  * [S] x inv_gdn_cache_bytes). Workspace: ws_bytes >=
  * inv_workspace_bytes(INV_OP_GDN_PREFILL, T, H, S), 16-byte aligned; it holds
- * k^, q^, alpha and every boundary state. */
+ * k^, q^, alpha, every boundary state and every chunk's M, gamma and gamma
+ * ratios. */
 inv_status inv_gdn_prefill(const inv_contract* c, const void* q, const void* k, const void* v, const float* g,
                            const float* beta, const int32_t* cu_seqlens, int32_t S, int64_t T, int32_t H,
                            int32_t D, void* out, void* cache, void* ws, size_t ws_bytes, hipStream_t stream);

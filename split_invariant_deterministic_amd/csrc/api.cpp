@@ -66,7 +66,8 @@ inv_status check_gdn_contract(const inv_contract* c) {
 }
 
 size_t gdn_prefill_ws_bytes(int64_t T, int64_t H, int64_t S, int64_t C) {
-  return ((size_t)2 * T * H * 128 + (size_t)T * H + (size_t)(T / C + S) * H * 128 * 128) * sizeof(float);
+  return ((size_t)2 * T * H * 128 + (size_t)T * H + (size_t)(T / C + S) * H * (128 * 128 + C * C + 2 * C)) *
+         sizeof(float);
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -365,10 +366,11 @@ inv_status inv_gdn_prefill(const inv_contract* c, const void* q, const void* k, 
   a.qh = w;
   a.kh = w + T * H * 128;
   a.alpha = w + 2 * T * H * 128;
-  // boundary states start on a 16-byte boundary
+  // boundary states and chunk coefficients start on 16-byte boundaries
+  const int64_t slots = T / c->kv_chunk + S, C = c->kv_chunk;
   a.bstates = w + ((2 * T * H * 128 + T * H + 3) / 4) * 4;
-  if (reinterpret_cast<char*>(a.bstates + (T / c->kv_chunk + S) * H * 128 * 128) >
-      static_cast<char*>(ws) + ws_bytes)
+  a.coef = a.bstates + slots * H * 128 * 128;
+  if (reinterpret_cast<char*>(a.coef + slots * H * (C * C + 2 * C)) > static_cast<char*>(ws) + ws_bytes)
     return INV_E_WORKSPACE;
   return hip_status(inv::launch_gdn_prefill(a, (int)c->kv_chunk, out_is_bf16(c), stream));
 }

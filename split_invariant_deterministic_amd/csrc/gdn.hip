@@ -6,16 +6,20 @@
 // parallel pass runs the recurrence inside every chunk from its boundary
 // state, and decode runs the recurrence but resynchronises to the boundary
 // state every C tokens. Prefill and decode therefore share one rounding
-// schedule: the same two device functions below (rec_step for a token,
-// chunk_update for a boundary), on the same thread layout, in both.
+// schedule: the same device functions below (rec_step for a token,
+// chunk_coeffs and chunk_state for a boundary), on the same thread layouts,
+// in both.
 //
 // Layer (gated delta rule, one head, width 128, restated):
 //   k^ = k / sqrt(sum k^2 + eps), q^ = q / sqrt(sum q^2 + eps) * 128^(-1/2)
 //   alpha = exp(g); S_t = alpha (S - beta k^ (k^T S)) + beta k^ v^T; o_t = S_t^T q^
 // Boundary states use the chunkwise closed form of the same recurrence:
 //   gamma_t = alpha_0 ... alpha_t (running product inside the chunk)
-//   w_t = beta_t (v_t - gamma_t S0^T k^_t - sum_{s<t} (gamma_t/gamma_s)(k^_s.k^_t) w_s)
+//   w = M r, M = (I + diag(beta) A)^(-1) diag(beta), A[t][s] = (gamma_t/gamma_s)(k^_s.k^_t)
+//       for s < t, r_t = v_t - gamma_t S0^T k^_t
 //   S_C = gamma_{C-1} S0 + sum_s (gamma_{C-1}/gamma_s) k^_s w_s^T
+// M, gamma and the ratios do not depend on the state, so in a prefill they
+// are computed for every chunk in parallel; only r, w and S_C stay serial.
 //
 // Thread layout (256 threads): for the recurrence, thread (ti, tj),
 // ti = lane % 16, tj = 4 * wave + lane / 16, holds S[8ti .. 8ti+8)[8tj .. 8tj+8)
@@ -123,24 +127,34 @@ __device__ __forceinline__ Tc col_layout() {
   return t;
 }
 
-// LDS of one chunk update of one column block: inputs K (k^, all 128 rows),
-// V (the block's 32 columns of v, fp32), alpha, beta; scratch P (then W, in
-// place), A, gamma, c.
+// LDS of one chunk update of one column block. K: k^ of the chunk's C tokens
+// (all 128 rows); V: the block's 32 columns of v (fp32); MT: M transposed
+// (MT[s][t] = M[t][s]); gates and their running products; A (coefficient
+// phase) shares space with R and W (state phase).
 template <int C>
 struct alignas(16) ChunkLds {
   float K[C][kKStride];
+  float MT[C][C];
   float V[C][kCB];
-  float PW[C][kCB];
-  float A[C][C];
   float alpha[C], beta[C], gamma[C], cf[C];
+  union {
+    float A[C][C];
+    struct {
+      float R[C][kCB];
+      float W[C][kCB];
+    } st;
+  } u;
 };
 
-// S (registers, the block of boundary state b_j on entry) becomes b_{j+1}.
-// The chunk's inputs are in L.K / L.V / L.alpha / L.beta, visible to all.
+// Coefficients of a chunk, independent of the state: gamma_t = alpha_0 ...
+// alpha_t (one thread, ascending), cf_s = gamma_last / gamma_s, the strictly
+// lower A[t][s] = (gamma_t / gamma_s) (k^_s . k^_t), and
+// M = (I + diag(beta) A)^(-1) diag(beta), lower triangular, column c by
+// forward substitution: M[t][c] = -beta_t (sum_{s<t} A[t][s] M[s][c] - [t == c])
+// (s ascending from 0): signed zeros above the diagonal, beta_c on it.
+// Needs K, alpha, beta; writes gamma, cf, MT (A is scratch).
 template <int C>
-__device__ void chunk_update(float (&S)[8][2], ChunkLds<C>& L, const Tc& T) {
-  // running products of the gates (one thread, ascending; the gates read
-  // into registers first so the chain does not wait on LDS)
+__device__ void chunk_coeffs(ChunkLds<C>& L, const Tc& T) {
   if (T.tid == 0) {
     float gm = 1.0f;  // 1 * alpha_0 = alpha_0 exactly
 #pragma unroll
@@ -155,30 +169,14 @@ __device__ void chunk_update(float (&S)[8][2], ChunkLds<C>& L, const Tc& T) {
       }
     }
   }
-  // P[t][j] = sum_i k^_t[i] S0[i][j]: the thread's 8 rows as one fma chain,
-  // then the balanced tree over the 16 row groups (a DPP row butterfly)
-  for (int t = 0; t < C; ++t) {
-    float k8[8];
-#pragma unroll
-    for (int ii = 0; ii < 8; ++ii) k8[ii] = L.K[t][8 * T.ti + ii];
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      float u = 0.0f;
-#pragma unroll
-      for (int ii = 0; ii < 8; ++ii) u = __builtin_fmaf(S[ii][jj], k8[ii], u);
-      u = row16_sum(u);
-      if (T.ti == 0) L.PW[t][2 * T.tc + jj] = u;
-    }
-  }
   __syncthreads();
-  if (T.tid < C) L.cf[T.tid] = L.gamma[C - 1] / L.gamma[T.tid];  // gamma_last / gamma_s
-  // A[t][s] = (gamma_t / gamma_s) * (k^_t . k^_s), s < t; each dot a sequential
-  // fma over the width in ascending order. Register tiles of 4 x 4 entries:
-  // per step a thread reads 4 + 4 values and issues 16 fmas.
+  if (T.tid < C) L.cf[T.tid] = L.gamma[C - 1] / L.gamma[T.tid];
+  // Gram entries: each dot a sequential fma over the width in ascending order,
+  // in register tiles of 4 x 4 (per step 4 + 4 reads, 16 fmas)
   static_assert(C % 16 == 0 && (C / 4) * (C / 4) <= 256, "chunk shape");
   if (T.tid < (C / 4) * (C / 4)) {
     const int t0 = 4 * (T.tid / (C / 4)), s0 = 4 * (T.tid % (C / 4));
-    if (s0 <= t0) {  // tiles that touch the strict lower triangle
+    if (s0 <= t0) {
       float dot[4][4];
 #pragma unroll
       for (int a = 0; a < 4; ++a)
@@ -199,57 +197,113 @@ __device__ void chunk_update(float (&S)[8][2], ChunkLds<C>& L, const Tc& T) {
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b)
-          if (s0 + b < t0 + a) L.A[t0 + a][s0 + b] = (L.gamma[t0 + a] / L.gamma[s0 + b]) * dot[a][b];
+          L.u.A[t0 + a][s0 + b] = s0 + b < t0 + a ? (L.gamma[t0 + a] / L.gamma[s0 + b]) * dot[a][b] : 0.0f;
     }
   }
   __syncthreads();
-  // forward substitution, one column per thread, the column's w in registers:
-  // w_t = beta_t (v_t - gamma_t P_t - sum_{s<t} A[t][s] w_s), s ascending.
-  // Rows go in blocks of 16: the block's 16 sums over the earlier blocks run
-  // as independent interleaved chains (A read four entries at a time), then
-  // the in-block terms in order; every w_t keeps its single ascending-s chain.
-  if (T.tid < kCB) {
-    const int j = T.tid;
-    float w[C];
+  // M column c on thread c, in registers. Rows go in blocks of 16: the block's
+  // 16 sums over the earlier blocks run as interleaved independent chains
+  // (A read four entries at a time), then the in-block terms in order; every
+  // entry keeps its single ascending-s chain.
+  if (T.tid < C) {
+    const int c = T.tid;
+    float m[C];
 #pragma unroll
     for (int b0 = 0; b0 < C; b0 += 16) {
       float acc[16];
 #pragma unroll
-      for (int q = 0; q < 16; ++q) acc[q] = L.V[b0 + q][j] - L.gamma[b0 + q] * L.PW[b0 + q][j];
+      for (int q = 0; q < 16; ++q) acc[q] = 0.0f;
 #pragma unroll
       for (int s4 = 0; s4 < b0; s4 += 4)
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
-          const float4 a4 = *reinterpret_cast<const float4*>(&L.A[b0 + q][s4]);
-          acc[q] = __builtin_fmaf(-a4.x, w[s4], acc[q]);
-          acc[q] = __builtin_fmaf(-a4.y, w[s4 + 1], acc[q]);
-          acc[q] = __builtin_fmaf(-a4.z, w[s4 + 2], acc[q]);
-          acc[q] = __builtin_fmaf(-a4.w, w[s4 + 3], acc[q]);
+          const float4 a4 = *reinterpret_cast<const float4*>(&L.u.A[b0 + q][s4]);
+          acc[q] = __builtin_fmaf(a4.x, m[s4], acc[q]);
+          acc[q] = __builtin_fmaf(a4.y, m[s4 + 1], acc[q]);
+          acc[q] = __builtin_fmaf(a4.z, m[s4 + 2], acc[q]);
+          acc[q] = __builtin_fmaf(a4.w, m[s4 + 3], acc[q]);
         }
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
+        const int t = b0 + q;
 #pragma unroll
-        for (int s = b0; s < b0 + q; ++s) acc[q] = __builtin_fmaf(-L.A[b0 + q][s], w[s], acc[q]);
-        w[b0 + q] = L.beta[b0 + q] * acc[q];
-        L.PW[b0 + q][j] = w[b0 + q];
+        for (int s = b0; s < t; ++s) acc[q] = __builtin_fmaf(L.u.A[t][s], m[s], acc[q]);
+        // right-hand side e_c: m_t = -beta_t (acc_t - [t == c]); above the
+        // diagonal acc is +0 and m_t a signed zero, on it m_c = beta_c exactly
+        m[t] = -L.beta[t] * (acc[q] - (t == c ? 1.0f : 0.0f));
       }
+#pragma unroll
+      for (int q = 0; q < 16; q += 4)
+        *reinterpret_cast<float4*>(&L.MT[c][b0 + q]) = make_float4(m[b0 + q], m[b0 + q + 1], m[b0 + q + 2],
+                                                                     m[b0 + q + 3]);
     }
   }
   __syncthreads();
-  // k^_s scaled by gamma_last / gamma_s, in place
-  for (int e = T.tid; e < C * kD; e += 256) L.K[e / kD][e % kD] = L.cf[e / kD] * L.K[e / kD][e % kD];
+}
+
+// S (registers, the block of boundary state b_j on entry) becomes b_{j+1}:
+//   r_t = v_t - gamma_t P_t with P_t = S0^T k^_t (per column: the thread's 8
+//         rows as one fma chain, then the balanced tree over the 16 row groups)
+//   w_t = sum_s M[t][s] r_s  (s ascending over the whole chunk; M is +0 above
+//         the diagonal)
+//   S_C = gamma_last S0 + sum_s (cf_s k^_s) w_s^T  (s ascending)
+// Needs K, V, MT, gamma, cf.
+template <int C>
+__device__ void chunk_state(float (&S)[8][2], ChunkLds<C>& L, const Tc& T) {
+#pragma unroll 4
+  for (int t = 0; t < C; ++t) {
+    float k8[8];
+#pragma unroll
+    for (int ii = 0; ii < 8; ++ii) k8[ii] = L.K[t][8 * T.ti + ii];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      float u = 0.0f;
+#pragma unroll
+      for (int ii = 0; ii < 8; ++ii) u = __builtin_fmaf(S[ii][jj], k8[ii], u);
+      u = row16_sum(u);
+      if (T.ti == 0) L.u.st.R[t][2 * T.tc + jj] = L.V[t][2 * T.tc + jj] - L.gamma[t] * u;
+    }
+  }
   __syncthreads();
-  // S_C = gamma_last S0 + sum_s (c_s k^_s) w_s^T, s ascending
+  // w: thread (column j, row group tq) makes rows 8 tq .. 8 tq + 8 of column j
+  {
+    const int j = T.tid & (kCB - 1), tq = T.tid / kCB;
+    static_assert(C / 8 * kCB == 256 || C == 32, "w layout");
+    if (tq < C / 8) {
+      float acc[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+#pragma unroll 4
+      for (int s2 = 0; s2 < C; ++s2) {
+        const float r = L.u.st.R[s2][j];
+        const float4 m0 = *reinterpret_cast<const float4*>(&L.MT[s2][8 * tq]);
+        const float4 m1 = *reinterpret_cast<const float4*>(&L.MT[s2][8 * tq + 4]);
+        acc[0] = __builtin_fmaf(m0.x, r, acc[0]);
+        acc[1] = __builtin_fmaf(m0.y, r, acc[1]);
+        acc[2] = __builtin_fmaf(m0.z, r, acc[2]);
+        acc[3] = __builtin_fmaf(m0.w, r, acc[3]);
+        acc[4] = __builtin_fmaf(m1.x, r, acc[4]);
+        acc[5] = __builtin_fmaf(m1.y, r, acc[5]);
+        acc[6] = __builtin_fmaf(m1.z, r, acc[6]);
+        acc[7] = __builtin_fmaf(m1.w, r, acc[7]);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) L.u.st.W[8 * tq + q][j] = acc[q];
+    }
+  }
+  __syncthreads();
   const float gl = L.gamma[C - 1];
 #pragma unroll
   for (int ii = 0; ii < 8; ++ii)
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) S[ii][jj] = gl * S[ii][jj];
+#pragma unroll 4
   for (int s = 0; s < C; ++s) {
     float kc[8];
+    const float c_s = L.cf[s];
 #pragma unroll
-    for (int ii = 0; ii < 8; ++ii) kc[ii] = L.K[s][8 * T.ti + ii];
-    const float2 w2 = *reinterpret_cast<const float2*>(&L.PW[s][2 * T.tc]);
+    for (int ii = 0; ii < 8; ++ii) kc[ii] = c_s * L.K[s][8 * T.ti + ii];  // cf_s k^_s
+    const float2 w2 = *reinterpret_cast<const float2*>(&L.u.st.W[s][2 * T.tc]);
 #pragma unroll
     for (int ii = 0; ii < 8; ++ii) {
       S[ii][0] = __builtin_fmaf(kc[ii], w2.x, S[ii][0]);
@@ -338,6 +392,7 @@ struct CacheView {
   float* vbuf;  // [C][H][128]
   float* abuf;  // [C][H]
   float* bbuf;  // [C][H]
+  float* coef;  // [H][C*C + 2C] the closing chunk's M^T, gamma, ratios (decode scratch)
 };
 __device__ __forceinline__ CacheView cache_view(void* base, int64_t seq, int H, int C) {
   const int64_t per = gdn_cache_floats(H, C);
@@ -349,6 +404,7 @@ __device__ __forceinline__ CacheView cache_view(void* base, int64_t seq, int H, 
   v.vbuf = v.kbuf + (int64_t)C * H * kD;
   v.abuf = v.vbuf + (int64_t)C * H * kD;
   v.bbuf = v.abuf + (int64_t)C * H;
+  v.coef = v.bbuf + (int64_t)C * H;
   return v;
 }
 
@@ -380,8 +436,44 @@ __device__ __forceinline__ int64_t cu_at(const GdnArgs& a, int s) {
 // well-formed table and stay below T/C + S for any table.
 __device__ __forceinline__ int64_t boundary_base(const GdnArgs& a, int s, int C) { return cu_at(a, s) / C + s; }
 
-// First pass: one workgroup per (sequence, head, column block), the chunks in
-// order.
+// Coefficients of every full chunk, independent of the state, all chunks in
+// parallel: one workgroup per (chunk slot, head). Slot c of sequence s is
+// chunk j = c - boundary_base(s).
+template <int C>
+__global__ __launch_bounds__(256, 2) void gdn_coef_kernel(GdnArgs a) {
+  __shared__ ChunkLds<C> L;
+  const Tc T = col_layout();
+  const int64_t c = blockIdx.x;
+  const int h = blockIdx.y;
+  int lo = 0, hi = a.S - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (boundary_base(a, mid, C) <= c) lo = mid;
+    else hi = mid - 1;
+  }
+  const int s = lo;
+  const int64_t t0 = cu_at(a, s), len = max(cu_at(a, s + 1) - t0, (int64_t)0);
+  const int64_t j = c - boundary_base(a, s, C);
+  if (j < 0 || (j + 1) * C > len) return;  // not a full chunk (uniform)
+  const int64_t tc0 = t0 + j * C;
+  fill_chunk<C>(
+      L, T, [&](int t, int i) { return a.kh[((tc0 + t) * a.H + h) * kD + i]; }, [&](int, int) { return 0.0f; },
+      [&](int t, float& al, float& be) {
+        al = a.alpha[(tc0 + t) * a.H + h];
+        be = a.beta[(tc0 + t) * a.H + h];
+      });
+  chunk_coeffs<C>(L, T);
+  float* dst = a.coef + (c * a.H + h) * (int64_t)(C * C + 2 * C);
+  for (int e = T.tid; e < C * C; e += 256) dst[e] = L.MT[e / C][e % C];
+  if (T.tid < C) {
+    dst[C * C + T.tid] = L.gamma[T.tid];
+    dst[C * C + C + T.tid] = L.cf[T.tid];
+  }
+}
+
+// First pass, the state-dependent part: one workgroup per (sequence, head,
+// column block), the chunks in order, each chunk's coefficients read from
+// the coefficient pass.
 template <int C>
 __global__ __launch_bounds__(256, 2) void gdn_boundary_kernel(GdnArgs a) {
   __shared__ ChunkLds<C> L;
@@ -397,14 +489,48 @@ __global__ __launch_bounds__(256, 2) void gdn_boundary_kernel(GdnArgs a) {
   store_block(S, a.bstates + (base * a.H + h) * plane, cb, T);
   for (int64_t j = 0; j < n; ++j) {
     const int64_t tc0 = t0 + j * C;
-    fill_chunk<C>(
-        L, T, [&](int t, int i) { return a.kh[((tc0 + t) * a.H + h) * kD + i]; },
-        [&](int t, int c) { return bf16_bits_to_f32(a.v[((tc0 + t) * a.H + h) * kD + kCB * cb + c]); },
-        [&](int t, float& al, float& be) {
-          al = a.alpha[(tc0 + t) * a.H + h];
-          be = a.beta[(tc0 + t) * a.H + h];
-        });
-    chunk_update<C>(S, L, T);
+    const float* cf = a.coef + ((base + j) * a.H + h) * (int64_t)(C * C + 2 * C);
+    // every load issued before the first LDS write
+    constexpr int PK = C * kD / 256, PV = C * kCB / 256, PM = C * C / 256;
+    float kr[PK], vr[PV], mr[PM];
+#pragma unroll
+    for (int u = 0; u < PK; ++u) {
+      const int e = T.tid + 256 * u;
+      kr[u] = a.kh[((tc0 + e / kD) * a.H + h) * kD + e % kD];
+    }
+#pragma unroll
+    for (int u = 0; u < PV; ++u) {
+      const int e = T.tid + 256 * u;
+      vr[u] = bf16_bits_to_f32(a.v[((tc0 + e / kCB) * a.H + h) * kD + kCB * cb + e % kCB]);
+    }
+#pragma unroll
+    for (int u = 0; u < PM; ++u) mr[u] = cf[T.tid + 256 * u];
+    float gm = 0.0f, cfv = 0.0f;
+    if (T.tid < C) {
+      gm = cf[C * C + T.tid];
+      cfv = cf[C * C + C + T.tid];
+    }
+#pragma unroll
+    for (int u = 0; u < PK; ++u) {
+      const int e = T.tid + 256 * u;
+      L.K[e / kD][e % kD] = kr[u];
+    }
+#pragma unroll
+    for (int u = 0; u < PV; ++u) {
+      const int e = T.tid + 256 * u;
+      L.V[e / kCB][e % kCB] = vr[u];
+    }
+#pragma unroll
+    for (int u = 0; u < PM; ++u) {
+      const int e = T.tid + 256 * u;
+      L.MT[e / C][e % C] = mr[u];
+    }
+    if (T.tid < C) {
+      L.gamma[T.tid] = gm;
+      L.cf[T.tid] = cfv;
+    }
+    __syncthreads();
+    chunk_state<C>(S, L, T);
     store_block(S, a.bstates + ((base + j + 1) * a.H + h) * plane, cb, T);
   }
   if (a.cache) {
@@ -559,9 +685,34 @@ __global__ __launch_bounds__(256) void gdn_decode_step_kernel(GdnDecodeArgs a) {
   }
 }
 
-// Decode, part 2: where the token closed a chunk, the boundary state is
-// advanced by the same chunk update as the first pass (one workgroup per
-// column block), and the running state resynchronises to it.
+// Decode, part 2: where the token closed a chunk, the chunk's coefficients
+// (one workgroup per (sequence, head)) ...
+template <int C>
+__global__ __launch_bounds__(256, 2) void gdn_decode_coef_kernel(GdnDecodeArgs a) {
+  __shared__ ChunkLds<C> L;
+  const Tc T = col_layout();
+  const int bseq = blockIdx.x, h = blockIdx.y;
+  const int64_t pos = a.pos[bseq];
+  if (pos < 0 || (pos + 1) % C != 0) return;  // uniform
+  const CacheView cv = cache_view(a.cache, bseq, a.H, C);
+  fill_chunk<C>(
+      L, T, [&](int t, int i) { return cv.kbuf[((int64_t)t * a.H + h) * kD + i]; }, [&](int, int) { return 0.0f; },
+      [&](int t, float& al, float& be) {
+        al = cv.abuf[(int64_t)t * a.H + h];
+        be = cv.bbuf[(int64_t)t * a.H + h];
+      });
+  chunk_coeffs<C>(L, T);
+  float* dst = cv.coef + (int64_t)h * (C * C + 2 * C);
+  for (int e = T.tid; e < C * C; e += 256) dst[e] = L.MT[e / C][e % C];
+  if (T.tid < C) {
+    dst[C * C + T.tid] = L.gamma[T.tid];
+    dst[C * C + C + T.tid] = L.cf[T.tid];
+  }
+}
+
+// ... then the boundary state advanced by the same chunk_state as the first
+// pass (one workgroup per column block), and the running state resynchronised
+// to it.
 template <int C>
 __global__ __launch_bounds__(256, 2) void gdn_decode_resync_kernel(GdnDecodeArgs a) {
   __shared__ ChunkLds<C> L;
@@ -570,17 +721,50 @@ __global__ __launch_bounds__(256, 2) void gdn_decode_resync_kernel(GdnDecodeArgs
   const int64_t pos = a.pos[bseq];
   if (pos < 0 || (pos + 1) % C != 0) return;  // uniform
   const CacheView cv = cache_view(a.cache, bseq, a.H, C);
-  fill_chunk<C>(
-      L, T, [&](int t, int i) { return cv.kbuf[((int64_t)t * a.H + h) * kD + i]; },
-      [&](int t, int c) { return cv.vbuf[((int64_t)t * a.H + h) * kD + kCB * cb + c]; },
-      [&](int t, float& al, float& be) {
-        al = cv.abuf[(int64_t)t * a.H + h];
-        be = cv.bbuf[(int64_t)t * a.H + h];
-      });
+  const float* cf = cv.coef + (int64_t)h * (C * C + 2 * C);
+  constexpr int PK = C * kD / 256, PV = C * kCB / 256, PM = C * C / 256;
+  float kr[PK], vr[PV], mr[PM];
+#pragma unroll
+  for (int u = 0; u < PK; ++u) {
+    const int e = T.tid + 256 * u;
+    kr[u] = cv.kbuf[((int64_t)(e / kD) * a.H + h) * kD + e % kD];
+  }
+#pragma unroll
+  for (int u = 0; u < PV; ++u) {
+    const int e = T.tid + 256 * u;
+    vr[u] = cv.vbuf[((int64_t)(e / kCB) * a.H + h) * kD + kCB * cb + e % kCB];
+  }
+#pragma unroll
+  for (int u = 0; u < PM; ++u) mr[u] = cf[T.tid + 256 * u];
+  float gm = 0.0f, cfv = 0.0f;
+  if (T.tid < C) {
+    gm = cf[C * C + T.tid];
+    cfv = cf[C * C + C + T.tid];
+  }
+#pragma unroll
+  for (int u = 0; u < PK; ++u) {
+    const int e = T.tid + 256 * u;
+    L.K[e / kD][e % kD] = kr[u];
+  }
+#pragma unroll
+  for (int u = 0; u < PV; ++u) {
+    const int e = T.tid + 256 * u;
+    L.V[e / kCB][e % kCB] = vr[u];
+  }
+#pragma unroll
+  for (int u = 0; u < PM; ++u) {
+    const int e = T.tid + 256 * u;
+    L.MT[e / C][e % C] = mr[u];
+  }
+  if (T.tid < C) {
+    L.gamma[T.tid] = gm;
+    L.cf[T.tid] = cfv;
+  }
+  __syncthreads();
   const int64_t plane = (int64_t)kD * kD;
   float S[8][2];
   load_block(S, cv.sb + h * plane, cb, T);
-  chunk_update<C>(S, L, T);
+  chunk_state<C>(S, L, T);
   store_block(S, cv.sb + h * plane, cb, T);
   store_block(S, cv.srun + h * plane, cb, T);
 }
@@ -598,11 +782,13 @@ hipError_t launch_gdn_prefill(const GdnArgs& a, int C, bool out_bf16, hipStream_
   const dim3 go((unsigned)(a.T / C + a.S), (unsigned)a.H);
   switch (C) {
     case 32:
+      hipLaunchKernelGGL(gdn_coef_kernel<32>, go, dim3(256), 0, s, a);
       hipLaunchKernelGGL(gdn_boundary_kernel<32>, gb, dim3(256), 0, s, a);
       if (out_bf16) hipLaunchKernelGGL((gdn_output_kernel<32, true>), go, dim3(256), 0, s, a);
       else hipLaunchKernelGGL((gdn_output_kernel<32, false>), go, dim3(256), 0, s, a);
       break;
     case 64:
+      hipLaunchKernelGGL(gdn_coef_kernel<64>, go, dim3(256), 0, s, a);
       hipLaunchKernelGGL(gdn_boundary_kernel<64>, gb, dim3(256), 0, s, a);
       if (out_bf16) hipLaunchKernelGGL((gdn_output_kernel<64, true>), go, dim3(256), 0, s, a);
       else hipLaunchKernelGGL((gdn_output_kernel<64, false>), go, dim3(256), 0, s, a);
@@ -620,11 +806,13 @@ hipError_t launch_gdn_decode(const GdnDecodeArgs& a, int C, bool out_bf16, hipSt
     case 32:
       if (out_bf16) hipLaunchKernelGGL((gdn_decode_step_kernel<32, true>), grid, dim3(256), 0, s, a);
       else hipLaunchKernelGGL((gdn_decode_step_kernel<32, false>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL(gdn_decode_coef_kernel<32>, grid, dim3(256), 0, s, a);
       hipLaunchKernelGGL(gdn_decode_resync_kernel<32>, grid_r, dim3(256), 0, s, a);
       break;
     case 64:
       if (out_bf16) hipLaunchKernelGGL((gdn_decode_step_kernel<64, true>), grid, dim3(256), 0, s, a);
       else hipLaunchKernelGGL((gdn_decode_step_kernel<64, false>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL(gdn_decode_coef_kernel<64>, grid, dim3(256), 0, s, a);
       hipLaunchKernelGGL(gdn_decode_resync_kernel<64>, grid_r, dim3(256), 0, s, a);
       break;
     default:

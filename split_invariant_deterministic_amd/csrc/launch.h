@@ -86,9 +86,10 @@ hipError_t launch_attn_combine(const float* ws, void* out, int64_t Tq, int Hq, i
 // ---- Gated DeltaNet (CPR) ---------------------------------------------------
 // Floats of one sequence's decode cache: running state and last boundary
 // state [H][128][128] each, then the open chunk's k^, v [C][H][128] and
-// alpha, beta [C][H].
+// alpha, beta [C][H], then per head the closing chunk's coefficients
+// [H][C*C + 2C] (scratch of the chunk-closing decode step).
 __host__ __device__ inline int64_t gdn_cache_floats(int H, int C) {
-  return 2LL * H * 128 * 128 + (int64_t)C * H * (2 * 128 + 2);
+  return 2LL * H * 128 * 128 + (int64_t)C * H * (2 * 128 + 2) + (int64_t)H * (C * C + 2 * C);
 }
 struct GdnArgs {
   const uint16_t* q;      // [T, H, 128] bf16
@@ -106,6 +107,7 @@ struct GdnArgs {
   float* kh;              // [T, H, 128]
   float* alpha;           // [T, H]
   float* bstates;         // [T/C + S, H, 128, 128] boundary states
+  float* coef;            // [T/C + S, H, C*C + 2C] per-chunk M^T, gamma, gamma_last/gamma
 };
 struct GdnDecodeArgs {
   const uint16_t* q;      // [B, H, 128] bf16

@@ -93,8 +93,9 @@ def test_workspace_sizes():
     cg = inv.contract(kv_chunk=64)
     T, H, S = 10240, 16, 5
     assert inv.workspace_bytes(cg, inv.OP_GDN_PREFILL, T, H, S) == \
-        (2 * T * H * 128 + T * H + (T // 64 + S) * H * 128 * 128) * 4 + 16
-    assert inv._lib.inv_gdn_cache_bytes(ctypes.byref(cg), 16) == (2 * 16 * 128 * 128 + 64 * 16 * 258) * 4
+        (2 * T * H * 128 + T * H + (T // 64 + S) * H * (128 * 128 + 64 * 64 + 128)) * 4 + 16
+    assert inv._lib.inv_gdn_cache_bytes(ctypes.byref(cg), 16) == \
+        (2 * 16 * 128 * 128 + 64 * 16 * 258 + 16 * (64 * 64 + 128)) * 4
 
 
 def test_entry_points_reject_before_any_launch():
