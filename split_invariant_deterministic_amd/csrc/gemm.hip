@@ -15,11 +15,11 @@
 // kernels are free to choose tiles by M; padding rows never reach C.
 //
 // Kernels
-//   gemm_ring_kernel    large M: 128 x 128 tile per workgroup, operands
-//                       through a deep LDS ring filled by direct global->LDS
-//                       loads; the balanced subtree of up to 8 leaves is
-//                       evaluated in registers in post-order (log2(nl)+1
-//                       live accumulator sets).
+//   gemm_ring_kernel    large M: 128 x 128 tile per workgroup of 8 waves,
+//                       operands through a deep LDS ring filled by direct
+//                       global->LDS loads; the balanced subtree of up to 8
+//                       leaves is evaluated in post-order (log2(nl)+1 live
+//                       accumulator sets, the last in LDS for 8 leaves).
 //   gemm_stream_kernel  small M (<= 64): each wave owns whole leaves of one
 //                       16FM x 16 tile and streams its K range straight from
 //                       HBM into MFMA fragments; the waves' subtrees are then
@@ -95,14 +95,15 @@ constexpr int kOutF32 = 0, kOutBF16 = 1, kOutLP = 2;
 // columns; the lane then reduces each 16-column vocabulary block in
 // registers (block16_stats) and writes its (m, s), and the target's logit if
 // the row's target falls in these columns. t: this wave's LDS scratch of
-// rows x kLpStride floats; the row stride of 68 floats keeps both the
-// transposing writes and the 16-byte row reads free of bank conflicts.
+// rows x STRIDE floats; a row stride of 68 floats (64 columns) or 36 (32
+// columns) keeps both the transposing writes and the 16-byte row reads free
+// of bank conflicts: 4 * STRIDE / 4 steps through all 16 four-bank groups.
 constexpr int kLpStride = 68;
 
-template <int NB>  // 16-column blocks per row held by the wave
+template <int NB, int STRIDE = kLpStride>  // 16-column blocks per row held by the wave; row stride
 __device__ __forceinline__ void lp_rows_epilogue(const TileParams& p, const float* t, int64_t row, bool row_ok,
                                                  int64_t col0, int lane) {
-  const float* mine = t + lane * kLpStride;
+  const float* mine = t + lane * STRIDE;
   const int64_t nb = (p.N + 15) / 16;
   const int32_t tgt = row_ok ? p.lp_target[row] : -1;
 #pragma unroll
@@ -131,10 +132,12 @@ __device__ __forceinline__ void lp_rows_epilogue(const TileParams& p, const floa
 
 // ---------------------------------------------------------------- ring kernel
 //
-// Large-M kernel. A workgroup of 4 waves owns a 128 x 128 output tile, each
-// wave 64 x 64 (4 x 4 MFMA blocks). Operands stream through a 128 KB LDS ring
-// of NS stages of BK k (BK = 64: 4 stages; BK = 32 for leaves that are an odd
-// multiple of 32: 8 stages), filled by global_load_lds_dwordx4: each wave-wide
+// Large-M kernel. A workgroup of 8 waves owns a 128 x 128 output tile, each
+// wave 64 x 32 (4 x 2 MFMA blocks); at most 256 registers a wave, so a CU
+// runs two waves per SIMD and one wave's barrier and LDS waits overlap the
+// other's MFMAs. Operands stream through an LDS ring (128 KB; 96 KB for 8
+// leaves) of NS stages of BK k (BK = 64; BK = 32 for leaves that are an odd
+// multiple of 32), filled by global_load_lds_dwordx4: each wave-wide
 // load writes 64 x 16 bytes contiguously at its LDS base, so a stage is laid
 // out as rows of BK bf16 with no padding, and the 16-byte chunk c of row r is
 // stored at slot c ^ ((r / RPW) % CPR). With that XOR swizzle the 16 lanes
@@ -147,16 +150,21 @@ __device__ __forceinline__ void lp_rows_epilogue(const TileParams& p, const floa
 // row m of an MFMA result depends only on row m of A (and column n only on
 // row n of B), so those rows never touch a stored output.
 
+// Waves per ring workgroup: 8 waves, each 64 rows x 32 columns of the
+// 128 x 128 tile (4 x 2 MFMA blocks of 16 x 16).
+constexpr int kRingWaves = 8;
+
 template <int BK, int RING = 131072>
 struct Ring {
+  static constexpr int NW = kRingWaves;
   static constexpr int BM = 128, BN = 128;
   static constexpr int ROWB = BK * 2;          // bytes per staged row
   static constexpr int CPR = BK / 8;           // 16-byte chunks per row
   static constexpr int RPW = 16 / CPR;         // rows per 256-byte bank window
   static constexpr int RPL = 1024 / ROWB;      // rows per wave-wide 1 KB load
   static constexpr int ABYTES = BM * ROWB, BBYTES = BN * ROWB, STAGE = ABYTES + BBYTES;
-  static constexpr int LA = ABYTES / 4096;     // 1 KB loads per wave per stage (4 waves)
-  static constexpr int LB = BBYTES / 4096;
+  static constexpr int LA = ABYTES / (1024 * NW);  // 1 KB loads per wave per stage
+  static constexpr int LB = BBYTES / (1024 * NW);
   static constexpr int LOADS = LA + LB;
   static constexpr int NS = RING / STAGE;      // stages in the ring
   static __device__ __forceinline__ int slot(int r, int c) { return c ^ ((r / RPW) % CPR); }
@@ -182,7 +190,10 @@ __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "
 template <int BK, int RING>
 struct RingCtx {
   using R = Ring<BK, RING>;
-  using Acc = AccT<4, 4>;
+  static constexpr int NW = R::NW;
+  static constexpr int WN = 128 / (NW / 2);  // wave tile: 64 rows x WN columns
+  static constexpr int FN = WN / 16;
+  using Acc = AccT<4, FN>;
   static constexpr int USED = R::NS * R::STAGE;  // ring bytes in use
   uint8_t* lds;
   // DMA sources: wave-uniform bases advanced along K, plus per-lane byte
@@ -216,10 +227,10 @@ struct RingCtx {
 #if defined(__HIP_DEVICE_COMPILE__)
     uint8_t* dst = lds + iss_off;
     if (u < R::LA)
-      __builtin_amdgcn_global_load_lds(abase + iss_k * 2 + aoff[u], &dst[(wave + 4 * u) * 1024], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(abase + iss_k * 2 + aoff[u], &dst[(wave + NW * u) * 1024], 16, 0, 0);
     else
       __builtin_amdgcn_global_load_lds(bbase + iss_k * 2 + boff[u - R::LA],
-                                       &dst[R::ABYTES + (wave + 4 * (u - R::LA)) * 1024], 16, 0, 0);
+                                       &dst[R::ABYTES + (wave + NW * (u - R::LA)) * 1024], 16, 0, 0);
 #endif
   }
   __device__ __forceinline__ void issue_done() {
@@ -235,10 +246,10 @@ struct RingCtx {
     uint8_t* dst = lds + iss_off;
 #pragma unroll
     for (int u = 0; u < R::LA; ++u)
-      __builtin_amdgcn_global_load_lds(a + aoff[u], &dst[(wave + 4 * u) * 1024], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(a + aoff[u], &dst[(wave + NW * u) * 1024], 16, 0, 0);
 #pragma unroll
     for (int u = 0; u < R::LB; ++u)
-      __builtin_amdgcn_global_load_lds(b + boff[u], &dst[R::ABYTES + (wave + 4 * u) * 1024], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(b + boff[u], &dst[R::ABYTES + (wave + NW * u) * 1024], 16, 0, 0);
 #endif
     iss_k += BK;
     iss_off += R::STAGE;
@@ -249,35 +260,35 @@ struct RingCtx {
     off += R::STAGE;
     return off == USED ? 0 : off;
   }
-  __device__ __forceinline__ void read_frags(int slot, int ks, bf16x8 (&fa)[4], bf16x8 (&fb)[4]) {
+  __device__ __forceinline__ void read_frags(int slot, int ks, bf16x8 (&fa)[4], bf16x8 (&fb)[FN]) {
     const uint8_t* pa = lds + slot + rd_a[ks];
     const uint8_t* pb = lds + slot + rd_b[ks];
 #pragma unroll
     for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(pa + 16 * i * R::ROWB);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) fb[j] = *reinterpret_cast<const bf16x8*>(pb + 16 * j * R::ROWB);
+    for (int j = 0; j < FN; ++j) fb[j] = *reinterpret_cast<const bf16x8*>(pb + 16 * j * R::ROWB);
   }
-  static __device__ __forceinline__ void mma(const bf16x8 (&fa)[4], const bf16x8 (&fb)[4], Acc& acc) {
+  static __device__ __forceinline__ void mma(const bf16x8 (&fa)[4], const bf16x8 (&fb)[FN], Acc& acc) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc.v[i][j] = mfma16(fa[i], fb[j], acc.v[i][j]);
+      for (int j = 0; j < FN; ++j) acc.v[i][j] = mfma16(fa[i], fb[j], acc.v[i][j]);
   }
   // The first MFMA of a leaf: C is the +0 literal rather than a zeroed
   // register set, so no zero set enters the accumulator's loop phi (which
   // made the register allocator rotate accumulators every iteration).
-  static __device__ __forceinline__ void mma_first(const bf16x8 (&fa)[4], const bf16x8 (&fb)[4], Acc& acc) {
+  static __device__ __forceinline__ void mma_first(const bf16x8 (&fa)[4], const bf16x8 (&fb)[FN], Acc& acc) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc.v[i][j] = mfma16(fa[i], fb[j], f32x4{0.f, 0.f, 0.f, 0.f});
+      for (int j = 0; j < FN; ++j) acc.v[i][j] = mfma16(fa[i], fb[j], f32x4{0.f, 0.f, 0.f, 0.f});
   }
 
   // BK = 64 keeps the next k-substep's operand fragments in flight while the
   // current substep's 16 MFMAs run: the ks = 0 fragments of a stage are read
   // right after the barrier that publishes it, in the middle of the previous
   // stage, so NS stages are in flight and no LDS read latency is exposed.
-  bf16x8 fa0[4], fb0[4];
+  bf16x8 fa0[4], fb0[FN];
 
   __device__ __forceinline__ void prologue() {
     if constexpr (BK == 64) {
@@ -296,7 +307,7 @@ struct RingCtx {
   // the middle, publish stage g+1 and prefetch its ks = 0 fragments.
   template <bool FIRST>
   __device__ __forceinline__ void stage64(Acc& acc) {
-    bf16x8 fa1[4], fb1[4];
+    bf16x8 fa1[4], fb1[FN];
     read_frags(rd_off, 1, fa1, fb1);
     if constexpr (FIRST) mma_first(fa0, fb0, acc);
     else mma(fa0, fb0, acc);
@@ -312,16 +323,16 @@ struct RingCtx {
     // MFMAs of substep 1 with the loads of stage g+NS (into stage g's slot)
     // spread between them
     const bool more = issued < total;
-    static_assert(R::LOADS == 8, "interleave assumes 8 loads per stage");
+    constexpr int LPI = R::LOADS / 4;  // loads per operand row block
+    static_assert(LPI * 4 == R::LOADS && FN % LPI == 0, "interleave");
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (more) issue_one(2 * i);
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc.v[i][j] = mfma16(fa1[i], fb1[j], acc.v[i][j]);
-      if (more) issue_one(2 * i + 1);
+      for (int h = 0; h < LPI; ++h) {
+        if (more) issue_one(LPI * i + h);
 #pragma unroll
-      for (int j = 2; j < 4; ++j) acc.v[i][j] = mfma16(fa1[i], fb1[j], acc.v[i][j]);
-    }
+        for (int j = h * FN / LPI; j < (h + 1) * FN / LPI; ++j) acc.v[i][j] = mfma16(fa1[i], fb1[j], acc.v[i][j]);
+      }
     if (more) issue_done();
     ++g;
   }
@@ -332,7 +343,7 @@ struct RingCtx {
     wait_vm_rem<R::LOADS, R::NS - 2>(total - 1 - g);
     block_barrier();  // every wave's stage g is in LDS; stage g-1 reads are done
     if (issued < total) issue_next();  // stage g+NS-1, into stage g-1's slot
-    bf16x8 fa[4], fb[4];
+    bf16x8 fa[4], fb[FN];
     read_frags(rd_off, 0, fa, fb);
     rd_off = next_slot(rd_off);
     if constexpr (FIRST) mma_first(fa, fb, acc);
@@ -355,21 +366,25 @@ struct RingCtx {
   }
 };
 
-// With 8 leaves the post-order tree needs four live 64 x 64 accumulator sets
-// per wave, more than the register file holds next to the operands; the
-// finished left half (leaves 0-3) then waits in LDS (64 KB, each lane its
-// own values) while the right half runs in registers, and the ring shrinks
-// to 96 KB. The arithmetic is the same tree.
+// With 8 leaves the post-order tree needs four live 64 x 32 accumulator sets
+// per wave, more than 256 registers hold next to double-buffered operands;
+// the finished left half (leaves 0-3) then waits in LDS (64 KB for the 8
+// waves, each lane its own values) while the right half runs in registers,
+// and the ring shrinks to 96 KB. The arithmetic is the same tree.
 template <int NL>
 constexpr int ring_bytes() { return NL == 8 ? 98304 : 131072; }
 
 template <int NL, int BK, int OUTM, bool GROUPED>
-__global__ __launch_bounds__(256, 1) void gemm_ring_kernel(TileParams p) {
+__global__ __launch_bounds__(64 * kRingWaves, 1) void gemm_ring_kernel(TileParams p) {
   constexpr int RING = ring_bytes<NL>();
   constexpr int SPILL = NL == 8 ? 65536 : 0;
   using R = Ring<BK, RING>;
   using Ctx = RingCtx<BK, RING>;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[R::NS * R::STAGE + SPILL];
+  constexpr int NW = Ctx::NW, WN = Ctx::WN, FN = Ctx::FN;
+  constexpr int LPS = WN + 4;  // row stride of the transposed tile (floats)
+  constexpr int LP_BYTES = OUTM == kOutLP ? NW * 64 * LPS * 4 : 0;
+  constexpr int LDS_BYTES = R::NS * R::STAGE + SPILL > LP_BYTES ? R::NS * R::STAGE + SPILL : LP_BYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -449,12 +464,13 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(TileParams p) {
   c.spl = p.kl / BK;
   c.total = c.spl * NL;
   c.g = 0;
+  const int wm = c.wave / (NW / 2), wn = c.wave % (NW / 2);  // wave tile (row, column) in the tile
   {
-    const int wm = c.wave >> 1, wn = c.wave & 1, g4 = lane >> 4, r16 = lane & 15;
+    const int g4 = lane >> 4, r16 = lane & 15;
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {
       c.rd_a[ks] = R::off(wm * 64 + r16, 4 * ks + g4);
-      c.rd_b[ks] = R::ABYTES + R::off(wn * 64 + r16, 4 * ks + g4);
+      c.rd_b[ks] = R::ABYTES + R::off(wn * WN + r16, 4 * ks + g4);
     }
   }
   // A rows: contiguous from m0, or gathered (offsets then from A itself)
@@ -463,7 +479,7 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(TileParams p) {
   c.bbase = reinterpret_cast<const uint8_t*>(B + n0 * p.K);
 #pragma unroll
   for (int u = 0; u < R::LA; ++u) {
-    const int r = (c.wave + 4 * u) * R::RPL + lane / R::CPR;
+    const int r = (c.wave + NW * u) * R::RPL + lane / R::CPR;
     const int chunk = R::slot(r, lane % R::CPR);  // the slot map is its own inverse
     int64_t row = min(m0 + r, m_end - 1);
     int64_t rel = row - m0;
@@ -477,7 +493,7 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(TileParams p) {
   }
 #pragma unroll
   for (int u = 0; u < R::LB; ++u) {
-    const int r = (c.wave + 4 * u) * R::RPL + lane / R::CPR;
+    const int r = (c.wave + NW * u) * R::RPL + lane / R::CPR;
     const int chunk = R::slot(r, lane % R::CPR);
     const int64_t col = min(n0 + r, p.N - 1);
     c.boff[u] = (uint32_t)(((col - n0) * p.K + chunk * 8) * 2);
@@ -485,42 +501,41 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(TileParams p) {
   c.prologue();
 
   typename Ctx::Acc acc;
-  if constexpr (NL == 8) {
-    float* spill = reinterpret_cast<float*>(&lds[R::NS * R::STAGE]) + wave * 64 * 64 + lane;
+  if constexpr (SPILL > 0) {
+    float* spill = reinterpret_cast<float*>(&lds[R::NS * R::STAGE]) + wave * 64 * WN + lane;
     run_tree<4>(c, acc);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) spill[((i * 4 + j) * 4 + r) * 64] = acc.v[i][j][r];
+        for (int r = 0; r < 4; ++r) spill[((i * FN + j) * 4 + r) * 64] = acc.v[i][j][r];
     run_tree<4>(c, acc);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc.v[i][j][r] = spill[((i * 4 + j) * 4 + r) * 64] + acc.v[i][j][r];
+        for (int r = 0; r < 4; ++r) acc.v[i][j][r] = spill[((i * FN + j) * 4 + r) * 64] + acc.v[i][j][r];
   } else {
     run_tree<NL>(c, acc);
   }
 
   // Epilogue: lane holds rows 4*(lane/16)+r of each 16x16 block, column lane%16.
-  const int64_t rbase = m0 + (c.wave >> 1) * 64 + 4 * (lane >> 4);
-  const int64_t cbase = n0 + (c.wave & 1) * 64 + (lane & 15);
+  const int64_t rbase = m0 + wm * 64 + 4 * (lane >> 4);
+  const int64_t cbase = n0 + wn * WN + (lane & 15);
   if constexpr (OUTM == kOutLP) {
-    static_assert(4 * 64 * kLpStride * 4 <= RING, "the transposed tile reuses the ring");
     block_barrier();  // every wave has consumed its last ring stage
-    float* t = reinterpret_cast<float*>(lds) + wave * 64 * kLpStride;
+    float* t = reinterpret_cast<float*>(lds) + wave * 64 * LPS;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) t[(16 * i + 4 * (lane >> 4) + r) * kLpStride + 16 * j + (lane & 15)] = acc.v[i][j][r];
+        for (int r = 0; r < 4; ++r) t[(16 * i + 4 * (lane >> 4) + r) * LPS + 16 * j + (lane & 15)] = acc.v[i][j][r];
     // the wave reads back only what it wrote; its LDS accesses complete in order
-    const int64_t row = m0 + (c.wave >> 1) * 64 + lane;
-    lp_rows_epilogue<4>(p, t, row, row < m_end, n0 + (c.wave & 1) * 64, lane);
+    const int64_t row = m0 + wm * 64 + lane;
+    lp_rows_epilogue<FN, LPS>(p, t, row, row < m_end, n0 + wn * WN, lane);
     return;
   }
 #pragma unroll
@@ -537,7 +552,7 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(TileParams p) {
         }
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < FN; ++j) {
         const int64_t col = cbase + 16 * j;
         if (col < p.N) {
           const int64_t off = (int64_t)z * p.c_group_stride + row * p.N + col;
@@ -747,7 +762,7 @@ __global__ __launch_bounds__(256) void cast_bf16_kernel(const float* __restrict_
 // ------------------------------------------------------------------ dispatch
 
 #define INV_RING_CASE(NL_, BK_)                                                                              \
-  hipLaunchKernelGGL((gemm_ring_kernel<NL_, BK_, OUTM, GROUPED>), grid, dim3(256), 0, s, p);                 \
+  hipLaunchKernelGGL((gemm_ring_kernel<NL_, BK_, OUTM, GROUPED>), grid, dim3(64 * kRingWaves), 0, s, p);     \
   break;
 
 template <int OUTM, bool GROUPED>
