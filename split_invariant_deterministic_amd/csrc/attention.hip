@@ -145,15 +145,14 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a, float scal
     bf16x8 kf[Cfg::KB][4];
 #pragma unroll
     for (int kb = 0; kb < Cfg::KB; ++kb) {
-      const int64_t pos = kbase + kb * 16 + c16;
-      const bool ok = pos < L;
-      const uint16_t* kp = K + (start + (ok ? pos : 0)) * kv_row + (int64_t)kvh * kD + 8 * g4;
+      // Keys past L read a clamped valid key: score row j of the MFMA below
+      // depends only on key row j, and those rows' scores are set to -inf.
+      // K and V are read once per (sequence, kv head, split): streaming loads.
+      const int64_t pos = min(kbase + kb * 16 + c16, L - 1);
+      const uint16_t* kp = K + (start + pos) * kv_row + (int64_t)kvh * kD + 8 * g4;
 #pragma unroll
-      for (int ds = 0; ds < 4; ++ds) {
-        u32x4 v = *reinterpret_cast<const u32x4*>(kp + ds * 32);
-        if (!ok) v = u32x4{0u, 0u, 0u, 0u};
-        kf[kb][ds] = __builtin_bit_cast(bf16x8, v);
-      }
+      for (int ds = 0; ds < 4; ++ds)
+        kf[kb][ds] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + ds * 32)));
     }
     // ---- V rows straight into LDS (keys past L load a clamped valid key:
     //      their p is exactly 0, and the key's values are finite cache data)
@@ -164,7 +163,7 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a, float scal
       const int slot = lane & 15;
       const int64_t pos = min(kbase + key, L - 1);
       const uint8_t* src = Vb + ((start + pos) * kv_row + (int64_t)kvh * kD) * 2 + vswz(key, slot) * 16;
-      __builtin_amdgcn_global_load_lds(src, &vs[i * 1024], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src, &vs[i * 1024], 16, 0, kNT);
     }
 #endif
     // ---- S^T = K Q^T: lane holds keys kb*16 + 4*g4 + r for head c16

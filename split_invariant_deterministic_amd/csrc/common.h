@@ -31,6 +31,10 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
 // format word 0x00020000: byte addressing, no stride or swizzle) in SGPRs, a
 // per-lane 32-bit offset in one VGPR and a wave-uniform offset in an SGPR.
 // Callers keep every access inside the described range.
+// Cache policy for data read once (buffer and direct-to-LDS loads): nt,
+// bit 1 of the gfx950 cache-policy field.
+constexpr int kNT = 2;
+
 typedef __amdgpu_buffer_rsrc_t buf_rsrc;
 __device__ __forceinline__ buf_rsrc make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
