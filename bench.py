@@ -401,7 +401,9 @@ def main():
     if "gdn" in stages:
         # CPR flops per (token, head): the recurrence step 7*128^2 (S^T k, the
         # rank-1 update with decay, S^T q) plus the chunk update amortised over
-        # C = 64 tokens, (4*128^2*C + 2*C*(C-1)*128) / C; fp32 vector ALU bound.
+        # C = 64 tokens, (4*128^2*C + 2*C*(C-1)*128) / C. fp32 throughout: the
+        # recurrence on vector FMAs, the chunk update on fp32 MFMA; both peak at
+        # 157.3 TFLOP/s on MI355X.
         fl_tok = 7 * 128 * 128 + (4 * 128 * 128 * 64 + 2 * 64 * 63 * 128) / 64
         add("gdn prefill 5x2048 tokens, 16 heads", "alu", fl_tok * 10240 * 16, ms["gdn_prefill"],
             PEAK_FP32_TFLOPS, "TFLOP/s")

@@ -21,15 +21,16 @@
 // M, gamma and the ratios do not depend on the state, so in a prefill they
 // are computed for every chunk in parallel; only r, w and S_C stay serial.
 //
-// Thread layout (256 threads): for the recurrence, thread (ti, tj),
-// ti = lane % 16, tj = 4 * wave + lane / 16, holds S[8ti .. 8ti+8)[8tj .. 8tj+8)
-// in registers; a chunk update splits the 128 value columns into 4 blocks of
-// 32, one workgroup each, thread (ti, tc) holding rows 8ti .. 8ti+8 of two
-// columns. Either way a reduction over the state rows (S^T x) is, per column,
-// a sequential fma chain over 8 rows, then a balanced tree over the 16 row
-// groups: the 16 lanes of a DPP row share the column, so that tree is an
-// in-register butterfly. Columns never mix, so the bits of a column do not
-// depend on which block or thread holds it.
+// Thread layouts. The recurrence (256 threads): thread (ti, tj), ti = lane %
+// 16, tj = 4 * wave + lane / 16, holds S[8ti .. 8ti+8)[8tj .. 8tj+8) in
+// registers; a reduction over the state rows (S^T x) is, per column, a
+// sequential fma chain over 8 rows, then a balanced tree over the 16 row
+// groups (the 16 lanes of a DPP row share the column: an in-register
+// butterfly). The chunk update: a wave owns 16 value columns of the state,
+// all 128 rows, as eight fp32 MFMA accumulators (16x16 blocks); the chunk's
+// three products (P = K^ S, w = M r, and the rank-C state update) are fp32
+// MFMA chains over those blocks. Columns never mix, so the bits of a column
+// do not depend on which wave or workgroup holds it.
 #include "common.h"
 #include "launch.h"
 
@@ -107,12 +108,8 @@ __device__ __forceinline__ void rec_step(float (&S)[8][8], const float (&k8)[8],
   }
 }
 
-// Chunk updates run on column blocks. Every value column of the state evolves
-// on its own (the recurrence mixes rows, never columns), so a workgroup of
-// 256 threads owns kCB = 32 columns: thread (ti, tc), ti = lane % 16,
-// tc = 4 * wave + lane / 16, holds rows 8ti .. 8ti+8 of columns 32 cb + 2 tc
-// and + 1. Each column's arithmetic is the same whichever block holds it.
-constexpr int kCB = 32;
+// The coefficient phase: a workgroup of 256 threads per chunk; the layout
+// below only numbers the threads.
 constexpr int kKStride = kD + 1;  // odd row stride: lanes reading different rows hit different banks
 
 struct Tc {
@@ -127,22 +124,16 @@ __device__ __forceinline__ Tc col_layout() {
   return t;
 }
 
-// LDS of one chunk update of one column block. K: k^ of the chunk's C tokens
-// (all 128 rows); V: the block's 32 columns of v (fp32); MT: M transposed
-// (MT[s][t] = M[t][s]); gates and their running products; A (coefficient
-// phase) shares space with R and W (state phase).
+// LDS of one chunk's coefficient phase. K: k^ of the chunk's C tokens (all
+// 128 rows); MT: M transposed (MT[s][t] = M[t][s]); gates and their running
+// products; A: the scaled Gram matrix.
 template <int C>
 struct alignas(16) ChunkLds {
   float K[C][kKStride];
   float MT[C][C];
-  float V[C][kCB];
   float alpha[C], beta[C], gamma[C], cf[C];
   union {
     float A[C][C];
-    struct {
-      float R[C][kCB];
-      float W[C][kCB];
-    } st;
   } u;
 };
 
@@ -241,94 +232,177 @@ __device__ void chunk_coeffs(ChunkLds<C>& L, const Tc& T) {
   __syncthreads();
 }
 
-// S (registers, the block of boundary state b_j on entry) becomes b_{j+1}:
-//   r_t = v_t - gamma_t P_t with P_t = S0^T k^_t (per column: the thread's 8
-//         rows as one fma chain, then the balanced tree over the 16 row groups)
-//   w_t = sum_s M[t][s] r_s  (s ascending over the whole chunk; M is +0 above
-//         the diagonal)
-//   S_C = gamma_last S0 + sum_s (cf_s k^_s) w_s^T  (s ascending)
-// Needs K, V, MT, gamma, cf.
+// State phase of a chunk update: a wave owns the 16 value columns c0 .. c0+15
+// of the state, all 128 rows, as 8 fp32 MFMA accumulators: lane l holds
+// S[16 ib + 4 (l / 16) + r][c0 + l % 16] in S[ib][r] (v_mfma_f32_16x16x4f32:
+// A[l % 16][l / 16], B[l / 16][l % 16], D[4 (l / 16) + r][l % 16]). With that
+// layout the state feeds the next product directly: k-step q of a 16-row
+// block takes register q as the B operand (rows 16 ib + 4 g + q for the four
+// lane groups g) and the matching A columns, so nothing is transposed.
+constexpr int kWC = 16;                      // state columns per wave
+constexpr int kStateWaves = 2;               // waves per state workgroup
+constexpr int kSB = kWC * kStateWaves;       // state columns per workgroup
+constexpr int kSKStride = kD + 4;            // K rows: 16-byte aligned, 16 rows cover the 64 banks
 template <int C>
-__device__ void chunk_state(float (&S)[8][2], ChunkLds<C>& L, const Tc& T) {
-#pragma unroll 4
-  for (int t = 0; t < C; ++t) {
-    float k8[8];
-#pragma unroll
-    for (int ii = 0; ii < 8; ++ii) k8[ii] = L.K[t][8 * T.ti + ii];
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      float u = 0.0f;
-#pragma unroll
-      for (int ii = 0; ii < 8; ++ii) u = __builtin_fmaf(S[ii][jj], k8[ii], u);
-      u = row16_sum(u);
-      if (T.ti == 0) L.u.st.R[t][2 * T.tc + jj] = L.V[t][2 * T.tc + jj] - L.gamma[t] * u;
-    }
-  }
-  __syncthreads();
-  // w: thread (column j, row group tq) makes rows 8 tq .. 8 tq + 8 of column j
-  {
-    const int j = T.tid & (kCB - 1), tq = T.tid / kCB;
-    static_assert(C / 8 * kCB == 256 || C == 32, "w layout");
-    if (tq < C / 8) {
-      float acc[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
-#pragma unroll 4
-      for (int s2 = 0; s2 < C; ++s2) {
-        const float r = L.u.st.R[s2][j];
-        const float4 m0 = *reinterpret_cast<const float4*>(&L.MT[s2][8 * tq]);
-        const float4 m1 = *reinterpret_cast<const float4*>(&L.MT[s2][8 * tq + 4]);
-        acc[0] = __builtin_fmaf(m0.x, r, acc[0]);
-        acc[1] = __builtin_fmaf(m0.y, r, acc[1]);
-        acc[2] = __builtin_fmaf(m0.z, r, acc[2]);
-        acc[3] = __builtin_fmaf(m0.w, r, acc[3]);
-        acc[4] = __builtin_fmaf(m1.x, r, acc[4]);
-        acc[5] = __builtin_fmaf(m1.y, r, acc[5]);
-        acc[6] = __builtin_fmaf(m1.z, r, acc[6]);
-        acc[7] = __builtin_fmaf(m1.w, r, acc[7]);
-      }
-#pragma unroll
-      for (int q = 0; q < 8; ++q) L.u.st.W[8 * tq + q][j] = acc[q];
-    }
-  }
-  __syncthreads();
-  const float gl = L.gamma[C - 1];
-#pragma unroll
-  for (int ii = 0; ii < 8; ++ii)
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) S[ii][jj] = gl * S[ii][jj];
-#pragma unroll 4
-  for (int s = 0; s < C; ++s) {
-    float kc[8];
-    const float c_s = L.cf[s];
-#pragma unroll
-    for (int ii = 0; ii < 8; ++ii) kc[ii] = c_s * L.K[s][8 * T.ti + ii];  // cf_s k^_s
-    const float2 w2 = *reinterpret_cast<const float2*>(&L.u.st.W[s][2 * T.tc]);
-#pragma unroll
-    for (int ii = 0; ii < 8; ++ii) {
-      S[ii][0] = __builtin_fmaf(kc[ii], w2.x, S[ii][0]);
-      S[ii][1] = __builtin_fmaf(kc[ii], w2.y, S[ii][1]);
-    }
-  }
-  __syncthreads();  // LDS free for the next chunk
+struct alignas(16) StateLds {
+  float K[C][kSKStride];  // k^ of the chunk's tokens
+  float M[C][C + 4];      // M[t][s]
+  float gamma[C], cf[C];
+};
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// The chunk's inputs into LDS: every global load issued before the first LDS
-// write, so the memory latency is paid once. K: all 128 rows of k^ for the
-// chunk's C tokens; V: the block's 32 columns.
-template <int C, typename KAt, typename VAt, typename GAt>
-__device__ __forceinline__ void fill_chunk(ChunkLds<C>& L, const Tc& T, KAt kat, VAt vat, GAt gat) {
-  constexpr int PK = C * kD / 256, PV = C * kCB / 256;
-  float kr[PK], vr[PV];
+// S (b_j on entry) becomes b_{j+1}:
+//   P_t = S0^T k^_t: per 16-token block, MFMA k-steps over row blocks ib
+//        ascending, k-step q taking rows 16 ib + 4 g + q;
+//   r_t = v_t - gamma_t P_t;
+//   w_t = sum_s M[t][s] r_s: k-steps over token blocks sb ascending, q as
+//        above (s over the whole chunk; M is +0 above the diagonal);
+//   S_C = gamma_last S0 + sum_s (cf_s k^_s) w_s^T: S0 scaled first, then
+//        k-steps over sb ascending; A entries cf_s * k^_s[i] rounded once.
+// v: this lane's v_t (t = 16 tb + 4 g + r).
+template <int C>
+__device__ __forceinline__ void chunk_state(f32x4 (&S)[8], const StateLds<C>& L, const float (&v)[C / 16][4],
+                                            int lane) {
+  constexpr int TB = C / 16;
+  const int g = lane >> 4, c16 = lane & 15;
+  f32x4 P[TB];
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb) P[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ib = 0; ib < 8; ++ib)
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      const f32x4 k4 = *reinterpret_cast<const f32x4*>(&L.K[16 * tb + c16][16 * ib + 4 * g]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) P[tb] = mfma4(k4[q], S[ib][q], P[tb]);
+    }
+  f32x4 R[TB];
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) R[tb][r] = v[tb][r] - L.gamma[16 * tb + 4 * g + r] * P[tb][r];
+  f32x4 W[TB];
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb) W[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int sb = 0; sb < TB; ++sb)
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      const f32x4 m4 = *reinterpret_cast<const f32x4*>(&L.M[16 * tb + c16][16 * sb + 4 * g]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) W[tb] = mfma4(m4[q], R[sb][q], W[tb]);
+    }
+  const float glast = L.gamma[C - 1];
+#pragma unroll
+  for (int ib = 0; ib < 8; ++ib)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) S[ib][r] = glast * S[ib][r];
+#pragma unroll
+  for (int sb = 0; sb < TB; ++sb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float* krow = &L.K[16 * sb + 4 * g + q][c16];
+      const float cf = L.cf[16 * sb + 4 * g + q];
+#pragma unroll
+      for (int ib = 0; ib < 8; ++ib) S[ib] = mfma4(cf * krow[16 * ib], W[sb][q], S[ib]);
+    }
+}
+
+// Buffer accesses: a descriptor over one array range (uniform), the lane's
+// part of the byte offset in one VGPR and the rest a scalar offset, so a
+// loop over blocks keeps no per-load 64-bit address.
+__device__ __forceinline__ float bload(buf_rsrc r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+__device__ __forceinline__ f32x4 bload4(buf_rsrc r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ void bstore(float v, buf_rsrc r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, soff, 0);
+}
+
+// The wave's state columns <-> one global state [128][128] fp32 (row-major).
+__device__ __forceinline__ void load_cols(f32x4 (&S)[8], const float* __restrict__ g, int c0, int lane) {
+  const buf_rsrc r = make_rsrc(g, kD * kD * 4);
+  const uint32_t vo = (uint32_t)((4 * (lane >> 4) * kD + c0 + (lane & 15)) * 4);
+#pragma unroll
+  for (int ib = 0; ib < 8; ++ib)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) S[ib][q] = bload(r, vo, (uint32_t)((16 * ib + q) * kD * 4));
+}
+__device__ __forceinline__ void store_cols(const f32x4 (&S)[8], float* __restrict__ g, int c0, int lane) {
+  const buf_rsrc r = make_rsrc(g, kD * kD * 4);
+  const uint32_t vo = (uint32_t)((4 * (lane >> 4) * kD + c0 + (lane & 15)) * 4);
+#pragma unroll
+  for (int ib = 0; ib < 8; ++ib)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) bstore(S[ib][q], r, vo, (uint32_t)((16 * ib + q) * kD * 4));
+}
+
+// One chunk's state-phase inputs. K (k^: C token rows of 128 fp32 at kbase,
+// tok_stride floats apart), M (row-major) and the gates' products go to LDS,
+// every global load issued before the first LDS write; the lane's own v
+// (C token rows at vbase, tok_stride elements apart, bf16 or fp32) goes to
+// registers. coef: the chunk's [M (C x C) | gamma (C) | cf (C)].
+template <int C, typename VT>
+__device__ __forceinline__ void state_inputs(StateLds<C>& L, const float* __restrict__ coef,
+                                             const float* __restrict__ kbase, const VT* __restrict__ vbase,
+                                             int64_t tok_stride, float (&v)[C / 16][4], int tid, int c0) {
+  constexpr int NT = 64 * kStateWaves;
+  constexpr int PK = C * kD / 4 / NT, PM = C * C / 4 / NT;
+  static_assert(NT % (kD / 4) == 0, "a thread keeps its k^ column across loads");
+  const int lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+  const uint32_t ts = (uint32_t)tok_stride;
+  const buf_rsrc rk = make_rsrc(kbase, (uint32_t)(((C - 1) * tok_stride + kD) * 4));
+  const buf_rsrc rc = make_rsrc(coef, (uint32_t)((C * C + 2 * C) * 4));
+  const buf_rsrc rv = make_rsrc(vbase, (uint32_t)(((C - 1) * tok_stride + kD) * sizeof(VT)));
+  const int tk = tid / (kD / 4), i4 = 4 * (tid % (kD / 4));  // token row and column of load u = 0
+  f32x4 kr[PK], mr[PM];
+#pragma unroll
+  for (int u = 0; u < PK; ++u)
+    kr[u] = bload4(rk, (uint32_t)((tk * ts + i4) * 4), (uint32_t)(u * (NT / (kD / 4)) * ts * 4));
+#pragma unroll
+  for (int u = 0; u < PM; ++u) mr[u] = bload4(rc, (uint32_t)(tid * 16), (uint32_t)(u * NT * 16));
+  const uint32_t vo = (uint32_t)((4 * g * ts + c0 + c16) * sizeof(VT));
+#pragma unroll
+  for (int tb = 0; tb < C / 16; ++tb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t so = (uint32_t)((16 * tb + r) * ts * sizeof(VT));
+      if constexpr (sizeof(VT) == 2)
+        v[tb][r] = bf16_bits_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rv, vo, so, 0));
+      else
+        v[tb][r] = bload(rv, vo, so);
+    }
+  float gc = 0.0f;
+  if (tid < 2 * C) gc = bload(rc, (uint32_t)((C * C + tid) * 4), 0u);  // gamma then cf
+  __syncthreads();  // every wave is done with the previous chunk's LDS
+#pragma unroll
+  for (int u = 0; u < PK; ++u) *reinterpret_cast<f32x4*>(&L.K[tk + u * (NT / (kD / 4))][i4]) = kr[u];
+#pragma unroll
+  for (int u = 0; u < PM; ++u) {
+    const int e = tid + NT * u;
+    *reinterpret_cast<f32x4*>(&L.M[e / (C / 4)][4 * (e % (C / 4))]) = mr[u];
+  }
+  if (tid < C) L.gamma[tid] = gc;
+  else if (tid < 2 * C) L.cf[tid - C] = gc;
+  __syncthreads();
+}
+
+// The coefficient phase's inputs into LDS: every global load issued before
+// the first LDS write, so the memory latency is paid once. K: all 128 rows of
+// k^ for the chunk's C tokens; the gates.
+template <int C, typename KAt, typename GAt>
+__device__ __forceinline__ void fill_chunk(ChunkLds<C>& L, const Tc& T, KAt kat, GAt gat) {
+  constexpr int PK = C * kD / 256;
+  float kr[PK];
 #pragma unroll
   for (int u = 0; u < PK; ++u) {
     const int e = T.tid + 256 * u;
     kr[u] = kat(e / kD, e % kD);
-  }
-#pragma unroll
-  for (int u = 0; u < PV; ++u) {
-    const int e = T.tid + 256 * u;
-    vr[u] = vat(e / kCB, e % kCB);
   }
   float al = 0.0f, be = 0.0f;
   if (T.tid < C) gat(T.tid, al, be);
@@ -337,31 +411,11 @@ __device__ __forceinline__ void fill_chunk(ChunkLds<C>& L, const Tc& T, KAt kat,
     const int e = T.tid + 256 * u;
     L.K[e / kD][e % kD] = kr[u];
   }
-#pragma unroll
-  for (int u = 0; u < PV; ++u) {
-    const int e = T.tid + 256 * u;
-    L.V[e / kCB][e % kCB] = vr[u];
-  }
   if (T.tid < C) {
     L.alpha[T.tid] = al;
     L.beta[T.tid] = be;
   }
   __syncthreads();
-}
-
-// Column block <-> global state [128][128] fp32 (row-major).
-__device__ __forceinline__ void load_block(float (&S)[8][2], const float* __restrict__ g, int cb, const Tc& T) {
-#pragma unroll
-  for (int ii = 0; ii < 8; ++ii) {
-    const float2 x = *reinterpret_cast<const float2*>(g + (8 * T.ti + ii) * kD + kCB * cb + 2 * T.tc);
-    S[ii][0] = x.x;
-    S[ii][1] = x.y;
-  }
-}
-__device__ __forceinline__ void store_block(const float (&S)[8][2], float* __restrict__ g, int cb, const Tc& T) {
-#pragma unroll
-  for (int ii = 0; ii < 8; ++ii)
-    *reinterpret_cast<float2*>(g + (8 * T.ti + ii) * kD + kCB * cb + 2 * T.tc) = make_float2(S[ii][0], S[ii][1]);
 }
 
 // State block <-> global [128][128] fp32 (row-major), thread's 8x8 block.
@@ -392,7 +446,7 @@ struct CacheView {
   float* vbuf;  // [C][H][128]
   float* abuf;  // [C][H]
   float* bbuf;  // [C][H]
-  float* coef;  // [H][C*C + 2C] the closing chunk's M^T, gamma, ratios (decode scratch)
+  float* coef;  // [H][C*C + 2C] the closing chunk's M (row-major), gamma, ratios (decode scratch)
 };
 __device__ __forceinline__ CacheView cache_view(void* base, int64_t seq, int H, int C) {
   const int64_t per = gdn_cache_floats(H, C);
@@ -457,14 +511,14 @@ __global__ __launch_bounds__(256, 2) void gdn_coef_kernel(GdnArgs a) {
   if (j < 0 || (j + 1) * C > len) return;  // not a full chunk (uniform)
   const int64_t tc0 = t0 + j * C;
   fill_chunk<C>(
-      L, T, [&](int t, int i) { return a.kh[((tc0 + t) * a.H + h) * kD + i]; }, [&](int, int) { return 0.0f; },
+      L, T, [&](int t, int i) { return a.kh[((tc0 + t) * a.H + h) * kD + i]; },
       [&](int t, float& al, float& be) {
         al = a.alpha[(tc0 + t) * a.H + h];
         be = a.beta[(tc0 + t) * a.H + h];
       });
   chunk_coeffs<C>(L, T);
   float* dst = a.coef + (c * a.H + h) * (int64_t)(C * C + 2 * C);
-  for (int e = T.tid; e < C * C; e += 256) dst[e] = L.MT[e / C][e % C];
+  for (int e = T.tid; e < C * C; e += 256) dst[e] = L.MT[e % C][e / C];  // M[t][s], row-major
   if (T.tid < C) {
     dst[C * C + T.tid] = L.gamma[T.tid];
     dst[C * C + C + T.tid] = L.cf[T.tid];
@@ -472,71 +526,35 @@ __global__ __launch_bounds__(256, 2) void gdn_coef_kernel(GdnArgs a) {
 }
 
 // First pass, the state-dependent part: one workgroup per (sequence, head,
-// column block), the chunks in order, each chunk's coefficients read from
-// the coefficient pass.
+// 32-column block), a wave per 16 columns, the chunks in order, each chunk's
+// coefficients read from the coefficient pass.
 template <int C>
-__global__ __launch_bounds__(256, 2) void gdn_boundary_kernel(GdnArgs a) {
-  __shared__ ChunkLds<C> L;
-  const Tc T = col_layout();
-  const int s = blockIdx.x, h = blockIdx.y, cb = blockIdx.z;
+__global__ __launch_bounds__(64 * kStateWaves) __attribute__((amdgpu_waves_per_eu(2))) void gdn_boundary_kernel(GdnArgs a) {
+  __shared__ StateLds<C> L;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int c0 = kSB * (int)blockIdx.z + kWC * (tid >> 6);
+  const int s = blockIdx.x, h = blockIdx.y;
   const int64_t t0 = cu_at(a, s), len = max(cu_at(a, s + 1) - t0, (int64_t)0);
   const int64_t n = len / C;
   const int64_t base = boundary_base(a, s, C);
   const int64_t plane = (int64_t)kD * kD;
-  float S[8][2];
+  f32x4 S[8];
 #pragma unroll
-  for (int ii = 0; ii < 8; ++ii) S[ii][0] = S[ii][1] = 0.0f;
-  store_block(S, a.bstates + (base * a.H + h) * plane, cb, T);
+  for (int ib = 0; ib < 8; ++ib) S[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
+  store_cols(S, a.bstates + (base * a.H + h) * plane, c0, lane);
   for (int64_t j = 0; j < n; ++j) {
     const int64_t tc0 = t0 + j * C;
-    const float* cf = a.coef + ((base + j) * a.H + h) * (int64_t)(C * C + 2 * C);
-    // every load issued before the first LDS write
-    constexpr int PK = C * kD / 256, PV = C * kCB / 256, PM = C * C / 256;
-    float kr[PK], vr[PV], mr[PM];
-#pragma unroll
-    for (int u = 0; u < PK; ++u) {
-      const int e = T.tid + 256 * u;
-      kr[u] = a.kh[((tc0 + e / kD) * a.H + h) * kD + e % kD];
-    }
-#pragma unroll
-    for (int u = 0; u < PV; ++u) {
-      const int e = T.tid + 256 * u;
-      vr[u] = bf16_bits_to_f32(a.v[((tc0 + e / kCB) * a.H + h) * kD + kCB * cb + e % kCB]);
-    }
-#pragma unroll
-    for (int u = 0; u < PM; ++u) mr[u] = cf[T.tid + 256 * u];
-    float gm = 0.0f, cfv = 0.0f;
-    if (T.tid < C) {
-      gm = cf[C * C + T.tid];
-      cfv = cf[C * C + C + T.tid];
-    }
-#pragma unroll
-    for (int u = 0; u < PK; ++u) {
-      const int e = T.tid + 256 * u;
-      L.K[e / kD][e % kD] = kr[u];
-    }
-#pragma unroll
-    for (int u = 0; u < PV; ++u) {
-      const int e = T.tid + 256 * u;
-      L.V[e / kCB][e % kCB] = vr[u];
-    }
-#pragma unroll
-    for (int u = 0; u < PM; ++u) {
-      const int e = T.tid + 256 * u;
-      L.MT[e / C][e % C] = mr[u];
-    }
-    if (T.tid < C) {
-      L.gamma[T.tid] = gm;
-      L.cf[T.tid] = cfv;
-    }
-    __syncthreads();
-    chunk_state<C>(S, L, T);
-    store_block(S, a.bstates + ((base + j + 1) * a.H + h) * plane, cb, T);
+    const float* coef = a.coef + ((base + j) * a.H + h) * (int64_t)(C * C + 2 * C);
+    float v[C / 16][4];
+    state_inputs<C>(L, coef, a.kh + (tc0 * a.H + h) * kD, a.v + (tc0 * a.H + h) * kD, (int64_t)a.H * kD, v, tid,
+                    c0);
+    chunk_state<C>(S, L, v, lane);
+    store_cols(S, a.bstates + ((base + j + 1) * a.H + h) * plane, c0, lane);
   }
   if (a.cache) {
     const CacheView cv = cache_view(a.cache, s, a.H, C);
-    store_block(S, cv.sb + h * plane, cb, T);
-    if (len % C == 0) store_block(S, cv.srun + h * plane, cb, T);
+    store_cols(S, cv.sb + h * plane, c0, lane);
+    if (len % C == 0) store_cols(S, cv.srun + h * plane, c0, lane);
   }
 }
 
@@ -696,14 +714,14 @@ __global__ __launch_bounds__(256, 2) void gdn_decode_coef_kernel(GdnDecodeArgs a
   if (pos < 0 || (pos + 1) % C != 0) return;  // uniform
   const CacheView cv = cache_view(a.cache, bseq, a.H, C);
   fill_chunk<C>(
-      L, T, [&](int t, int i) { return cv.kbuf[((int64_t)t * a.H + h) * kD + i]; }, [&](int, int) { return 0.0f; },
+      L, T, [&](int t, int i) { return cv.kbuf[((int64_t)t * a.H + h) * kD + i]; },
       [&](int t, float& al, float& be) {
         al = cv.abuf[(int64_t)t * a.H + h];
         be = cv.bbuf[(int64_t)t * a.H + h];
       });
   chunk_coeffs<C>(L, T);
   float* dst = cv.coef + (int64_t)h * (C * C + 2 * C);
-  for (int e = T.tid; e < C * C; e += 256) dst[e] = L.MT[e / C][e % C];
+  for (int e = T.tid; e < C * C; e += 256) dst[e] = L.MT[e % C][e / C];  // M[t][s], row-major
   if (T.tid < C) {
     dst[C * C + T.tid] = L.gamma[T.tid];
     dst[C * C + C + T.tid] = L.cf[T.tid];
@@ -711,62 +729,26 @@ __global__ __launch_bounds__(256, 2) void gdn_decode_coef_kernel(GdnDecodeArgs a
 }
 
 // ... then the boundary state advanced by the same chunk_state as the first
-// pass (one workgroup per column block), and the running state resynchronised
-// to it.
+// pass (one workgroup per 32 columns, a wave per 16), and the running state
+// resynchronised to it.
 template <int C>
-__global__ __launch_bounds__(256, 2) void gdn_decode_resync_kernel(GdnDecodeArgs a) {
-  __shared__ ChunkLds<C> L;
-  const Tc T = col_layout();
-  const int bseq = blockIdx.x, h = blockIdx.y, cb = blockIdx.z;
+__global__ __launch_bounds__(64 * kStateWaves) __attribute__((amdgpu_waves_per_eu(2))) void gdn_decode_resync_kernel(GdnDecodeArgs a) {
+  __shared__ StateLds<C> L;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int c0 = kSB * (int)blockIdx.z + kWC * (tid >> 6);
+  const int bseq = blockIdx.x, h = blockIdx.y;
   const int64_t pos = a.pos[bseq];
   if (pos < 0 || (pos + 1) % C != 0) return;  // uniform
   const CacheView cv = cache_view(a.cache, bseq, a.H, C);
-  const float* cf = cv.coef + (int64_t)h * (C * C + 2 * C);
-  constexpr int PK = C * kD / 256, PV = C * kCB / 256, PM = C * C / 256;
-  float kr[PK], vr[PV], mr[PM];
-#pragma unroll
-  for (int u = 0; u < PK; ++u) {
-    const int e = T.tid + 256 * u;
-    kr[u] = cv.kbuf[((int64_t)(e / kD) * a.H + h) * kD + e % kD];
-  }
-#pragma unroll
-  for (int u = 0; u < PV; ++u) {
-    const int e = T.tid + 256 * u;
-    vr[u] = cv.vbuf[((int64_t)(e / kCB) * a.H + h) * kD + kCB * cb + e % kCB];
-  }
-#pragma unroll
-  for (int u = 0; u < PM; ++u) mr[u] = cf[T.tid + 256 * u];
-  float gm = 0.0f, cfv = 0.0f;
-  if (T.tid < C) {
-    gm = cf[C * C + T.tid];
-    cfv = cf[C * C + C + T.tid];
-  }
-#pragma unroll
-  for (int u = 0; u < PK; ++u) {
-    const int e = T.tid + 256 * u;
-    L.K[e / kD][e % kD] = kr[u];
-  }
-#pragma unroll
-  for (int u = 0; u < PV; ++u) {
-    const int e = T.tid + 256 * u;
-    L.V[e / kCB][e % kCB] = vr[u];
-  }
-#pragma unroll
-  for (int u = 0; u < PM; ++u) {
-    const int e = T.tid + 256 * u;
-    L.MT[e / C][e % C] = mr[u];
-  }
-  if (T.tid < C) {
-    L.gamma[T.tid] = gm;
-    L.cf[T.tid] = cfv;
-  }
-  __syncthreads();
+  const float* coef = cv.coef + (int64_t)h * (C * C + 2 * C);
   const int64_t plane = (int64_t)kD * kD;
-  float S[8][2];
-  load_block(S, cv.sb + h * plane, cb, T);
-  chunk_state<C>(S, L, T);
-  store_block(S, cv.sb + h * plane, cb, T);
-  store_block(S, cv.srun + h * plane, cb, T);
+  f32x4 S[8];
+  load_cols(S, cv.sb + h * plane, c0, lane);
+  float v[C / 16][4];
+  state_inputs<C>(L, coef, cv.kbuf + (int64_t)h * kD, cv.vbuf + (int64_t)h * kD, (int64_t)a.H * kD, v, tid, c0);
+  chunk_state<C>(S, L, v, lane);
+  store_cols(S, cv.sb + h * plane, c0, lane);
+  store_cols(S, cv.srun + h * plane, c0, lane);
 }
 
 }  // namespace
@@ -778,18 +760,18 @@ hipError_t launch_gdn_prefill(const GdnArgs& a, int C, bool out_bf16, hipStream_
                        reinterpret_cast<const uint32_t*>(a.q), reinterpret_cast<const uint32_t*>(a.k), a.g, a.qh, a.kh,
                        a.alpha, TH);
   }
-  const dim3 gb((unsigned)a.S, (unsigned)a.H, (unsigned)(kD / kCB));
+  const dim3 gb((unsigned)a.S, (unsigned)a.H, (unsigned)(kD / kSB));
   const dim3 go((unsigned)(a.T / C + a.S), (unsigned)a.H);
   switch (C) {
     case 32:
       hipLaunchKernelGGL(gdn_coef_kernel<32>, go, dim3(256), 0, s, a);
-      hipLaunchKernelGGL(gdn_boundary_kernel<32>, gb, dim3(256), 0, s, a);
+      hipLaunchKernelGGL(gdn_boundary_kernel<32>, gb, dim3(64 * kStateWaves), 0, s, a);
       if (out_bf16) hipLaunchKernelGGL((gdn_output_kernel<32, true>), go, dim3(256), 0, s, a);
       else hipLaunchKernelGGL((gdn_output_kernel<32, false>), go, dim3(256), 0, s, a);
       break;
     case 64:
       hipLaunchKernelGGL(gdn_coef_kernel<64>, go, dim3(256), 0, s, a);
-      hipLaunchKernelGGL(gdn_boundary_kernel<64>, gb, dim3(256), 0, s, a);
+      hipLaunchKernelGGL(gdn_boundary_kernel<64>, gb, dim3(64 * kStateWaves), 0, s, a);
       if (out_bf16) hipLaunchKernelGGL((gdn_output_kernel<64, true>), go, dim3(256), 0, s, a);
       else hipLaunchKernelGGL((gdn_output_kernel<64, false>), go, dim3(256), 0, s, a);
       break;
@@ -801,19 +783,19 @@ hipError_t launch_gdn_prefill(const GdnArgs& a, int C, bool out_bf16, hipStream_
 
 hipError_t launch_gdn_decode(const GdnDecodeArgs& a, int C, bool out_bf16, hipStream_t s) {
   const dim3 grid((unsigned)a.B, (unsigned)a.H);
-  const dim3 grid_r((unsigned)a.B, (unsigned)a.H, (unsigned)(kD / kCB));
+  const dim3 grid_r((unsigned)a.B, (unsigned)a.H, (unsigned)(kD / kSB));
   switch (C) {
     case 32:
       if (out_bf16) hipLaunchKernelGGL((gdn_decode_step_kernel<32, true>), grid, dim3(256), 0, s, a);
       else hipLaunchKernelGGL((gdn_decode_step_kernel<32, false>), grid, dim3(256), 0, s, a);
       hipLaunchKernelGGL(gdn_decode_coef_kernel<32>, grid, dim3(256), 0, s, a);
-      hipLaunchKernelGGL(gdn_decode_resync_kernel<32>, grid_r, dim3(256), 0, s, a);
+      hipLaunchKernelGGL(gdn_decode_resync_kernel<32>, grid_r, dim3(64 * kStateWaves), 0, s, a);
       break;
     case 64:
       if (out_bf16) hipLaunchKernelGGL((gdn_decode_step_kernel<64, true>), grid, dim3(256), 0, s, a);
       else hipLaunchKernelGGL((gdn_decode_step_kernel<64, false>), grid, dim3(256), 0, s, a);
       hipLaunchKernelGGL(gdn_decode_coef_kernel<64>, grid, dim3(256), 0, s, a);
-      hipLaunchKernelGGL(gdn_decode_resync_kernel<64>, grid_r, dim3(256), 0, s, a);
+      hipLaunchKernelGGL(gdn_decode_resync_kernel<64>, grid_r, dim3(64 * kStateWaves), 0, s, a);
       break;
     default:
       return hipErrorInvalidValue;

@@ -107,7 +107,7 @@ struct GdnArgs {
   float* kh;              // [T, H, 128]
   float* alpha;           // [T, H]
   float* bstates;         // [T/C + S, H, 128, 128] boundary states
-  float* coef;            // [T/C + S, H, C*C + 2C] per-chunk M^T, gamma, gamma_last/gamma
+  float* coef;            // [T/C + S, H, C*C + 2C] per-chunk M (row-major), gamma, gamma_last/gamma
 };
 struct GdnDecodeArgs {
   const uint16_t* q;      // [B, H, 128] bf16
