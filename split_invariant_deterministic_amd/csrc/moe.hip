@@ -255,15 +255,35 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
   const int nv = (int)min((int64_t)4, H - h);
   float v[KK][4];
   bool bad = false;
+  if (H % 4 == 0 && (reinterpret_cast<uintptr_t>(Y) & 15) == 0) {
+    // rows 16-byte aligned and h < H a multiple of 4: one float4 per expert
+    // row, all KK loads in flight (a row past the table reads row 0 and the
+    // token becomes NaN below)
+    f32x4 y[KK];
+    float wj[KK];
 #pragma unroll
-  for (int j = 0; j < KK; ++j) {
-    const int32_t s = slot[t * KK + j];
-    const float wj = w[t * KK + j];
-    const bool ok = s >= 0 && s < y_rows;
-    bad |= !ok;
-    const float* yr = Y + (ok ? (int64_t)s : 0) * H + h;
+    for (int j = 0; j < KK; ++j) {
+      const int32_t s = slot[t * KK + j];
+      wj[j] = w[t * KK + j];
+      const bool ok = s >= 0 && s < y_rows;
+      bad |= !ok;
+      y[j] = *reinterpret_cast<const f32x4*>(Y + (ok ? (int64_t)s : 0) * H + h);
+    }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) v[j][q] = (q < nv && ok) ? wj * yr[q] : 0.0f;
+    for (int j = 0; j < KK; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[j][q] = wj[j] * y[j][q];
+  } else {
+#pragma unroll
+    for (int j = 0; j < KK; ++j) {
+      const int32_t s = slot[t * KK + j];
+      const float wj = w[t * KK + j];
+      const bool ok = s >= 0 && s < y_rows;
+      bad |= !ok;
+      const float* yr = Y + (ok ? (int64_t)s : 0) * H + h;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[j][q] = (q < nv && ok) ? wj * yr[q] : 0.0f;
+    }
   }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {

@@ -198,3 +198,19 @@ def test_permute_small_and_ragged(inv, T):
     assert np.array_equal(offsets.cpu().numpy(), o)
     assert np.array_equal(rows.cpu().numpy(), r)
     assert np.array_equal(slot.cpu().numpy(), s)
+
+
+@pytest.mark.parametrize("H,offset", [(2048, 0), (2048, 1), (2046, 0), (6, 0)])
+def test_combine_vector_and_scalar_paths(inv, H, offset):
+    """The combine's float4 path (H % 4 == 0, Y 16-byte aligned) and its
+    per-element path (a Y pointer 4 bytes off, or H % 4 != 0) both replay the
+    oracle's combine bit for bit."""
+    T, KK, rows = 64, 8, 300
+    g = torch.Generator().manual_seed(1000 * H + offset)
+    flat = torch.randn(rows * H + 4, generator=g).to(DEV)
+    Y = flat[offset:offset + rows * H].view(rows, H)
+    w = torch.rand((T, KK), generator=g).to(DEV)
+    slot = torch.randint(0, rows, (T, KK), generator=g, dtype=torch.int32).to(DEV)
+    out = inv.moe_combine(Y, w, slot, inv.contract(leaves=8))
+    ref = omoe.combine(Y.cpu().numpy()[slot.cpu().numpy()], w.cpu().numpy())
+    assert np.array_equal(_np(out), ref.astype(np.float32))
