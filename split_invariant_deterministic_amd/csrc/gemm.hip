@@ -60,6 +60,10 @@ template <int NL, class Ctx>
 __device__ __forceinline__ void run_tree(Ctx& c, typename Ctx::Acc& out) {
   if constexpr (NL == 1) {
     c.leaf(out);
+  } else if constexpr (NL == 2 && Ctx::kOddLeaves) {
+    typename Ctx::Acc right;
+    c.leaf_pair(out, right);
+    acc_add(out, right);
   } else {
     run_tree<NL / 2>(c, out);
     typename Ctx::Acc right;
@@ -187,7 +191,7 @@ __device__ __forceinline__ void wait_vm_rem(int rem) {
 
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-template <int BK, int RING>
+template <int BK, int RING, bool ODD = false>
 struct RingCtx {
   using R = Ring<BK, RING>;
   static constexpr int NW = R::NW;
@@ -213,7 +217,7 @@ struct RingCtx {
   int rd_off;     // ring slot of stage g
   int g;          // next stage to compute
   int total;      // stages in the range
-  int spl;        // stages per leaf
+  int spl;        // stages per leaf (ODD: 32-wide substeps per leaf)
   int wave;       // wave-uniform
 
   // The direct-to-LDS builtin is compiled in the device pass only: seen by the
@@ -351,9 +355,58 @@ struct RingCtx {
     ++g;
   }
 
+  // Leaves of an odd number 2m+1 of 32-wide k substeps (kl = 64 m + 32) on
+  // 64-k stages. Post-order always runs leaves in pairs (2l, 2l+1), and a pair
+  // spans exactly 2m+1 stages: m whole stages of the first leaf, one stage
+  // whose k substep 0 ends the first leaf and whose substep 1 starts the
+  // second, then m whole stages of the second. The split stage is stage64
+  // with the two substeps' MFMAs on different accumulators.
+  static constexpr bool kOddLeaves = ODD;
+  template <bool AFIRST>
+  __device__ __forceinline__ void split_stage(Acc& a, Acc& b) {
+    bf16x8 fa1[4], fb1[FN];
+    read_frags(rd_off, 1, fa1, fb1);
+    if constexpr (AFIRST) mma_first(fa0, fb0, a);
+    else mma(fa0, fb0, a);
+    wait_vm_rem<R::LOADS, R::NS - 2>(total - 2 - g);
+    block_barrier();  // stage g+1 visible; every wave's reads of stage g are done
+    rd_off = next_slot(rd_off);
+    read_frags(rd_off, 0, fa0, fb0);
+    const bool more = issued < total;
+    constexpr int LPI = R::LOADS / 4;
+    static_assert(LPI * 4 == R::LOADS && FN % LPI == 0, "interleave");
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int h = 0; h < LPI; ++h) {
+        if (more) issue_one(LPI * i + h);
+#pragma unroll
+        for (int j = h * FN / LPI; j < (h + 1) * FN / LPI; ++j)
+          b.v[i][j] = mfma16(fa1[i], fb1[j], f32x4{0.f, 0.f, 0.f, 0.f});  // the second leaf starts at +0
+      }
+    if (more) issue_done();
+    ++g;
+  }
+  // Two consecutive leaves (spl = 2m+1 substeps each) into a and b.
+  __device__ __forceinline__ void leaf_pair(Acc& a, Acc& b) {
+    static_assert(ODD && BK == 64, "odd leaves on 64-k stages");
+    const int m = (spl - 1) / 2;
+    if (m == 0) {
+      split_stage<true>(a, b);
+      return;
+    }
+    stage64<true>(a);
+#pragma clang loop unroll(disable)
+    for (int s = 1; s < m; ++s) stage64<false>(a);
+    split_stage<false>(a, b);
+#pragma clang loop unroll(disable)
+    for (int s = 0; s < m; ++s) stage64<false>(b);
+  }
+
   // One leaf: the chain starts at +0 and takes the leaf's stages in
   // ascending k, each stage as its 32-wide k substeps in ascending order.
   __device__ __forceinline__ void leaf(Acc& acc) {
+    static_assert(!ODD, "odd leaves run in pairs (leaf_pair)");
     if constexpr (BK == 64) {
       stage64<true>(acc);
 #pragma clang loop unroll(disable)
@@ -374,12 +427,15 @@ struct RingCtx {
 template <int NL>
 constexpr int ring_bytes() { return NL == 8 ? 98304 : 131072; }
 
-template <int NL, int BK, int OUTM, bool GROUPED>
+// ODD: leaves that are an odd multiple of 32 on 64-k stages (NL even, so the
+// range is whole stages).
+template <int NL, int BK, int OUTM, bool GROUPED, bool ODD = false>
 __global__ __launch_bounds__(64 * kRingWaves, 1) void gemm_ring_kernel(TileParams p) {
   constexpr int RING = ring_bytes<NL>();
   constexpr int SPILL = NL == 8 ? 65536 : 0;
   using R = Ring<BK, RING>;
-  using Ctx = RingCtx<BK, RING>;
+  using Ctx = RingCtx<BK, RING, ODD>;
+  static_assert(!ODD || (BK == 64 && NL % 2 == 0), "odd leaves pair up into 64-k stages");
   constexpr int NW = Ctx::NW, WN = Ctx::WN, FN = Ctx::FN;
   constexpr int LPS = WN + 4;  // row stride of the transposed tile (floats)
   constexpr int LP_BYTES = OUTM == kOutLP ? NW * 64 * LPS * 4 : 0;
@@ -461,8 +517,8 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void gemm_ring_kernel(TileParam
   c.iss_off = 0;
   c.issued = 0;
   c.rd_off = 0;
-  c.spl = p.kl / BK;
-  c.total = c.spl * NL;
+  c.spl = ODD ? p.kl / 32 : p.kl / BK;
+  c.total = ODD ? NL * p.kl / 64 : c.spl * NL;
   c.g = 0;
   const int wm = c.wave / (NW / 2), wn = c.wave % (NW / 2);  // wave tile (row, column) in the tile
   {
@@ -761,22 +817,25 @@ __global__ __launch_bounds__(256) void cast_bf16_kernel(const float* __restrict_
 
 // ------------------------------------------------------------------ dispatch
 
-#define INV_RING_CASE(NL_, BK_)                                                                              \
-  hipLaunchKernelGGL((gemm_ring_kernel<NL_, BK_, OUTM, GROUPED>), grid, dim3(64 * kRingWaves), 0, s, p);     \
+#define INV_RING_CASE(NL_, BK_, ODD_)                                                                        \
+  hipLaunchKernelGGL((gemm_ring_kernel<NL_, BK_, OUTM, GROUPED, ODD_>), grid, dim3(64 * kRingWaves), 0, s, p); \
   break;
 
+// Leaves that are a multiple of 64 run on 64-k stages; leaves that are an odd
+// multiple of 32 run on 64-k stages as 32-wide substeps when the leaf count
+// is even, else (one leaf) on 32-k stages.
 template <int OUTM, bool GROUPED>
 hipError_t ring_dispatch(const TileParams& p, dim3 grid, int nl, hipStream_t s) {
-  const bool bk64 = p.kl % 64 == 0;  // else the leaf is an odd multiple of 32
+  const bool bk64 = p.kl % 64 == 0;
   switch (nl * 2 + (bk64 ? 1 : 0)) {
-    case 2: INV_RING_CASE(1, 32)
-    case 3: INV_RING_CASE(1, 64)
-    case 4: INV_RING_CASE(2, 32)
-    case 5: INV_RING_CASE(2, 64)
-    case 8: INV_RING_CASE(4, 32)
-    case 9: INV_RING_CASE(4, 64)
-    case 16: INV_RING_CASE(8, 32)
-    case 17: INV_RING_CASE(8, 64)
+    case 2: INV_RING_CASE(1, 32, false)
+    case 3: INV_RING_CASE(1, 64, false)
+    case 4: INV_RING_CASE(2, 64, true)
+    case 5: INV_RING_CASE(2, 64, false)
+    case 8: INV_RING_CASE(4, 64, true)
+    case 9: INV_RING_CASE(4, 64, false)
+    case 16: INV_RING_CASE(8, 64, true)
+    case 17: INV_RING_CASE(8, 64, false)
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

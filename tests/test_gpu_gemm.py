@@ -49,7 +49,11 @@ def test_tiny_against_oracle(inv, out):
 
 
 @pytest.mark.parametrize("M,N,K,L", [(8, 512, 256, 4), (100, 300, 1024, 8), (33, 17, 512, 8),
-                                     (130, 129, 256, 2), (64, 64, 64, 1)])
+                                     (130, 129, 256, 2), (64, 64, 64, 1),
+                                     # leaves of 96 (an odd multiple of 32): the fused launch runs them
+                                     # as 32-wide substeps of 64-k stages, the per-leaf launches on
+                                     # 32-k stages
+                                     (200, 300, 768, 8), (150, 200, 384, 4), (130, 129, 192, 2)])
 def test_leaf_partials_bound_and_bit_exact_replay(inv, M, N, K, L):
     A = synth.randn((M, K), 101)
     B = synth.randn((N, K), 102, 0.02)
@@ -160,6 +164,22 @@ def test_rank_partitions_are_bitwise_equal(inv, dense_inputs, K, N, M):
         P = torch.stack([inv.gemm_rank(X, W, r, c) for r in range(R)])
         assert bitwise_equal(inv.tree_combine(P, c), base), f"gemm_rank ranks={R}"
     # per-leaf launches replayed by the combine
+    P8 = inv.gemm_leaves(X, W, 0, 8, inv.contract(leaves=8, out="fp32"))
+    assert bitwise_equal(inv.tree_combine(P8, inv.contract(leaves=8)), base)
+
+
+@pytest.mark.parametrize("M", [65, 300])
+def test_odd_leaf_rank_partitions_are_bitwise_equal(inv, M):
+    """K = 768, 8 leaves of 96: ranks 1, 2 and 4 run their leaves as 32-wide
+    substeps of 64-k stages, ranks 8 (one leaf a launch) on 32-k stages; the
+    chain per element is the same, so the bits are."""
+    X = synth.randn((M, 768), 111).to(DEV)
+    W = synth.randn((256, 768), 112, 0.02).to(DEV)
+    base = inv.gemm(X, W, inv.contract(leaves=8, ranks=1))
+    for R in (2, 4, 8):
+        c = inv.contract(leaves=8, ranks=R)
+        P = torch.stack([inv.gemm_rank(X, W, r, c) for r in range(R)])
+        assert bitwise_equal(inv.tree_combine(P, c), base), f"gemm_rank ranks={R}"
     P8 = inv.gemm_leaves(X, W, 0, 8, inv.contract(leaves=8, out="fp32"))
     assert bitwise_equal(inv.tree_combine(P8, inv.contract(leaves=8)), base)
 
