@@ -223,7 +223,7 @@ inv_status inv_sha256(const void* data, size_t bytes, uint8_t digest[32]);
  * partials (ws_bytes >= inv_workspace_bytes(INV_OP_GEMM)), and the top
  * log2(R) tree levels finish the sum. The result is bitwise identical for
  * every proven R. tree must be BALANCED.
- * ranks == 1: the workspace is optional. For 64 < M with too few 128 x 128
+ * ranks == 1: the workspace is optional. For M >= 8 with too few 128 x 128
  * output tiles to fill the chip (tiles * G <= 256), inv_workspace_bytes
  * reports G*M*N*4 bytes; given that much, G aligned subtrees are reduced in
  * parallel and combined by the same tree (bitwise the same result as without

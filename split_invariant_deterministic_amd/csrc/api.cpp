@@ -83,7 +83,8 @@ inv_status check_logprob_contract(const inv_contract* c, int64_t V) {
 bool out_is_bf16(const inv_contract* c) { return c->out_dtype == INV_BF16; }
 
 // Leaf groups for the single-rank GEMM when 128 x 128 tiles alone leave
-// compute units idle (64 < M): G aligned subtrees of L/G leaves each are
+// compute units idle (M >= 8; below 8 rows the stream kernel reads the
+// weights fastest in one pass): G aligned subtrees of L/G leaves each are
 // reduced by separate workgroups into a workspace and the top log2(G) tree
 // levels finish the sum. Every subtree is a node of the same balanced tree,
 // so the bits equal the single-pass kernel's. A tile's time is set by its K
@@ -91,7 +92,7 @@ bool out_is_bf16(const inv_contract* c) { return c->out_dtype == INV_BF16; }
 // workgroup per compute unit on MI355X); measured best on 4096-12288 wide
 // projections.
 int gemm_split_groups(const inv_contract* c, int64_t M, int64_t N) {
-  if (c->ranks != 1 || M <= 64) return 1;
+  if (c->ranks != 1 || M < 8) return 1;
   const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
   int G = 1;
   while (G < (int)c->leaves && tiles * G * 2 <= 256) G *= 2;

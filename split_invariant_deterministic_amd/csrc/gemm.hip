@@ -910,7 +910,11 @@ hipError_t launch_gemm(const GemmLaunch& g, hipStream_t s) {
     return g.out_bf16 ? ring_dispatch<kOutBF16, true>(p, grid, g.nl, s)
                       : ring_dispatch<kOutF32, true>(p, grid, g.nl, s);
   }
-  if (g.M <= 64 && g.K < (int64_t{1} << 25)) {  // stream kernel: 32-bit buffer offsets
+  // Stream kernel for M <= 64 (32-bit buffer offsets), except a launch split
+  // into leaf groups with at least 8 rows: there the ring kernel with G
+  // groups streams the weights faster (measured: M = 8..64 at 4096 x 12288 and
+  // 12288 x 4096 in 20-30 us against 21-71 us).
+  if (g.M <= 64 && (g.groups == 1 || g.M < 8) && g.K < (int64_t{1} << 25)) {
     const int fm = (int)((g.M + 15) / 16);
     // each wave owns one leaf; groups of nl leaves become nl waves per WG
     dim3 grid((unsigned)((g.N + 15) / 16), 1u, (unsigned)g.groups);

@@ -76,7 +76,8 @@ def test_contract_violations():
 
 def test_workspace_sizes():
     inv = _inv()
-    assert inv.workspace_bytes(inv.contract(ranks=1), inv.OP_GEMM, 64, 128, 4096) == 0
+    assert inv.workspace_bytes(inv.contract(ranks=1), inv.OP_GEMM, 7, 128, 4096) == 0   # stream kernel, M < 8
+    assert inv.workspace_bytes(inv.contract(ranks=1), inv.OP_GEMM, 64, 128, 4096) == 8 * 64 * 128 * 4  # 1 tile
     assert inv.workspace_bytes(inv.contract(ranks=1), inv.OP_GEMM, 4096, 12288, 4096) == 0
     # few 128x128 tiles: optional leaf groups (32 tiles x 8 groups at M=128, N=4096)
     assert inv.workspace_bytes(inv.contract(ranks=1), inv.OP_GEMM, 128, 4096, 12288) == 8 * 128 * 4096 * 4
