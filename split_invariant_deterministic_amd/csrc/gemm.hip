@@ -175,18 +175,31 @@ struct Ring {
   static __device__ __forceinline__ int off(int r, int c) { return r * ROWB + (slot(r, c) << 4); }
 };
 
-// s_waitcnt vmcnt(n) lgkmcnt(0) for n = PER * rem, rem <= MAXR (immediate operand)
+// s_waitcnt vmcnt(n) for n = PER * rem, rem <= R (an immediate operand, hence the recursion)
 template <int PER, int R>
-__device__ __forceinline__ void wait_vm_rem(int rem) {
+__device__ __forceinline__ void wait_vm_only(int rem) {
   if constexpr (R < 0) {
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   } else {
     if (rem >= R) {
-      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(PER * R) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER * R) : "memory");
     } else {
-      wait_vm_rem<PER, R - 1>(rem);
+      wait_vm_only<PER, R - 1>(rem);
     }
   }
+}
+
+// lgkmcnt(0), then vmcnt(PER * rem). The LDS wait goes through the builtin
+// on every path, so the compiler knows that every fragment read issued so
+// far has landed; with the wait hidden in inline asm it waited again for
+// all LDS reads after the barrier, including the next stage's prefetch,
+// before the first MFMA of the second k substep. The empty asm keeps
+// earlier memory operations from sinking below the wait.
+template <int PER, int R>
+__device__ __forceinline__ void wait_vm_rem(int rem) {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt(63) and expcnt(7) wait for nothing
+  wait_vm_only<PER, R>(rem);
 }
 
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
