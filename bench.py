@@ -16,6 +16,12 @@ synthetic input, every stage in the library's HIP kernels:
           selected-token logprob, 4096 tokens; the fused LM head (logprob
           from 16-column blocks in the GEMM epilogue, no stored logits) is
           timed beside the step, not inside it
+  sweep   outside the step, median of 20 launches each: the dense pair at
+          M = 1, 7, 64, 512 (prefixes; warm, and rotated over three weight
+          copies so the 201 MB never sits in the 256 MB Infinity Cache), next
+          to hipBLASLt and the 1-leaf kernel; RMSNorm latency at M = 1 ..
+          4096; attention at B = 1, 8, 64 (prefixes of the 256 sequences);
+          the MoE layer run as 4 and 16 contiguous token splits; a 1 GiB copy
 
 Inputs are resident in HBM before the timed region. ``value`` is the
 invariant GEMM throughput of the dense stage (its FLOPs over the time of its
@@ -48,8 +54,8 @@ def parse():
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--stages", default="dense,norm,attn,moe,lmhead,gdn",
-                   help="comma list of dense,norm,attn,moe,lmhead,gdn (the whole path by default); "
+    p.add_argument("--stages", default="dense,norm,attn,moe,lmhead,gdn,sweep",
+                   help="comma list of dense,norm,attn,moe,lmhead,gdn,sweep (all by default); "
                         "'copy' adds a plain 1 GiB device copy used only to calibrate traffic counters")
     return p.parse_args()
 
@@ -76,6 +82,121 @@ class Timer:
 
     def reset(self):
         self.ev = {}
+
+
+_SLEEP = {"cycles": 0}
+
+
+def median_us(torch, fn, iters=20, warm=5):
+    """Median GPU time of one call of ``fn`` over ``iters`` back-to-back calls,
+    after ``warm`` untimed ones. A spin kernel keeps the GPU busy while the host
+    enqueues the calls, and an event sits between every two calls, so host-side
+    marshalling (several µs per call) never shows up as GPU time; the spin is
+    lengthened until the host has finished enqueueing before it ends."""
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    if not _SLEEP["cycles"]:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.cuda._sleep(1 << 20)
+        e1.record()
+        torch.cuda.synchronize()
+        _SLEEP["cycles"] = int((1 << 20) * 2000.0 / max(e0.elapsed_time(e1) * 1e3, 1.0))  # about 2 ms
+    for _ in range(4):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+        e_s = torch.cuda.Event(enable_timing=True)
+        e_s.record()
+        torch.cuda._sleep(_SLEEP["cycles"])
+        h0 = time.perf_counter()
+        ev[0].record()
+        for i in range(iters):
+            fn()
+            ev[i + 1].record()
+        host_us = (time.perf_counter() - h0) * 1e6
+        torch.cuda.synchronize()
+        if host_us < 0.8 * e_s.elapsed_time(ev[0]) * 1e3:
+            break
+        _SLEEP["cycles"] *= 2  # the host was still enqueueing when the spin ended: spin longer
+    t = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(iters))
+    return t[len(t) // 2]
+
+
+def sweep(torch, inv, synth, X, W_up, W_down, gamma, att, moe, c8, cn, ca, dev):
+    """The shape lists of the measurement plan, each kernel at its own roofline."""
+    import torch.nn.functional as F
+    out = {}
+    Hd, Ff = W_up.shape[1], W_up.shape[0]
+    # dense pair at small M: HBM-bound on the 201 MB of weights up to M = 64
+    sets = [(W_up, W_down), (W_up.clone(), W_down.clone()), (W_up.clone(), W_down.clone())]
+    dn = {}
+    for M in (1, 7, 64, 512):
+        x = X[:M]
+        a = torch.empty((M, Ff), dtype=torch.bfloat16, device=dev)
+        b = torch.empty((M, Hd), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(max(inv.workspace_bytes(c8, inv.OP_GEMM, M, Ff, Hd),
+                             inv.workspace_bytes(c8, inv.OP_GEMM, M, Hd, Ff), 1), dtype=torch.uint8, device=dev)
+        rot = [0]
+
+        def inv_pair(i=None, c=c8):
+            wu, wd = sets[rot[0] % 3] if i is None else sets[i]
+            rot[0] += 1
+            inv.gemm(x, wu, c, out=a, ws=ws)
+            inv.gemm(a, wd, c, out=b, ws=ws)
+
+        def fast_pair(i=None):
+            wu, wd = sets[rot[0] % 3] if i is None else sets[i]
+            rot[0] += 1
+            torch.matmul(torch.matmul(x, wu.t()), wd.t())
+
+        t = {"inv_warm": median_us(torch, lambda: inv_pair(0)), "inv_rotated": median_us(torch, inv_pair),
+             "leaves1_warm": median_us(torch, lambda: inv_pair(0, cn)),
+             "hipblaslt_warm": median_us(torch, lambda: fast_pair(0)), "hipblaslt_rotated": median_us(torch, fast_pair)}
+        byt = 2.0 * (M * Hd + Ff * Hd + M * Ff) + 2.0 * (M * Ff + Hd * Ff + M * Hd)
+        fl = 2.0 * M * (Hd * Ff + Ff * Hd)
+        r = {k: round(v, 2) for k, v in t.items()}
+        r["inv_rotated_pct_hbm"] = round(100 * byt / (t["inv_rotated"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 1)
+        r["inv_warm_tflops"] = round(fl / (t["inv_warm"] * 1e-6) / 1e12, 1)
+        r["overhead_vs_hipblaslt_rotated"] = round(t["inv_rotated"] / t["hipblaslt_rotated"] - 1.0, 3)
+        dn[f"M={M}"] = r
+    out["gemm_dense_pair_us"] = dn
+    del sets
+    # RMSNorm latency at the dense batch sizes
+    out["rmsnorm_us"] = {f"M={M}": round(median_us(torch, lambda: inv.rmsnorm(X[:M], gamma, cn)), 2)
+                         for M in (1, 7, 64, 512, 4096)}
+    # decode attention at batch prefixes (the same 16 splits at every B)
+    if att is not None:
+        ar = {}
+        cu = att["cu_seqlens"]
+        for B in (1, 8, 64):
+            L = int(cu[B])
+            q = att["q"][:B]
+            wsb = inv.attn_workspace(q, ca)
+            us = median_us(torch, lambda: inv.decode_attn(q, att["k"][:L], att["v"][:L], cu[:B + 1], att["q_seq"][:B],
+                                                          att["q_pos"][:B], ca, ws=wsb))
+            ar[f"B={B}"] = {"us": round(us, 2), "kv_tokens": L,
+                            "pct_hbm": round(100 * 4096.0 * L / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 1)}
+        out["decode_attn"] = ar
+    # the MoE layer over contiguous token splits (weights re-read per split)
+    if moe is not None:
+        T = moe["x"].shape[0]
+        mr = {}
+        for S in (4, 16):
+            n = T // S
+
+            def split_layer():
+                for i in range(S):
+                    inv.moe_layer(moe["x"][i * n:(i + 1) * n], moe["logits"][i * n:(i + 1) * n],
+                                  moe["W1"], moe["W2"], c8, c8)
+            mr[f"splits={S}"] = round(median_us(torch, split_layer, iters=10, warm=2) / 1e3, 4)
+        out["moe_ms"] = mr
+    # copy ceiling (context for the HBM-bound rows)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    cus = median_us(torch, lambda: dst.copy_(src), iters=10, warm=2)
+    out["copy_1GiB_gbs"] = round(2.0 * (1 << 30) / (cus * 1e-6) / 1e9, 1)
+    del src, dst
+    return out
 
 
 def cpu_baseline(dense_X, W_up, W_down, target_s=15.0):
@@ -295,6 +416,13 @@ def main():
         del g_ws, gd, g_cache
         log("CPR Gated DeltaNet timed")
 
+    # ------------------------------------------------------------ shape sweep (outside the step)
+    sw = None
+    if "sweep" in stages:
+        sw = sweep(torch, inv, synth, X, W_up, W_down, gamma, att if "attn" in stages else None,
+                   moe if "moe" in stages else None, c8, cn, ca if "attn" in stages else None, dev)
+        log("shape sweep done")
+
     # ------------------------------------------------------------ fast paths
     Tf = Timer(torch)
     fast = {}
@@ -414,6 +542,8 @@ def main():
         add("moe layer 8192 tokens", "mfma", 2.0 * 8192 * 8 * (1536 * 2048 + 2048 * 768), ms["moe"],
             PEAK_BF16_TFLOPS, "TFLOP/s")
     result["rooflines"] = rl
+    if sw is not None:
+        result["sweep"] = sw
     result["stage_ms"] = {k: round(v, 4) for k, v in ms.items()}
     result["fast_ms"] = {k: round(v, 4) for k, v in fast.items()}
     result["overhead_vs_fast"] = {k: round(v, 3) for k, v in overhead.items()}
