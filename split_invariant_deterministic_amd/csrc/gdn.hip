@@ -240,7 +240,8 @@ __device__ void chunk_coeffs(ChunkLds<C>& L, const Tc& T) {
 // block takes register q as the B operand (rows 16 ib + 4 g + q for the four
 // lane groups g) and the matching A columns, so nothing is transposed.
 constexpr int kWC = 16;                      // state columns per wave
-constexpr int kStateWaves = 2;               // waves per state workgroup
+constexpr int kStateWaves = 4;               // waves per state workgroup: with two, pairs of
+                                             // waves could share a SIMD's MFMA unit
 constexpr int kSB = kWC * kStateWaves;       // state columns per workgroup
 constexpr int kSKStride = kD + 4;            // K rows: 16-byte aligned, 16 rows cover the 64 banks
 template <int C>
@@ -271,14 +272,18 @@ __device__ __forceinline__ void chunk_state(f32x4 (&S)[8], const StateLds<C>& L,
   f32x4 P[TB];
 #pragma unroll
   for (int tb = 0; tb < TB; ++tb) P[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Each P[tb] is its own chain over (ib, q) ascending; the TB chains are
+  // interleaved so that consecutive MFMAs never wait on each other.
 #pragma unroll
-  for (int ib = 0; ib < 8; ++ib)
+  for (int ib = 0; ib < 8; ++ib) {
+    f32x4 k4[TB];
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
-      const f32x4 k4 = *reinterpret_cast<const f32x4*>(&L.K[16 * tb + c16][16 * ib + 4 * g]);
+    for (int tb = 0; tb < TB; ++tb) k4[tb] = *reinterpret_cast<const f32x4*>(&L.K[16 * tb + c16][16 * ib + 4 * g]);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) P[tb] = mfma4(k4[q], S[ib][q], P[tb]);
-    }
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) P[tb] = mfma4(k4[tb][q], S[ib][q], P[tb]);
+  }
   f32x4 R[TB];
 #pragma unroll
   for (int tb = 0; tb < TB; ++tb)
@@ -288,13 +293,15 @@ __device__ __forceinline__ void chunk_state(f32x4 (&S)[8], const StateLds<C>& L,
 #pragma unroll
   for (int tb = 0; tb < TB; ++tb) W[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int sb = 0; sb < TB; ++sb)
+  for (int sb = 0; sb < TB; ++sb) {
+    f32x4 m4[TB];
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
-      const f32x4 m4 = *reinterpret_cast<const f32x4*>(&L.M[16 * tb + c16][16 * sb + 4 * g]);
+    for (int tb = 0; tb < TB; ++tb) m4[tb] = *reinterpret_cast<const f32x4*>(&L.M[16 * tb + c16][16 * sb + 4 * g]);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) W[tb] = mfma4(m4[q], R[sb][q], W[tb]);
-    }
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) W[tb] = mfma4(m4[tb][q], R[sb][q], W[tb]);
+  }
   const float glast = L.gamma[C - 1];
 #pragma unroll
   for (int ib = 0; ib < 8; ++ib)
@@ -347,25 +354,34 @@ __device__ __forceinline__ void store_cols(const f32x4 (&S)[8], float* __restric
 // every global load issued before the first LDS write; the lane's own v
 // (C token rows at vbase, tok_stride elements apart, bf16 or fp32) goes to
 // registers. coef: the chunk's [M (C x C) | gamma (C) | cf (C)].
+template <int C>
+struct StateRegs {
+  static constexpr int NT = 64 * kStateWaves;
+  static constexpr int PK = C * kD / 4 / NT, PM = C * C / 4 / NT;
+  f32x4 kr[PK], mr[PM];
+  float v[C / 16][4];
+  float gc;
+};
+
+// Issue the chunk's loads into registers (nothing waits for them here).
 template <int C, typename VT>
-__device__ __forceinline__ void state_inputs(StateLds<C>& L, const float* __restrict__ coef,
-                                             const float* __restrict__ kbase, const VT* __restrict__ vbase,
-                                             int64_t tok_stride, float (&v)[C / 16][4], int tid, int c0) {
-  constexpr int NT = 64 * kStateWaves;
-  constexpr int PK = C * kD / 4 / NT, PM = C * C / 4 / NT;
+__device__ __forceinline__ void state_load(StateRegs<C>& R, const float* __restrict__ coef,
+                                           const float* __restrict__ kbase, const VT* __restrict__ vbase,
+                                           int64_t tok_stride, int tid, int c0) {
+  constexpr int NT = StateRegs<C>::NT, PK = StateRegs<C>::PK, PM = StateRegs<C>::PM;
   static_assert(NT % (kD / 4) == 0, "a thread keeps its k^ column across loads");
+  static_assert(NT >= 2 * C, "one thread per gamma and cf entry");
   const int lane = tid & 63, g = lane >> 4, c16 = lane & 15;
   const uint32_t ts = (uint32_t)tok_stride;
   const buf_rsrc rk = make_rsrc(kbase, (uint32_t)(((C - 1) * tok_stride + kD) * 4));
   const buf_rsrc rc = make_rsrc(coef, (uint32_t)((C * C + 2 * C) * 4));
   const buf_rsrc rv = make_rsrc(vbase, (uint32_t)(((C - 1) * tok_stride + kD) * sizeof(VT)));
   const int tk = tid / (kD / 4), i4 = 4 * (tid % (kD / 4));  // token row and column of load u = 0
-  f32x4 kr[PK], mr[PM];
 #pragma unroll
   for (int u = 0; u < PK; ++u)
-    kr[u] = bload4(rk, (uint32_t)((tk * ts + i4) * 4), (uint32_t)(u * (NT / (kD / 4)) * ts * 4));
+    R.kr[u] = bload4(rk, (uint32_t)((tk * ts + i4) * 4), (uint32_t)(u * (NT / (kD / 4)) * ts * 4));
 #pragma unroll
-  for (int u = 0; u < PM; ++u) mr[u] = bload4(rc, (uint32_t)(tid * 16), (uint32_t)(u * NT * 16));
+  for (int u = 0; u < PM; ++u) R.mr[u] = bload4(rc, (uint32_t)(tid * 16), (uint32_t)(u * NT * 16));
   const uint32_t vo = (uint32_t)((4 * g * ts + c0 + c16) * sizeof(VT));
 #pragma unroll
   for (int tb = 0; tb < C / 16; ++tb)
@@ -373,23 +389,43 @@ __device__ __forceinline__ void state_inputs(StateLds<C>& L, const float* __rest
     for (int r = 0; r < 4; ++r) {
       const uint32_t so = (uint32_t)((16 * tb + r) * ts * sizeof(VT));
       if constexpr (sizeof(VT) == 2)
-        v[tb][r] = bf16_bits_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rv, vo, so, 0));
+        R.v[tb][r] = bf16_bits_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rv, vo, so, 0));
       else
-        v[tb][r] = bload(rv, vo, so);
+        R.v[tb][r] = bload(rv, vo, so);
     }
-  float gc = 0.0f;
-  if (tid < 2 * C) gc = bload(rc, (uint32_t)((C * C + tid) * 4), 0u);  // gamma then cf
+  R.gc = 0.0f;
+  if (tid < 2 * C) R.gc = bload(rc, (uint32_t)((C * C + tid) * 4), 0u);  // gamma then cf
+}
+
+// Publish loaded inputs in LDS: k^ rows, M, gamma and cf.
+template <int C>
+__device__ __forceinline__ void state_commit(StateLds<C>& L, const StateRegs<C>& R, int tid) {
+  constexpr int NT = StateRegs<C>::NT, PK = StateRegs<C>::PK, PM = StateRegs<C>::PM;
+  const int tk = tid / (kD / 4), i4 = 4 * (tid % (kD / 4));
   __syncthreads();  // every wave is done with the previous chunk's LDS
 #pragma unroll
-  for (int u = 0; u < PK; ++u) *reinterpret_cast<f32x4*>(&L.K[tk + u * (NT / (kD / 4))][i4]) = kr[u];
+  for (int u = 0; u < PK; ++u) *reinterpret_cast<f32x4*>(&L.K[tk + u * (NT / (kD / 4))][i4]) = R.kr[u];
 #pragma unroll
   for (int u = 0; u < PM; ++u) {
     const int e = tid + NT * u;
-    *reinterpret_cast<f32x4*>(&L.M[e / (C / 4)][4 * (e % (C / 4))]) = mr[u];
+    *reinterpret_cast<f32x4*>(&L.M[e / (C / 4)][4 * (e % (C / 4))]) = R.mr[u];
   }
-  if (tid < C) L.gamma[tid] = gc;
-  else if (tid < 2 * C) L.cf[tid - C] = gc;
+  if (tid < C) L.gamma[tid] = R.gc;
+  else if (tid < 2 * C) L.cf[tid - C] = R.gc;
   __syncthreads();
+}
+
+template <int C, typename VT>
+__device__ __forceinline__ void state_inputs(StateLds<C>& L, const float* __restrict__ coef,
+                                             const float* __restrict__ kbase, const VT* __restrict__ vbase,
+                                             int64_t tok_stride, float (&v)[C / 16][4], int tid, int c0) {
+  StateRegs<C> R;
+  state_load<C>(R, coef, kbase, vbase, tok_stride, tid, c0);
+  state_commit<C>(L, R, tid);
+#pragma unroll
+  for (int tb = 0; tb < C / 16; ++tb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[tb][r] = R.v[tb][r];
 }
 
 // The coefficient phase's inputs into LDS: every global load issued before
@@ -542,12 +578,22 @@ __global__ __launch_bounds__(64 * kStateWaves) __attribute__((amdgpu_waves_per_e
 #pragma unroll
   for (int ib = 0; ib < 8; ++ib) S[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
   store_cols(S, a.bstates + (base * a.H + h) * plane, c0, lane);
-  for (int64_t j = 0; j < n; ++j) {
+  // Chunk j+1's inputs are loaded into registers while chunk j is computed.
+  auto load = [&](StateRegs<C>& R, int64_t j) {
     const int64_t tc0 = t0 + j * C;
-    const float* coef = a.coef + ((base + j) * a.H + h) * (int64_t)(C * C + 2 * C);
+    state_load<C>(R, a.coef + ((base + j) * a.H + h) * (int64_t)(C * C + 2 * C), a.kh + (tc0 * a.H + h) * kD,
+                  a.v + (tc0 * a.H + h) * kD, (int64_t)a.H * kD, tid, c0);
+  };
+  StateRegs<C> nx;
+  if (n > 0) load(nx, 0);
+  for (int64_t j = 0; j < n; ++j) {
+    state_commit<C>(L, nx, tid);
     float v[C / 16][4];
-    state_inputs<C>(L, coef, a.kh + (tc0 * a.H + h) * kD, a.v + (tc0 * a.H + h) * kD, (int64_t)a.H * kD, v, tid,
-                    c0);
+#pragma unroll
+    for (int tb = 0; tb < C / 16; ++tb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[tb][r] = nx.v[tb][r];
+    if (j + 1 < n) load(nx, j + 1);
     chunk_state<C>(S, L, v, lane);
     store_cols(S, a.bstates + ((base + j + 1) * a.H + h) * plane, c0, lane);
   }
