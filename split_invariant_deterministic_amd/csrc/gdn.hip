@@ -712,6 +712,13 @@ __global__ __launch_bounds__(256) void gdn_decode_step_kernel(GdnDecodeArgs a) {
   }
   const int slot = (int)(pos % C);
   const CacheView cv = cache_view(a.cache, bseq, a.H, C);
+  const int64_t plane = (int64_t)kD * kD;
+  // the state and v loads go out first, so their latency overlaps the token's preparation
+  float S[8][8];
+  load_state(S, cv.srun + h * plane, T);
+  float k8[8], q8[8], v8[8], o8[8];
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) v8[jj] = bf16_bits_to_f32(a.v[r + 8 * T.tj + jj]);
   if (T.tid < 64) {
     const float2 kk = l2norm_pair(reinterpret_cast<const uint32_t*>(a.k)[r / 2 + T.lane], 1.0f);
     const float2 qq = l2norm_pair(reinterpret_cast<const uint32_t*>(a.q)[r / 2 + T.lane], kInvSqrtD);
@@ -725,17 +732,11 @@ __global__ __launch_bounds__(256) void gdn_decode_step_kernel(GdnDecodeArgs a) {
     }
   }
   __syncthreads();
-  const int64_t plane = (int64_t)kD * kD;
-  float S[8][8];
-  load_state(S, cv.srun + h * plane, T);
-  float k8[8], q8[8], v8[8], o8[8];
 #pragma unroll
   for (int ii = 0; ii < 8; ++ii) {
     k8[ii] = kq[0][8 * T.ti + ii];
     q8[ii] = kq[1][8 * T.ti + ii];
   }
-#pragma unroll
-  for (int jj = 0; jj < 8; ++jj) v8[jj] = bf16_bits_to_f32(a.v[r + 8 * T.tj + jj]);
   rec_step(S, k8, q8, v8, ab[0], ab[1], o8);
   store_out<OUT_BF16>(a.out, r, o8, T);
   store_state(S, cv.srun + h * plane, T);
