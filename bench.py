@@ -21,7 +21,8 @@ synthetic input, every stage in the library's HIP kernels:
           copies so the 201 MB never sits in the 256 MB Infinity Cache), next
           to hipBLASLt and the 1-leaf kernel; RMSNorm latency at M = 1 ..
           4096; attention at B = 1, 8, 64 (prefixes of the 256 sequences);
-          the MoE layer run as 4 and 16 contiguous token splits; a 1 GiB copy
+          the MoE layer run as 4 and 16 contiguous token splits; the LM head +
+          logprob at M = 1 and 64 (fused, unfused and the fast path); a 1 GiB copy
 
 Inputs are resident in HBM before the timed region. ``value`` is the
 invariant GEMM throughput of the dense stage (its FLOPs over the time of its
@@ -122,7 +123,7 @@ def median_us(torch, fn, iters=20, warm=5):
     return t[len(t) // 2]
 
 
-def sweep(torch, inv, synth, X, W_up, W_down, gamma, att, moe, c8, cn, ca, dev):
+def sweep(torch, inv, synth, X, W_up, W_down, gamma, att, moe, lm, c8, cn, ca, dev):
     """The shape lists of the measurement plan, each kernel at its own roofline."""
     import torch.nn.functional as F
     out = {}
@@ -190,6 +191,34 @@ def sweep(torch, inv, synth, X, W_up, W_down, gamma, att, moe, c8, cn, ca, dev):
                                   moe["W1"], moe["W2"], c8, c8)
             mr[f"splits={S}"] = round(median_us(torch, split_layer, iters=10, warm=2) / 1e3, 4)
         out["moe_ms"] = mr
+    # LM head + selected-token logprob at small batch: HBM-bound on the 1.24 GB vocabulary matrix
+    if lm is not None:
+        W, V = lm["W"], lm["W"].shape[0]
+        c8f, c64 = inv.contract(leaves=8, out="fp32"), inv.contract(leaves=64)
+        lr = {}
+        for M in (1, 64):
+            h, tg = lm["h"][:M], lm["targets"][:M]
+            logits = torch.empty((M, V), dtype=torch.float32, device=dev)
+            ws = inv.block16_workspace(M, V, dev)
+            gws = torch.empty(max(inv.workspace_bytes(c8f, inv.OP_GEMM, M, V, W.shape[1]), 1), dtype=torch.uint8,
+                              device=dev)
+
+            def unfused():
+                inv.gemm(h, W, c8f, out=logits, ws=gws)
+                inv.logprob(logits, tg, c64)
+
+            def fast():
+                torch.log_softmax(torch.matmul(h, W.t()).float(), -1).gather(1, tg.long()[:, None])
+            t = {"unfused": median_us(torch, unfused, iters=10, warm=3),
+                 "fused": median_us(torch, lambda: inv.lmhead_logprob(h, W, tg, c8f, ws=ws), iters=10, warm=3),
+                 "fast_path": median_us(torch, fast, iters=10, warm=3)}
+            wbytes = 2.0 * V * W.shape[1]
+            r = {k: round(v, 1) for k, v in t.items()}
+            r["fused_pct_hbm"] = round(100 * wbytes / (t["fused"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 1)
+            r["fused_tokens_per_s"] = round(M / (t["fused"] * 1e-6), 1)
+            lr[f"M={M}"] = r
+            del logits, ws, gws
+        out["lmhead_logprob_us"] = lr
     # copy ceiling (context for the HBM-bound rows)
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
@@ -420,7 +449,8 @@ def main():
     sw = None
     if "sweep" in stages:
         sw = sweep(torch, inv, synth, X, W_up, W_down, gamma, att if "attn" in stages else None,
-                   moe if "moe" in stages else None, c8, cn, ca if "attn" in stages else None, dev)
+                   moe if "moe" in stages else None, lm if "lmhead" in stages else None, c8, cn,
+                   ca if "attn" in stages else None, dev)
         log("shape sweep done")
 
     # ------------------------------------------------------------ fast paths

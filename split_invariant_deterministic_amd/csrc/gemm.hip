@@ -923,11 +923,15 @@ hipError_t launch_gemm(const GemmLaunch& g, hipStream_t s) {
     return g.out_bf16 ? ring_dispatch<kOutBF16, true>(p, grid, g.nl, s)
                       : ring_dispatch<kOutF32, true>(p, grid, g.nl, s);
   }
-  // Stream kernel for M <= 64 (32-bit buffer offsets), except a launch split
-  // into leaf groups with at least 8 rows: there the ring kernel with G
-  // groups streams the weights faster (measured: M = 8..64 at 4096 x 12288 and
-  // 12288 x 4096 in 20-30 us against 21-71 us).
-  if (g.M <= 64 && (g.groups == 1 || g.M < 8) && g.K < (int64_t{1} << 25)) {
+  // Stream kernel below 8 rows, and up to 16 rows when the ring kernel would
+  // run fewer than 256 whole-K tiles; the ring kernel everywhere else. The
+  // stream kernel re-reads A per wave, so its time grows with M, while a ring
+  // tile costs the same up to 128 rows (measured, 8 leaves, K = 4096:
+  // 4096 x 12288 without leaf groups 25.7 / 28.2 / 39.4 / 63.0 us at M = 8 /
+  // 16 / 32 / 64 against 33-35 us on the ring; the 4096 x 151936 LM head 271 /
+  // 323 / 470 / 787 us against 259-286 us).
+  const int64_t ring_tiles = ((g.M + 127) / 128) * ((g.N + 127) / 128) * g.groups;
+  if ((g.M < 8 || (g.M <= 16 && g.groups == 1 && ring_tiles < 256)) && g.K < (int64_t{1} << 25)) {
     const int fm = (int)((g.M + 15) / 16);
     // each wave owns one leaf; groups of nl leaves become nl waves per WG
     dim3 grid((unsigned)((g.N + 15) / 16), 1u, (unsigned)g.groups);
