@@ -487,6 +487,20 @@ inv_status inv_moe_gemm(const inv_contract* c, const void* X, int64_t x_rows, co
                         const int32_t* offsets, const void* W, void* Y, int64_t R, int32_t E,
                         int64_t N, int64_t K, hipStream_t stream);
 
+/* Gate/up grouped GEMM with the SwiGLU fused into its epilogue (the
+ * pages' MoE FFN: packed gate/up projection, SwiGLU, down projection; the
+ * elementwise step is done where the GEMM holds its outputs, so the [R, 2F]
+ * gate/up tensor never reaches memory). W [E, 2F, K] bf16 holds each
+ * expert's gate rows then its up rows; Aout [R, F] bf16. Aout is bitwise
+ * inv_swiglu of what inv_moe_gemm would write for the same arguments with
+ * N = 2F and a bf16 out_dtype (the contract's out_dtype is not used): every
+ * gate and up value is rounded to bf16 first. Rows, offsets, the contract
+ * and the clamping of malformed tables are as for inv_moe_gemm; one
+ * expert's 2F x K weights must span fewer than 2^32 bytes. ranks must be 1. */
+inv_status inv_moe_gemm_swiglu(const inv_contract* c, const void* X, int64_t x_rows, const int32_t* rows,
+                               const int32_t* offsets, const void* W, void* Aout, int64_t R, int32_t E,
+                               int64_t F, int64_t K, hipStream_t stream);
+
 /* SwiGLU on a packed [gate | up] row: a = bf16( silu(g) * u ) with
  * silu(g) = g / (1 + exp(-g)), g and u read as bf16, math fp32.
  * GU [R, 2F] bf16, Aout [R, F] bf16. */

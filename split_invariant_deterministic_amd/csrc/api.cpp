@@ -615,6 +615,31 @@ inv_status inv_moe_gemm(const inv_contract* c, const void* X, int64_t x_rows, co
   return hip_status(inv::launch_gemm(g, stream));
 }
 
+inv_status inv_moe_gemm_swiglu(const inv_contract* c, const void* X, int64_t x_rows, const int32_t* rows,
+                               const int32_t* offsets, const void* W, void* Aout, int64_t R, int32_t E, int64_t F,
+                               int64_t K, hipStream_t stream) {
+  inv_status s = check_gemm_contract(c, K);
+  if (s != INV_OK) return s;
+  if (c->ranks != 1) return INV_E_TOPOLOGY;
+  if (R < 0 || F < 0 || E <= 0 || x_rows < 0) return INV_E_ARG;
+  if (E > 65536 || R > ((int64_t)1 << 31) - 1) return INV_E_UNSUPPORTED;
+  if (rows && x_rows * K * 2 > ((int64_t)1 << 32) - 1) return INV_E_UNSUPPORTED;
+  // one expert's [gate; up] rows are addressed by 32-bit byte offsets
+  if (2 * F * K * 2 > ((int64_t)1 << 32) - 1) return INV_E_UNSUPPORTED;
+  if (R == 0 || F == 0) return INV_OK;
+  if (!X || !offsets || !W || !Aout) return INV_E_ARG;
+  if (!rows && x_rows < R) return INV_E_ARG;
+  if ((reinterpret_cast<uintptr_t>(X) | reinterpret_cast<uintptr_t>(W)) & 15u) return INV_E_ARG;
+  inv::GemmLaunch g = gemm_launch(X, W, Aout, R, 2 * F, K, (int)(K / c->leaves), 0, (int)c->leaves, 1, true);
+  g.rows = rows;
+  g.offsets = offsets;
+  g.E = E;
+  g.a_rows = x_rows;
+  g.b_expert_stride = 2 * F * K;
+  g.swiglu = true;
+  return hip_status(inv::launch_gemm(g, stream));
+}
+
 inv_status inv_swiglu(const inv_contract* c, const void* GU, void* Aout, int64_t R, int64_t F, hipStream_t stream) {
   inv_status s = check_contract(c);
   if (s != INV_OK) return s;

@@ -53,6 +53,16 @@ __device__ __forceinline__ float exp_shifted(float x, float m) {
   return exp2_hw(t);
 }
 
+// SwiGLU of one element: silu(g) * u with silu(g) = g / (1 + exp(-g)), in
+// fp32, exp as exp2(-g * log2e). The MoE SwiGLU kernels and the gate/up
+// GEMM's fused epilogue both call this, so the two paths agree bit for bit.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  const float t = -g * kLog2e;
+  const float den = 1.0f + exp2_hw(t);
+  const float s = g / den;
+  return s * u;
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   __bf16 h = (__bf16)f;
   return __builtin_bit_cast(uint16_t, h);

@@ -90,9 +90,11 @@ struct TileParams {
   const int32_t* lp_target;  // [M]
 };
 
-// Output modes of the GEMM kernels: fp32 C, bf16 C, or (LM head) no C at all
-// but the vocabulary-block statistics of each row and its target's logit.
-constexpr int kOutF32 = 0, kOutBF16 = 1, kOutLP = 2;
+// Output modes of the GEMM kernels: fp32 C, bf16 C, (LM head) no C at all
+// but the vocabulary-block statistics of each row and its target's logit, or
+// (MoE gate/up, grouped launches) the SwiGLU of each gate column with its up
+// column.
+constexpr int kOutF32 = 0, kOutBF16 = 1, kOutLP = 2, kOutSwiGLU = 3;
 
 // kOutLP epilogue. A wave's fp32 result block (rows x 16*cols, in the MFMA
 // output layout) is transposed through LDS so that lane l holds row l's
@@ -457,14 +459,22 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void gemm_ring_kernel(TileParam
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int tiles_n = (int)((p.N + R::BN - 1) / R::BN);
+  // Fused SwiGLU: B holds [gate; up] rows (N = 2F). A tile's 128 B rows
+  // alternate 16 gate rows and the 16 matching up rows, so each tile covers
+  // 64 output columns of A [M, F] and every wave's two 16-column blocks are
+  // a gate block and its up block: the SwiGLU needs no exchange.
+  constexpr bool SWI = OUTM == kOutSwiGLU;
+  static_assert(!SWI || GROUPED, "the fused SwiGLU runs on grouped launches");
+  constexpr int TN = SWI ? R::BN / 2 : R::BN;  // output columns per tile
+  const int64_t NC = SWI ? p.N / 2 : p.N;      // output columns
+  const int tiles_n = (int)((NC + TN - 1) / TN);
   int64_t m0, m_end, n0;
   const uint16_t* B = p.B;
   if constexpr (GROUPED) {
     // slot -> (expert, rows): experts own consecutive runs of ceil(count_e / BM)
     // row tiles, in expert order; every row tile spans all column tiles
     const int t = (int)(blockIdx.x / tiles_n);
-    n0 = (int64_t)(blockIdx.x % tiles_n) * R::BN;
+    n0 = (int64_t)(blockIdx.x % tiles_n) * TN;
     // The tile counts are prefix-summed 64 experts at a time across the
     // wave (two loads per lane, integer shuffles) and the owner found by a
     // ballot, instead of a serial walk over every expert's offsets.
@@ -545,7 +555,7 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void gemm_ring_kernel(TileParam
   // A rows: contiguous from m0, or gathered (offsets then from A itself)
   const uint8_t* A8 = reinterpret_cast<const uint8_t*>(p.A);
   c.abase = (GROUPED && p.rows) ? A8 : A8 + m0 * p.K * 2;
-  c.bbase = reinterpret_cast<const uint8_t*>(B + n0 * p.K);
+  c.bbase = reinterpret_cast<const uint8_t*>(SWI ? B : B + n0 * p.K);
 #pragma unroll
   for (int u = 0; u < R::LA; ++u) {
     const int r = (c.wave + NW * u) * R::RPL + lane / R::CPR;
@@ -564,8 +574,10 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void gemm_ring_kernel(TileParam
   for (int u = 0; u < R::LB; ++u) {
     const int r = (c.wave + NW * u) * R::RPL + lane / R::CPR;
     const int chunk = R::slot(r, lane % R::CPR);
-    const int64_t col = min(n0 + r, p.N - 1);
-    c.boff[u] = (uint32_t)(((col - n0) * p.K + chunk * 8) * 2);
+    int64_t brow;  // B row relative to bbase
+    if constexpr (SWI) brow = ((r >> 4) & 1) * NC + min(n0 + 16 * (r >> 5) + (r & 15), NC - 1);
+    else brow = min(n0 + r, p.N - 1) - n0;
+    c.boff[u] = (uint32_t)((brow * p.K + chunk * 8) * 2);
   }
   c.prologue();
 
@@ -593,6 +605,31 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void gemm_ring_kernel(TileParam
   // Epilogue: lane holds rows 4*(lane/16)+r of each 16x16 block, column lane%16.
   const int64_t rbase = m0 + wm * 64 + 4 * (lane >> 4);
   const int64_t cbase = n0 + wn * WN + (lane & 15);
+  if constexpr (SWI) {
+    // Block 0 of the wave is gate, block 1 the matching up columns: both are
+    // rounded to bf16 as the unfused GEMM would store them, then the
+    // wave stores bf16(silu_mul(g, u)). A malformed gather row is NaN in both
+    // halves, as in the unfused path.
+    static_assert(FN == 2, "one gate and one up block per wave");
+    uint16_t* Ao = reinterpret_cast<uint16_t*>(p.C);
+    const int64_t col = n0 + 16 * wn + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t row = rbase + 16 * i + r;
+        if (row >= m_end || col >= NC) continue;
+        bool bad = false;
+        if (p.rows) {
+          const int64_t gr = p.rows[row];
+          bad = gr < 0 || gr >= p.a_rows;
+        }
+        const float g = bf16_bits_to_f32(f32_to_bf16_bits(bad ? __builtin_nanf("") : acc.v[i][0][r]));
+        const float u = bf16_bits_to_f32(f32_to_bf16_bits(bad ? __builtin_nanf("") : acc.v[i][1][r]));
+        Ao[row * NC + col] = f32_to_bf16_bits(silu_mul(g, u));
+      }
+    return;
+  }
   if constexpr (OUTM == kOutLP) {
     block_barrier();  // every wave has consumed its last ring stage
     float* t = reinterpret_cast<float*>(lds) + wave * 64 * LPS;
@@ -915,11 +952,13 @@ hipError_t launch_gemm(const GemmLaunch& g, hipStream_t s) {
   p.lp_target = g.lp_target;
   const bool lp = g.lp_stats != nullptr;
   if (lp && (g.offsets || g.groups != 1)) return hipErrorInvalidValue;  // statistics need whole trees
+  if (g.swiglu && (!g.offsets || g.groups != 1 || g.N % 2 != 0)) return hipErrorInvalidValue;
 
   if (g.offsets) {  // grouped: row-tile slots = an upper bound on sum_e ceil(count_e / 128)
     const int64_t slots = g.M / 128 + g.E;
-    const int64_t tiles_n = (g.N + 127) / 128;
+    const int64_t tiles_n = g.swiglu ? (g.N / 2 + 63) / 64 : (g.N + 127) / 128;
     dim3 grid((unsigned)(slots * tiles_n), 1u, (unsigned)g.groups);
+    if (g.swiglu) return ring_dispatch<kOutSwiGLU, true>(p, grid, g.nl, s);
     return g.out_bf16 ? ring_dispatch<kOutBF16, true>(p, grid, g.nl, s)
                       : ring_dispatch<kOutF32, true>(p, grid, g.nl, s);
   }

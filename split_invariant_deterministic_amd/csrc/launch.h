@@ -34,6 +34,10 @@ struct GemmLaunch {
   float* lp_stats = nullptr;
   float* lp_tlogit = nullptr;
   const int32_t* lp_target = nullptr;
+  // Fused SwiGLU (grouped only): B = W [E, N, K] holds [gate; up] rows
+  // (N = 2F); C is A [M, F] bf16 with A[r, f] = bf16(silu_mul(bf16 g, bf16 u)),
+  // g and u being what the unfused GEMM would store at columns f and F + f.
+  bool swiglu = false;
 };
 hipError_t launch_gemm(const GemmLaunch& g, hipStream_t s);
 

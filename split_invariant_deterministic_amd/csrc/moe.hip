@@ -235,14 +235,8 @@ __global__ __launch_bounds__(256) void moe_scatter_kernel(const int32_t* __restr
 
 // ------------------------------------------------------------------ SwiGLU
 //
-// a = bf16( silu(g) * u ), silu(g) = g / (1 + exp(-g)), g and u the bf16
-// halves of a packed [gate | up] row, math in fp32 (exp as exp2(-g*log2e)).
-__device__ __forceinline__ float silu_mul(float g, float u) {
-  const float t = -g * kLog2e;
-  const float den = 1.0f + exp2_hw(t);
-  const float s = g / den;
-  return s * u;
-}
+// a = bf16( silu_mul(g, u) ) (common.h) for the bf16 halves of a packed
+// [gate | up] row; the gate/up GEMM's fused epilogue calls the same function.
 
 // Scalar form (any F).
 __global__ __launch_bounds__(256) void swiglu_kernel(const uint16_t* __restrict__ gu, uint16_t* __restrict__ a,

@@ -87,6 +87,7 @@ _SIGS = {
     "inv_moe_route": [_CP, _P, _P, _P, _I64, _I32, _P],
     "inv_moe_permute": [_CP, _P, _P, _P, _P, _I64, _I32, _P],
     "inv_moe_gemm": [_CP, _P, _I64, _P, _P, _P, _P, _I64, _I32, _I64, _I64, _P],
+    "inv_moe_gemm_swiglu": [_CP, _P, _I64, _P, _P, _P, _P, _I64, _I32, _I64, _I64, _P],
     "inv_swiglu": [_CP, _P, _P, _I64, _I64, _P],
     "inv_moe_combine": [_CP, _P, _P, _P, _I64, _P, _I64, _I64, _P],
     "inv_lmhead_logprob": [_CP, _P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P],
@@ -540,6 +541,27 @@ def moe_gemm(X, rows, offsets, W, R, c, out=None):
     return out
 
 
+def moe_gemm_swiglu(X, rows, offsets, W, R, c, out=None):
+    """A [R, F]: the gate/up grouped GEMM (W [E, 2F, K], gate rows then up rows)
+    with the SwiGLU in its epilogue (inv_moe_gemm_swiglu); bitwise
+    swiglu(moe_gemm(...)) with a bf16 gate/up output."""
+    _need(X, torch.bfloat16, "X", 2)
+    _need(W, torch.bfloat16, "W", 3)
+    _need(offsets, torch.int32, "offsets", 1)
+    if rows is not None:
+        _need(rows, torch.int32, "rows", 1)
+    E, N2, K = W.shape
+    if X.shape[1] != K or N2 % 2:
+        raise ValueError("X and W disagree on K, or W has an odd number of rows")
+    F = N2 // 2
+    if out is None:
+        out = torch.empty((R, F), dtype=torch.bfloat16, device=X.device)
+    _need(out, torch.bfloat16, "out", 2)
+    _call("inv_moe_gemm_swiglu", ctypes.byref(c), _ptr(X), X.shape[0], _ptr(rows), _ptr(offsets), _ptr(W), _ptr(out),
+          R, E, F, K, _stream())
+    return out
+
+
 def swiglu(GU, c, out=None):
     _need(GU, torch.bfloat16, "GU", 2)
     R, F2 = GU.shape
@@ -564,7 +586,8 @@ def moe_combine(Y, w, slot, c, out=None):
 
 
 def moe_layer(x, logits, W1, W2, c_gemm, c_route, out_stage=None):
-    """The whole MoE layer: route, group, gate/up GEMM, SwiGLU, down GEMM, combine.
+    """The whole MoE layer: route, group, gate/up GEMM with the SwiGLU fused in
+    its epilogue, down GEMM, combine.
 
     c_gemm pins the expert GEMMs' K leaves; c_route.leaves is the top-k and
     the combine's leaf count. Returns out [T, H] bf16 (and the stage tensors
@@ -577,12 +600,12 @@ def moe_layer(x, logits, W1, W2, c_gemm, c_route, out_stage=None):
     R = T * c_route.leaves
     cg = Contract.from_buffer_copy(c_gemm)
     cg.out_dtype = BF16
-    GU = moe_gemm(x, rows, offsets, W1, R, cg)
-    A = swiglu(GU, cg)
+    A = moe_gemm_swiglu(x, rows, offsets, W1, R, cg)
     cd = Contract.from_buffer_copy(c_gemm)
     cd.out_dtype = FP32
     Y = moe_gemm(A, None, offsets, W2, R, cd)
     out = moe_combine(Y, w, slot, c_route)
-    if out_stage is not None:
+    if out_stage is not None:  # the unfused gate/up output too, for inspection
+        GU = moe_gemm(x, rows, offsets, W1, R, cg)
         out_stage.update(ids=ids, w=w, offsets=offsets, rows=rows, slot=slot, GU=GU, A=A, Y=Y)
     return out

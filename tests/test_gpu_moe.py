@@ -163,6 +163,33 @@ def test_identical_experts_equal_one_expert(inv):
     assert bitwise_equal(out, inv.cast_bf16(y))
 
 
+@pytest.mark.parametrize("T,E,H,F,L", [(96, 128, 2048, 768, 8),   # the layer's shape (96 tokens)
+                                         (40, 16, 256, 100, 8),     # ragged F, 32-wide leaves (odd path)
+                                         (33, 8, 512, 64, 4),       # one output tile per expert
+                                         (7, 4, 128, 200, 1)])      # one leaf, a partial last tile
+def test_fused_swiglu_equals_unfused(inv, T, E, H, F, L):
+    """The gate/up GEMM with the SwiGLU in its epilogue is bitwise the
+    unfused grouped GEMM (bf16 gate/up) followed by the SwiGLU kernel,
+    including the NaN rows of malformed gather indices."""
+    c = inv.contract(leaves=L)
+    x = synth.randn((T, H), 41).to(DEV)
+    W1 = synth.randn((E, 2 * F, H), 42, 0.02).to(DEV)
+    logits = synth.randn((T, E), 43, dtype=torch.float32).to(DEV)
+    k = min(8, E)
+    ids, _ = inv.moe_route(logits, inv.contract(leaves=k))
+    offsets, rows, _ = inv.moe_permute(ids, E, inv.contract(leaves=k))
+    R = T * k
+    bad = rows.clone()
+    bad[3] = T + 5  # outside [0, T): a NaN row in both paths
+    bad[R // 2] = -1
+    for rr in (rows, bad):
+        fused = inv.moe_gemm_swiglu(x, rr, offsets, W1, R, c)
+        ref = inv.swiglu(inv.moe_gemm(x, rr, offsets, W1, R, c), c)
+        assert bitwise_equal(fused, ref)
+    assert torch.isnan(fused[3]).all() and torch.isnan(fused[R // 2]).all()
+    assert not torch.isnan(fused[4]).any()
+
+
 def test_grouped_gemm_rows_equal_plain_gemm(inv, moe_full):
     """A grouped row is bitwise what the plain K-leaf GEMM gives for it alone."""
     d = moe_full
