@@ -140,6 +140,14 @@ def test_entry_points_reject_before_any_launch():
     assert lib.inv_moe_route(by(cm), fake, fake, fake, 4, 4, null) == inv.E_UNSUPPORTED      # k > E
     assert lib.inv_moe_gemm(by(inv.contract(ranks=2)), fake, 4, fake, fake, fake, fake, 4, 2, 64, 4096,
                             null) == inv.E_TOPOLOGY
+    # fused gate/up + SwiGLU: one rank, 16-byte aligned operands, one expert's 2F x K under 4 GiB
+    assert lib.inv_moe_gemm_swiglu(by(inv.contract(ranks=2)), fake, 4, fake, fake, fake, fake, 4, 2, 64, 4096,
+                                   null) == inv.E_TOPOLOGY
+    assert lib.inv_moe_gemm_swiglu(by(cm), fake, 4, fake, fake, fake, fake, 4, 2, 1 << 19, 4096,
+                                   null) == inv.E_UNSUPPORTED
+    assert lib.inv_moe_gemm_swiglu(by(cm), ctypes.c_void_p((1 << 20) + 2), 4, fake, fake, fake, fake, 4, 2, 64, 4096,
+                                   null) == inv.E_ARG
+    assert lib.inv_moe_gemm_swiglu(by(cm), null, 0, null, null, null, null, 0, 2, 64, 4096, null) == inv.OK
     assert lib.inv_moe_combine(by(cm), null, null, null, 0, null, 0, 2048, null) == inv.OK
     # fused LM head + logprob: fp32 logits, one rank, V <= 262144, enough aligned workspace
     cl = inv.contract(leaves=8, out="fp32")
