@@ -666,10 +666,9 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void gemm_ring_kernel(TileParam
           if constexpr (OUTM == kOutBF16)
             reinterpret_cast<uint16_t*>(p.C)[off] = f32_to_bf16_bits(v);
           else
-            if constexpr (!GROUPED)  // streamed: fp32 logits are read once, by a later pass
-              __builtin_nontemporal_store(v, reinterpret_cast<float*>(p.C) + off);
-            else
-              reinterpret_cast<float*>(p.C)[off] = v;
+            // streamed: fp32 outputs (LM-head logits, the MoE down projection's
+            // rows) are read once, by a later pass
+            __builtin_nontemporal_store(v, reinterpret_cast<float*>(p.C) + off);
         }
       }
     }
