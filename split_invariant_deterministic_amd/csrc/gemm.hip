@@ -644,14 +644,17 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void gemm_ring_kernel(TileParam
     lp_rows_epilogue<FN, LPS>(p, t, row, row < m_end, n0 + wn * WN, lane);
     return;
   }
-  if constexpr (OUTM == kOutBF16 && !GROUPED) {
+  if constexpr ((OUTM == kOutBF16 || OUTM == kOutF32) && !GROUPED) {
     // Whole 16-byte row segments when the wave's column strip is inside C and
     // rows are 16-byte aligned: the block is transposed through LDS (the
-    // layout of the statistics epilogue above), then each lane converts 8
-    // consecutive columns of one row and stores them at once; a wave stores
-    // 64-byte row pieces instead of 2-byte elements.
-    const bool whole = n0 + wn * WN + WN <= p.N && p.N % 8 == 0 &&
-                       ((reinterpret_cast<uintptr_t>(p.C) | (uintptr_t)(z * p.c_group_stride * 2)) & 15u) == 0;
+    // layout of the statistics epilogue above), then each lane stores 8 bf16
+    // or 4 fp32 consecutive columns of one row at once; a wave writes 64- or
+    // 128-byte row pieces instead of single elements. fp32 output (logits,
+    // read once by a later pass) is streamed.
+    constexpr int EB = OUTM == kOutBF16 ? 2 : 4;  // bytes per element
+    constexpr int EPS = 16 / EB;                  // elements per 16-byte segment
+    const bool whole = n0 + wn * WN + WN <= p.N && p.N % EPS == 0 &&
+                       ((reinterpret_cast<uintptr_t>(p.C) | (uintptr_t)(z * p.c_group_stride * EB)) & 15u) == 0;
     block_barrier();  // every wave has consumed its last ring stage
     if (whole) {
       float* t = reinterpret_cast<float*>(lds) + wave * 64 * LPS;
@@ -662,18 +665,22 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void gemm_ring_kernel(TileParam
 #pragma unroll
           for (int r = 0; r < 4; ++r) t[(16 * i + 4 * (lane >> 4) + r) * LPS + 16 * j + (lane & 15)] = acc.v[i][j][r];
       // the wave reads back only what it wrote; its LDS accesses complete in order
-      constexpr int SEG = WN / 8;      // 8-column segments per row
+      constexpr int SEG = WN / EPS;    // segments per row
       constexpr int RPI = 64 / SEG;    // rows per pass of the wave
-      uint16_t* C = reinterpret_cast<uint16_t*>(p.C) + z * p.c_group_stride;
 #pragma unroll
       for (int q = 0; q < 64 / RPI; ++q) {
-        const int rl = q * RPI + lane / SEG, cs = 8 * (lane % SEG);
+        const int rl = q * RPI + lane / SEG, cs = EPS * (lane % SEG);
         const int64_t row = m0 + wm * 64 + rl;
+        const int64_t off = z * p.c_group_stride + row * p.N + n0 + wn * WN + cs;
         const f32x4 a0 = *reinterpret_cast<const f32x4*>(&t[rl * LPS + cs]);
-        const f32x4 a1 = *reinterpret_cast<const f32x4*>(&t[rl * LPS + cs + 4]);
-        const u32x4 o = u32x4{pack_bf16x2(a0[0], a0[1]), pack_bf16x2(a0[2], a0[3]), pack_bf16x2(a1[0], a1[1]),
-                              pack_bf16x2(a1[2], a1[3])};
-        if (row < m_end) *reinterpret_cast<u32x4*>(C + row * p.N + n0 + wn * WN + cs) = o;
+        if constexpr (OUTM == kOutBF16) {
+          const f32x4 a1 = *reinterpret_cast<const f32x4*>(&t[rl * LPS + cs + 4]);
+          const u32x4 o = u32x4{pack_bf16x2(a0[0], a0[1]), pack_bf16x2(a0[2], a0[3]), pack_bf16x2(a1[0], a1[1]),
+                                pack_bf16x2(a1[2], a1[3])};
+          if (row < m_end) *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.C) + off) = o;
+        } else {
+          if (row < m_end) __builtin_nontemporal_store(a0, reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.C) + off));
+        }
       }
       return;
     }
