@@ -644,13 +644,14 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void gemm_ring_kernel(TileParam
     lp_rows_epilogue<FN, LPS>(p, t, row, row < m_end, n0 + wn * WN, lane);
     return;
   }
-  if constexpr ((OUTM == kOutBF16 || OUTM == kOutF32) && !GROUPED) {
+  if constexpr (OUTM == kOutBF16 || OUTM == kOutF32) {
     // Whole 16-byte row segments when the wave's column strip is inside C and
     // rows are 16-byte aligned: the block is transposed through LDS (the
     // layout of the statistics epilogue above), then each lane stores 8 bf16
     // or 4 fp32 consecutive columns of one row at once; a wave writes 64- or
-    // 128-byte row pieces instead of single elements. fp32 output (logits,
-    // read once by a later pass) is streamed.
+    // 128-byte row pieces instead of single elements. fp32 output (LM-head
+    // logits, the MoE down projection's rows: read once, by a later pass) is
+    // streamed. A malformed gather row is NaN, as below.
     constexpr int EB = OUTM == kOutBF16 ? 2 : 4;  // bytes per element
     constexpr int EPS = 16 / EB;                  // elements per 16-byte segment
     const bool whole = n0 + wn * WN + WN <= p.N && p.N % EPS == 0 &&
@@ -672,9 +673,17 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void gemm_ring_kernel(TileParam
         const int rl = q * RPI + lane / SEG, cs = EPS * (lane % SEG);
         const int64_t row = m0 + wm * 64 + rl;
         const int64_t off = z * p.c_group_stride + row * p.N + n0 + wn * WN + cs;
-        const f32x4 a0 = *reinterpret_cast<const f32x4*>(&t[rl * LPS + cs]);
+        bool bad = false;
+        if constexpr (GROUPED) {
+          if (row < m_end && p.rows) {
+            const int64_t gr = p.rows[row];
+            bad = gr < 0 || gr >= p.a_rows;
+          }
+        }
+        const f32x4 nan4 = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+        const f32x4 a0 = bad ? nan4 : *reinterpret_cast<const f32x4*>(&t[rl * LPS + cs]);
         if constexpr (OUTM == kOutBF16) {
-          const f32x4 a1 = *reinterpret_cast<const f32x4*>(&t[rl * LPS + cs + 4]);
+          const f32x4 a1 = bad ? nan4 : *reinterpret_cast<const f32x4*>(&t[rl * LPS + cs + 4]);
           const u32x4 o = u32x4{pack_bf16x2(a0[0], a0[1]), pack_bf16x2(a0[2], a0[3]), pack_bf16x2(a1[0], a1[1]),
                                 pack_bf16x2(a1[2], a1[3])};
           if (row < m_end) *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.C) + off) = o;

@@ -190,6 +190,34 @@ def test_fused_swiglu_equals_unfused(inv, T, E, H, F, L):
     assert not torch.isnan(fused[4]).any()
 
 
+@pytest.mark.parametrize("out,K", [("fp32", 768), ("bf16", 512), ("fp32", 256)])
+def test_grouped_gemm_malformed_rows_are_nan(inv, out, K):
+    """A gathered index outside [0, x_rows) gives a NaN output row; every other
+    row is bitwise the plain K-leaf GEMM of its gathered input row (both store
+    paths of the epilogue, whole and ragged column strips)."""
+    T, E, N = 37, 8, 200
+    c = inv.contract(leaves=8, out=out)
+    x = synth.randn((T, K), 51).to(DEV)
+    W = synth.randn((E, N, K), 52, 0.02).to(DEV)
+    ids, _ = inv.moe_route(synth.randn((T, E), 53, dtype=torch.float32).to(DEV), inv.contract(leaves=4))
+    offsets, rows, _ = inv.moe_permute(ids, E, inv.contract(leaves=4))
+    R = T * 4
+    rows = rows.clone()
+    rows[5] = T
+    rows[R - 1] = -7
+    Y = inv.moe_gemm(x, rows, offsets, W, R, c)
+    assert torch.isnan(Y[5]).all() and torch.isnan(Y[R - 1]).all()
+    offs = offsets.cpu().numpy()
+    for e in range(E):
+        r0, r1 = int(offs[e]), int(offs[e + 1])
+        good = [r for r in range(r0, r1) if r not in (5, R - 1)]
+        if not good:
+            continue
+        gi = torch.as_tensor(good, device=DEV)
+        ref = inv.gemm(x[rows[gi].long()].contiguous(), W[e], c)
+        assert bitwise_equal(Y[gi], ref), e
+
+
 def test_grouped_gemm_rows_equal_plain_gemm(inv, moe_full):
     """A grouped row is bitwise what the plain K-leaf GEMM gives for it alone."""
     d = moe_full
