@@ -88,6 +88,9 @@ struct TileParams {
   float* lp_stats;           // [M, ceil(N/16)] (m, s) pairs
   float* lp_tlogit;          // [M] logit of the row's target column
   const int32_t* lp_target;  // [M]
+  // persistent ring launches: tiles blockIdx.x, + gridDim.x, ... below ntiles
+  int persist;
+  int64_t ntiles;
 };
 
 // Output modes of the GEMM kernels: fp32 C, bf16 C, (LM head) no C at all
@@ -224,14 +227,24 @@ struct RingCtx {
   uint32_t boff[R::LB];
   int64_t iss_k;  // first k of the next stage to issue
   int iss_off;    // its ring slot (byte offset)
-  int issued;     // stages issued so far
+  int issued;     // stages issued so far (over every tile of the workgroup)
+  int iss_end;    // issued count at which the issuing tile's stages end
+  int limit;      // stages that may be issued: those of the tiles set up so far
+  // The next tile's operands (persistent launches): the issue side switches
+  // to them at iss_end, so the ring runs on from one tile into the next.
+  bool has_next;
+  const uint8_t* nabase;
+  const uint8_t* nbbase;
+  uint32_t naoff[R::LA];
+  uint32_t nboff[R::LB];
+  int64_t nk0;
+  int nstages;
   // Fragment reads: per-lane byte offsets of operand block 0 for k substeps
   // 0 and 1 (block i adds 16 * i rows, an immediate: the swizzle depends on
   // the row only through (row / RPW) % CPR, which 16 rows leave unchanged).
   uint32_t rd_a[BK / 32], rd_b[BK / 32];
   int rd_off;     // ring slot of stage g
-  int g;          // next stage to compute
-  int total;      // stages in the range
+  int g;          // next stage to compute (over every tile of the workgroup)
   int spl;        // stages per leaf (ODD: 32-wide substeps per leaf)
   int wave;       // wave-uniform
 
@@ -257,6 +270,17 @@ struct RingCtx {
     iss_off += R::STAGE;
     if (iss_off == USED) iss_off = 0;
     ++issued;
+    if (issued == iss_end && has_next) {  // wave-uniform
+      abase = nabase;
+      bbase = nbbase;
+#pragma unroll
+      for (int u = 0; u < R::LA; ++u) aoff[u] = naoff[u];
+#pragma unroll
+      for (int u = 0; u < R::LB; ++u) boff[u] = nboff[u];
+      iss_k = nk0;
+      iss_end += nstages;
+      has_next = false;
+    }
   }
   __device__ __forceinline__ void issue_next() {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -270,10 +294,7 @@ struct RingCtx {
     for (int u = 0; u < R::LB; ++u)
       __builtin_amdgcn_global_load_lds(b + boff[u], &dst[R::ABYTES + (wave + NW * u) * 1024], 16, 0, 0);
 #endif
-    iss_k += BK;
-    iss_off += R::STAGE;
-    if (iss_off == USED) iss_off = 0;
-    ++issued;
+    issue_done();
   }
   static __device__ __forceinline__ int next_slot(int off) {
     off += R::STAGE;
@@ -312,13 +333,13 @@ struct RingCtx {
   __device__ __forceinline__ void prologue() {
     if constexpr (BK == 64) {
       for (int st = 0; st < R::NS; ++st)
-        if (issued < total) issue_next();
-      wait_vm_rem<R::LOADS, R::NS - 1>(total - 1);
+        if (issued < limit) issue_next();
+      wait_vm_rem<R::LOADS, R::NS - 1>(issued - 1);
       block_barrier();
       read_frags(rd_off, 0, fa0, fb0);
     } else {
       for (int st = 0; st < R::NS - 1; ++st)
-        if (issued < total) issue_next();
+        if (issued < limit) issue_next();
     }
   }
 
@@ -335,13 +356,13 @@ struct RingCtx {
     // fetches a stale slot that is never used: keeping this section
     // unconditional leaves no control-flow merge that would make the
     // compiler drain these reads before the MFMAs that follow).
-    wait_vm_rem<R::LOADS, R::NS - 2>(total - 2 - g);
+    wait_vm_rem<R::LOADS, R::NS - 2>(issued - 2 - g);
     block_barrier();  // stage g+1 visible; every wave's reads of stage g are done
     rd_off = next_slot(rd_off);
     read_frags(rd_off, 0, fa0, fb0);
     // MFMAs of substep 1 with the loads of stage g+NS (into stage g's slot)
     // spread between them
-    const bool more = issued < total;
+    const bool more = issued < limit;
     constexpr int LPI = R::LOADS / 4;  // loads per operand row block
     static_assert(LPI * 4 == R::LOADS && FN % LPI == 0, "interleave");
 #pragma unroll
@@ -359,9 +380,9 @@ struct RingCtx {
   __device__ __forceinline__ void stage32(Acc& acc) {
     // this thread's loads of stage g are done once at most the loads of
     // the (up to NS-2) later stages already issued are outstanding
-    wait_vm_rem<R::LOADS, R::NS - 2>(total - 1 - g);
+    wait_vm_rem<R::LOADS, R::NS - 2>(issued - 1 - g);
     block_barrier();  // every wave's stage g is in LDS; stage g-1 reads are done
-    if (issued < total) issue_next();  // stage g+NS-1, into stage g-1's slot
+    if (issued < limit) issue_next();  // stage g+NS-1, into stage g-1's slot
     bf16x8 fa[4], fb[FN];
     read_frags(rd_off, 0, fa, fb);
     rd_off = next_slot(rd_off);
@@ -383,11 +404,11 @@ struct RingCtx {
     read_frags(rd_off, 1, fa1, fb1);
     if constexpr (AFIRST) mma_first(fa0, fb0, a);
     else mma(fa0, fb0, a);
-    wait_vm_rem<R::LOADS, R::NS - 2>(total - 2 - g);
+    wait_vm_rem<R::LOADS, R::NS - 2>(issued - 2 - g);
     block_barrier();  // stage g+1 visible; every wave's reads of stage g are done
     rd_off = next_slot(rd_off);
     read_frags(rd_off, 0, fa0, fb0);
-    const bool more = issued < total;
+    const bool more = issued < limit;
     constexpr int LPI = R::LOADS / 4;
     static_assert(LPI * 4 == R::LOADS && FN % LPI == 0, "interleave");
 #pragma unroll
@@ -442,6 +463,16 @@ struct RingCtx {
 template <int NL>
 constexpr int ring_bytes() { return NL == 8 ? 98304 : 131072; }
 
+// Position and operand addressing of one output tile of the ring kernel.
+template <int LA, int LB>
+struct TileAddr {
+  int64_t m0, m_end, n0;
+  const uint8_t* abase;
+  const uint8_t* bbase;
+  uint32_t aoff[LA];
+  uint32_t boff[LB];
+};
+
 // ODD: leaves that are an odd multiple of 32 on 64-k stages (NL even, so the
 // range is whole stages).
 template <int NL, int BK, int OUTM, bool GROUPED, bool ODD = false>
@@ -456,6 +487,11 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void gemm_ring_kernel(TileParam
   constexpr int LP_BYTES = OUTM == kOutLP ? NW * 64 * LPS * 4 : 0;
   constexpr int LDS_BYTES = R::NS * R::STAGE + SPILL > LP_BYTES ? R::NS * R::STAGE + SPILL : LP_BYTES;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
+  // Persistent launches take several tiles per workgroup and let the ring
+  // run on into the next tile's stages (8 leaves on 64-k stages).
+  // (Odd-multiple-of-32 leaves are left out: their tree already fills the
+  // registers, and carrying the next tile's addressing spills.)
+  constexpr bool PERSIST_OK = NL == 8 && BK == 64 && OUTM != kOutLP && !ODD;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -468,80 +504,118 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void gemm_ring_kernel(TileParam
   constexpr int TN = SWI ? R::BN / 2 : R::BN;  // output columns per tile
   const int64_t NC = SWI ? p.N / 2 : p.N;      // output columns
   const int tiles_n = (int)((NC + TN - 1) / TN);
-  int64_t m0, m_end, n0;
-  const uint16_t* B = p.B;
-  if constexpr (GROUPED) {
-    // slot -> (expert, rows): experts own consecutive runs of ceil(count_e / BM)
-    // row tiles, in expert order; every row tile spans all column tiles
-    const int t = (int)(blockIdx.x / tiles_n);
-    n0 = (int64_t)(blockIdx.x % tiles_n) * TN;
-    // The tile counts are prefix-summed 64 experts at a time across the
-    // wave (two loads per lane, integer shuffles) and the owner found by a
-    // ballot, instead of a serial walk over every expert's offsets.
-    // Offsets come from device memory: clamp so a malformed table can never
-    // address rows outside [0, M).
-    int e = -1, tstart = 0, r0 = 0, r1 = 0, running = 0;
-    for (int cbase = 0; cbase < p.E && e < 0; cbase += 64) {
-      const int ee = cbase + lane;
-      int a0 = 0, a1 = 0, nt = 0;
-      if (ee < p.E) {
-        a0 = (int)min(max((int64_t)p.offsets[ee], (int64_t)0), p.M);
-        a1 = (int)min(max((int64_t)p.offsets[ee + 1], (int64_t)a0), p.M);
-        nt = (a1 - a0 + R::BM - 1) / R::BM;
+  // Tile position and operand addressing: blockIdx.x for a plain launch,
+  // tiles blockIdx.x, + gridDim.x, ... for a persistent one. False for a
+  // grouped slot past the last tile.
+  const uint8_t* A8 = reinterpret_cast<const uint8_t*>(p.A);
+  const int cw = __builtin_amdgcn_readfirstlane(wave);
+  auto setup = [&](int64_t tile, TileAddr<R::LA, R::LB>& T) -> bool {
+    int64_t m0, m_end, n0;
+    const uint16_t* B = p.B;
+    if constexpr (GROUPED) {
+      // slot -> (expert, rows): experts own consecutive runs of ceil(count_e / BM)
+      // row tiles, in expert order; every row tile spans all column tiles
+      const int t = (int)(tile / tiles_n);
+      n0 = (int64_t)(tile % tiles_n) * TN;
+      // The tile counts are prefix-summed 64 experts at a time across the
+      // wave (two loads per lane, integer shuffles) and the owner found by a
+      // ballot, instead of a serial walk over every expert's offsets.
+      // Offsets come from device memory: clamp so a malformed table can never
+      // address rows outside [0, M).
+      int e = -1, tstart = 0, r0 = 0, r1 = 0, running = 0;
+      for (int cbase = 0; cbase < p.E && e < 0; cbase += 64) {
+        const int ee = cbase + lane;
+        int a0 = 0, a1 = 0, nt = 0;
+        if (ee < p.E) {
+          a0 = (int)min(max((int64_t)p.offsets[ee], (int64_t)0), p.M);
+          a1 = (int)min(max((int64_t)p.offsets[ee + 1], (int64_t)a0), p.M);
+          nt = (a1 - a0 + R::BM - 1) / R::BM;
+        }
+        int incl = nt;
+  #pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int v = __shfl_up(incl, off, 64);
+          if (lane >= off) incl += v;
+        }
+        incl += running;
+        const uint64_t hit = __ballot(ee < p.E && t < incl);
+        if (hit) {  // wave-uniform
+          const int f = __ffsll((unsigned long long)hit) - 1;
+          e = cbase + f;
+          tstart = __shfl(incl - nt, f, 64);
+          r0 = __shfl(a0, f, 64);
+          r1 = __shfl(a1, f, 64);
+        } else {
+          running = __shfl(incl, 63, 64);
+        }
       }
-      int incl = nt;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int v = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += v;
-      }
-      incl += running;
-      const uint64_t hit = __ballot(ee < p.E && t < incl);
-      if (hit) {  // wave-uniform
-        const int f = __ffsll((unsigned long long)hit) - 1;
-        e = cbase + f;
-        tstart = __shfl(incl - nt, f, 64);
-        r0 = __shfl(a0, f, 64);
-        r1 = __shfl(a1, f, 64);
-      } else {
-        running = __shfl(incl, 63, 64);
-      }
+      if (e < 0) return false;  // slot past the last tile (uniform)
+      m0 = r0 + (int64_t)(t - tstart) * R::BM;
+      m_end = r1;
+      B += (int64_t)e * p.b_expert_stride;
+    } else {
+      // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so
+      // give XCD x a contiguous run of tile ids, and walk tile ids in bands
+      // of 4 row tiles so that the workgroups resident on one XCD share A and
+      // B panels in its L2.
+      const int tiles_m = (int)((p.M + R::BM - 1) / R::BM);
+      const int nb = tiles_m * tiles_n;
+      int t = (int)tile;
+      if (nb % 8 == 0) t = (t % 8) * (nb / 8) + t / 8;
+      constexpr int GM = 4;
+      const int band = t / (GM * tiles_n);
+      const int rows_in_band = min(GM, tiles_m - band * GM);
+      const int within = t - band * GM * tiles_n;
+      const int tm = band * GM + within % rows_in_band;
+      const int tn = within / rows_in_band;
+      m0 = (int64_t)tm * R::BM;
+      n0 = (int64_t)tn * R::BN;
+      m_end = p.M;
     }
-    if (e < 0) return;  // slot past the last tile: uniform exit before any barrier
-    m0 = r0 + (int64_t)(t - tstart) * R::BM;
-    m_end = r1;
-    B += (int64_t)e * p.b_expert_stride;
-  } else {
-    // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so
-    // give XCD x a contiguous run of tile ids, and walk tile ids in bands
-    // of 4 row tiles so that the workgroups resident on one XCD share A and
-    // B panels in its L2.
-    const int tiles_m = (int)((p.M + R::BM - 1) / R::BM);
-    const int nb = tiles_m * tiles_n;
-    int t = (int)blockIdx.x;
-    if (nb % 8 == 0) t = (t % 8) * (nb / 8) + t / 8;
-    constexpr int GM = 4;
-    const int band = t / (GM * tiles_n);
-    const int rows_in_band = min(GM, tiles_m - band * GM);
-    const int within = t - band * GM * tiles_n;
-    const int tm = band * GM + within % rows_in_band;
-    const int tn = within / rows_in_band;
-    m0 = (int64_t)tm * R::BM;
-    n0 = (int64_t)tn * R::BN;
-    m_end = p.M;
-  }
+    // A rows: contiguous from m0, or gathered (offsets then from A itself)
+    T.abase = (GROUPED && p.rows) ? A8 : A8 + m0 * p.K * 2;
+    T.bbase = reinterpret_cast<const uint8_t*>(SWI ? B : B + n0 * p.K);
+  #pragma unroll
+    for (int u = 0; u < R::LA; ++u) {
+      const int r = (cw + NW * u) * R::RPL + lane / R::CPR;
+      const int chunk = R::slot(r, lane % R::CPR);  // the slot map is its own inverse
+      int64_t row = min(m0 + r, m_end - 1);
+      int64_t rel = row - m0;
+      if constexpr (GROUPED) {
+        if (p.rows) {
+          const int64_t gr = p.rows[row];
+          rel = (gr >= 0 && gr < p.a_rows) ? gr : 0;
+        }
+      }
+      T.aoff[u] = (uint32_t)((rel * p.K + chunk * 8) * 2);
+    }
+  #pragma unroll
+    for (int u = 0; u < R::LB; ++u) {
+      const int r = (cw + NW * u) * R::RPL + lane / R::CPR;
+      const int chunk = R::slot(r, lane % R::CPR);
+      int64_t brow;  // B row relative to bbase
+      if constexpr (SWI) brow = ((r >> 4) & 1) * NC + min(n0 + 16 * (r >> 5) + (r & 15), NC - 1);
+      else brow = min(n0 + r, p.N - 1) - n0;
+      T.boff[u] = (uint32_t)((brow * p.K + chunk * 8) * 2);
+    }
+    T.m0 = m0;
+    T.m_end = m_end;
+    T.n0 = n0;
+    return true;
+  };
+  TileAddr<R::LA, R::LB> cur;
+  int64_t tile = blockIdx.x;
+  if (!setup(tile, cur)) return;  // uniform exit before any barrier
   const int z = blockIdx.z;
   const int leaf0 = p.leaf_lo + z * NL;
 
   Ctx c;
   c.lds = lds;
   c.wave = __builtin_amdgcn_readfirstlane(wave);
-  c.iss_k = (int64_t)leaf0 * p.kl;
   c.iss_off = 0;
   c.issued = 0;
   c.rd_off = 0;
   c.spl = ODD ? p.kl / 32 : p.kl / BK;
-  c.total = ODD ? NL * p.kl / 64 : c.spl * NL;
   c.g = 0;
   const int wm = c.wave / (NW / 2), wn = c.wave % (NW / 2);  // wave tile (row, column) in the tile
   {
@@ -552,176 +626,235 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void gemm_ring_kernel(TileParam
       c.rd_b[ks] = R::ABYTES + R::off(wn * WN + r16, 4 * ks + g4);
     }
   }
-  // A rows: contiguous from m0, or gathered (offsets then from A itself)
-  const uint8_t* A8 = reinterpret_cast<const uint8_t*>(p.A);
-  c.abase = (GROUPED && p.rows) ? A8 : A8 + m0 * p.K * 2;
-  c.bbase = reinterpret_cast<const uint8_t*>(SWI ? B : B + n0 * p.K);
+  const int stages = ODD ? NL * p.kl / 64 : c.spl * NL;  // per tile
+  const int64_t k0 = (int64_t)leaf0 * p.kl;
+  c.abase = cur.abase;
+  c.bbase = cur.bbase;
 #pragma unroll
-  for (int u = 0; u < R::LA; ++u) {
-    const int r = (c.wave + NW * u) * R::RPL + lane / R::CPR;
-    const int chunk = R::slot(r, lane % R::CPR);  // the slot map is its own inverse
-    int64_t row = min(m0 + r, m_end - 1);
-    int64_t rel = row - m0;
-    if constexpr (GROUPED) {
-      if (p.rows) {
-        const int64_t gr = p.rows[row];
-        rel = (gr >= 0 && gr < p.a_rows) ? gr : 0;
-      }
-    }
-    c.aoff[u] = (uint32_t)((rel * p.K + chunk * 8) * 2);
-  }
+  for (int u = 0; u < R::LA; ++u) c.aoff[u] = cur.aoff[u];
 #pragma unroll
-  for (int u = 0; u < R::LB; ++u) {
-    const int r = (c.wave + NW * u) * R::RPL + lane / R::CPR;
-    const int chunk = R::slot(r, lane % R::CPR);
-    int64_t brow;  // B row relative to bbase
-    if constexpr (SWI) brow = ((r >> 4) & 1) * NC + min(n0 + 16 * (r >> 5) + (r & 15), NC - 1);
-    else brow = min(n0 + r, p.N - 1) - n0;
-    c.boff[u] = (uint32_t)((brow * p.K + chunk * 8) * 2);
-  }
+  for (int u = 0; u < R::LB; ++u) c.boff[u] = cur.boff[u];
+  c.iss_k = k0;
+  c.iss_end = stages;
+  c.limit = stages;
+  c.has_next = false;
   c.prologue();
 
-  typename Ctx::Acc acc;
-  if constexpr (SPILL > 0) {
-    float* spill = reinterpret_cast<float*>(&lds[R::NS * R::STAGE]) + wave * 64 * WN + lane;
-    run_tree<4>(c, acc);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) spill[((i * FN + j) * 4 + r) * 64] = acc.v[i][j][r];
-    run_tree<4>(c, acc);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc.v[i][j][r] = spill[((i * FN + j) * 4 + r) * 64] + acc.v[i][j][r];
-  } else {
-    run_tree<NL>(c, acc);
-  }
-
   // Epilogue: lane holds rows 4*(lane/16)+r of each 16x16 block, column lane%16.
-  const int64_t rbase = m0 + wm * 64 + 4 * (lane >> 4);
-  const int64_t cbase = n0 + wn * WN + (lane & 15);
-  if constexpr (SWI) {
-    // Block 0 of the wave is gate, block 1 the matching up columns: both are
-    // rounded to bf16 as the unfused GEMM would store them, then the
-    // wave stores bf16(silu_mul(g, u)). A malformed gather row is NaN in both
-    // halves, as in the unfused path.
-    static_assert(FN == 2, "one gate and one up block per wave");
-    uint16_t* Ao = reinterpret_cast<uint16_t*>(p.C);
-    const int64_t col = n0 + 16 * wn + (lane & 15);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t row = rbase + 16 * i + r;
-        if (row >= m_end || col >= NC) continue;
-        bool bad = false;
-        if (p.rows) {
-          const int64_t gr = p.rows[row];
-          bad = gr < 0 || gr >= p.a_rows;
+  auto finish = [&](const TileAddr<R::LA, R::LB>& T, typename Ctx::Acc& acc) {
+    const int64_t rbase = T.m0 + wm * 64 + 4 * (lane >> 4);
+    const int64_t cbase = T.n0 + wn * WN + (lane & 15);
+    if constexpr (SWI) {
+      // Block 0 of the wave is gate, block 1 the matching up columns: both are
+      // rounded to bf16 as the unfused GEMM would store them, then the
+      // wave stores bf16(silu_mul(g, u)). A malformed gather row is NaN in both
+      // halves, as in the unfused path.
+      static_assert(FN == 2, "one gate and one up block per wave");
+      uint16_t* Ao = reinterpret_cast<uint16_t*>(p.C);
+      const int64_t col0 = T.n0 + 16 * wn;  // the wave's 16 output columns
+      if constexpr (SPILL > 0) {
+        // Whole 16-byte row pieces (8 columns) when the strip is inside A and
+        // rows are 16-byte aligned: the 64 x 16 results go through the wave's
+        // own spill slice (free once the tree is summed, touched by no other
+        // wave), then each lane stores 8 consecutive columns of one row.
+        if (col0 + 16 <= NC && NC % 8 == 0 && (reinterpret_cast<uintptr_t>(Ao) & 15u) == 0) {
+          uint16_t* t = reinterpret_cast<uint16_t*>(&lds[R::NS * R::STAGE]) + wave * 64 * WN * 2;
+  #pragma unroll
+          for (int i = 0; i < 4; ++i)
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float g = bf16_bits_to_f32(f32_to_bf16_bits(acc.v[i][0][r]));
+              const float u = bf16_bits_to_f32(f32_to_bf16_bits(acc.v[i][1][r]));
+              t[(16 * i + 4 * (lane >> 4) + r) * 16 + (lane & 15)] = f32_to_bf16_bits(silu_mul(g, u));
+            }
+          // the row value of a malformed gather row, computed at run time on
+          // the same inputs as the unfused path (not folded by the compiler)
+          float qg = __builtin_nanf(""), qu = __builtin_nanf("");
+          asm volatile("" : "+v"(qg), "+v"(qu));
+          qg = bf16_bits_to_f32(f32_to_bf16_bits(qg));
+          qu = bf16_bits_to_f32(f32_to_bf16_bits(qu));
+          const uint16_t nanv = f32_to_bf16_bits(silu_mul(qg, qu));
+          const uint32_t nan2 = (uint32_t)nanv | ((uint32_t)nanv << 16);
+  #pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int rl = 32 * q + (lane >> 1), cs = 8 * (lane & 1);
+            const int64_t row = T.m0 + wm * 64 + rl;
+            if (row >= T.m_end) continue;
+            bool bad = false;
+            if (p.rows) {
+              const int64_t gr = p.rows[row];
+              bad = gr < 0 || gr >= p.a_rows;
+            }
+            const u32x4 v = bad ? u32x4{nan2, nan2, nan2, nan2} : *reinterpret_cast<const u32x4*>(&t[rl * 16 + cs]);
+            *reinterpret_cast<u32x4*>(Ao + row * NC + col0 + cs) = v;
+          }
+          return;
         }
-        const float g = bf16_bits_to_f32(f32_to_bf16_bits(bad ? __builtin_nanf("") : acc.v[i][0][r]));
-        const float u = bf16_bits_to_f32(f32_to_bf16_bits(bad ? __builtin_nanf("") : acc.v[i][1][r]));
-        Ao[row * NC + col] = f32_to_bf16_bits(silu_mul(g, u));
       }
-    return;
-  }
-  if constexpr (OUTM == kOutLP) {
-    block_barrier();  // every wave has consumed its last ring stage
-    float* t = reinterpret_cast<float*>(lds) + wave * 64 * LPS;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) t[(16 * i + 4 * (lane >> 4) + r) * LPS + 16 * j + (lane & 15)] = acc.v[i][j][r];
-    // the wave reads back only what it wrote; its LDS accesses complete in order
-    const int64_t row = m0 + wm * 64 + lane;
-    lp_rows_epilogue<FN, LPS>(p, t, row, row < m_end, n0 + wn * WN, lane);
-    return;
-  }
-  if constexpr (OUTM == kOutBF16 || OUTM == kOutF32) {
-    // Whole 16-byte row segments when the wave's column strip is inside C and
-    // rows are 16-byte aligned: the block is transposed through LDS (the
-    // layout of the statistics epilogue above), then each lane stores 8 bf16
-    // or 4 fp32 consecutive columns of one row at once; a wave writes 64- or
-    // 128-byte row pieces instead of single elements. fp32 output (LM-head
-    // logits, the MoE down projection's rows: read once, by a later pass) is
-    // streamed. A malformed gather row is NaN, as below.
-    constexpr int EB = OUTM == kOutBF16 ? 2 : 4;  // bytes per element
-    constexpr int EPS = 16 / EB;                  // elements per 16-byte segment
-    const bool whole = n0 + wn * WN + WN <= p.N && p.N % EPS == 0 &&
-                       ((reinterpret_cast<uintptr_t>(p.C) | (uintptr_t)(z * p.c_group_stride * EB)) & 15u) == 0;
-    block_barrier();  // every wave has consumed its last ring stage
-    if (whole) {
-      float* t = reinterpret_cast<float*>(lds) + wave * 64 * LPS;
-#pragma unroll
+      const int64_t col = col0 + (lane & 15);
+  #pragma unroll
       for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) t[(16 * i + 4 * (lane >> 4) + r) * LPS + 16 * j + (lane & 15)] = acc.v[i][j][r];
-      // the wave reads back only what it wrote; its LDS accesses complete in order
-      constexpr int SEG = WN / EPS;    // segments per row
-      constexpr int RPI = 64 / SEG;    // rows per pass of the wave
-#pragma unroll
-      for (int q = 0; q < 64 / RPI; ++q) {
-        const int rl = q * RPI + lane / SEG, cs = EPS * (lane % SEG);
-        const int64_t row = m0 + wm * 64 + rl;
-        const int64_t off = z * p.c_group_stride + row * p.N + n0 + wn * WN + cs;
-        bool bad = false;
-        if constexpr (GROUPED) {
-          if (row < m_end && p.rows) {
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t row = rbase + 16 * i + r;
+          if (row >= T.m_end || col >= NC) continue;
+          bool bad = false;
+          if (p.rows) {
             const int64_t gr = p.rows[row];
             bad = gr < 0 || gr >= p.a_rows;
           }
+          const float g = bf16_bits_to_f32(f32_to_bf16_bits(bad ? __builtin_nanf("") : acc.v[i][0][r]));
+          const float u = bf16_bits_to_f32(f32_to_bf16_bits(bad ? __builtin_nanf("") : acc.v[i][1][r]));
+          Ao[row * NC + col] = f32_to_bf16_bits(silu_mul(g, u));
         }
-        const f32x4 nan4 = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
-        const f32x4 a0 = bad ? nan4 : *reinterpret_cast<const f32x4*>(&t[rl * LPS + cs]);
-        if constexpr (OUTM == kOutBF16) {
-          const f32x4 a1 = bad ? nan4 : *reinterpret_cast<const f32x4*>(&t[rl * LPS + cs + 4]);
-          const u32x4 o = u32x4{pack_bf16x2(a0[0], a0[1]), pack_bf16x2(a0[2], a0[3]), pack_bf16x2(a1[0], a1[1]),
-                                pack_bf16x2(a1[2], a1[3])};
-          if (row < m_end) *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.C) + off) = o;
-        } else {
-          if (row < m_end) __builtin_nontemporal_store(a0, reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.C) + off));
-        }
-      }
       return;
     }
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t row = rbase + 16 * i + r;
-      if (row >= m_end) continue;
-      bool bad = false;
-      if constexpr (GROUPED) {
-        if (p.rows) {
-          const int64_t gr = p.rows[row];
-          bad = gr < 0 || gr >= p.a_rows;  // a malformed gather index gives a NaN row
+    if constexpr (OUTM == kOutLP) {
+      block_barrier();  // every wave has consumed its last ring stage
+      float* t = reinterpret_cast<float*>(lds) + wave * 64 * LPS;
+  #pragma unroll
+      for (int i = 0; i < 4; ++i)
+  #pragma unroll
+        for (int j = 0; j < FN; ++j)
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) t[(16 * i + 4 * (lane >> 4) + r) * LPS + 16 * j + (lane & 15)] = acc.v[i][j][r];
+      // the wave reads back only what it wrote; its LDS accesses complete in order
+      const int64_t row = T.m0 + wm * 64 + lane;
+      lp_rows_epilogue<FN, LPS>(p, t, row, row < T.m_end, T.n0 + wn * WN, lane);
+      return;
+    }
+    if constexpr (OUTM == kOutBF16 || OUTM == kOutF32) {
+      // Whole 16-byte row segments when the wave's column strip is inside C and
+      // rows are 16-byte aligned: the block is transposed through LDS (the
+      // layout of the statistics epilogue above), then each lane stores 8 bf16
+      // or 4 fp32 consecutive columns of one row at once; a wave writes 64- or
+      // 128-byte row pieces instead of single elements. fp32 output (LM-head
+      // logits, the MoE down projection's rows: read once, by a later pass) is
+      // streamed. A malformed gather row is NaN, as below.
+      constexpr int EB = OUTM == kOutBF16 ? 2 : 4;  // bytes per element
+      constexpr int EPS = 16 / EB;                  // elements per 16-byte segment
+      const bool whole = T.n0 + wn * WN + WN <= p.N && p.N % EPS == 0 &&
+                         ((reinterpret_cast<uintptr_t>(p.C) | (uintptr_t)(z * p.c_group_stride * EB)) & 15u) == 0;
+      // Transpose space: with 8 leaves the wave's own spill slice (64 x WN
+      // floats, free once the tree is summed, touched by no other wave; in a
+      // persistent launch the ring already holds the next tile's stages), else
+      // the ring once every wave has left it.
+      constexpr int LPX = SPILL > 0 ? WN : LPS;
+      if constexpr (SPILL == 0) block_barrier();  // every wave has consumed its last ring stage
+      if (whole) {
+        float* t = SPILL > 0 ? reinterpret_cast<float*>(&lds[R::NS * R::STAGE]) + wave * 64 * WN
+                             : reinterpret_cast<float*>(lds) + wave * 64 * LPS;
+  #pragma unroll
+        for (int i = 0; i < 4; ++i)
+  #pragma unroll
+          for (int j = 0; j < FN; ++j)
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) t[(16 * i + 4 * (lane >> 4) + r) * LPX + 16 * j + (lane & 15)] = acc.v[i][j][r];
+        // the wave reads back only what it wrote; its LDS accesses complete in order
+        constexpr int SEG = WN / EPS;    // segments per row
+        constexpr int RPI = 64 / SEG;    // rows per pass of the wave
+  #pragma unroll
+        for (int q = 0; q < 64 / RPI; ++q) {
+          const int rl = q * RPI + lane / SEG, cs = EPS * (lane % SEG);
+          const int64_t row = T.m0 + wm * 64 + rl;
+          const int64_t off = z * p.c_group_stride + row * p.N + T.n0 + wn * WN + cs;
+          bool bad = false;
+          if constexpr (GROUPED) {
+            if (row < T.m_end && p.rows) {
+              const int64_t gr = p.rows[row];
+              bad = gr < 0 || gr >= p.a_rows;
+            }
+          }
+          const f32x4 nan4 = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+          const f32x4 a0 = bad ? nan4 : *reinterpret_cast<const f32x4*>(&t[rl * LPX + cs]);
+          if constexpr (OUTM == kOutBF16) {
+            const f32x4 a1 = bad ? nan4 : *reinterpret_cast<const f32x4*>(&t[rl * LPX + cs + 4]);
+            const u32x4 o = u32x4{pack_bf16x2(a0[0], a0[1]), pack_bf16x2(a0[2], a0[3]), pack_bf16x2(a1[0], a1[1]),
+                                  pack_bf16x2(a1[2], a1[3])};
+            if (row < T.m_end) *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.C) + off) = o;
+          } else {
+            if (row < T.m_end) __builtin_nontemporal_store(a0, reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.C) + off));
+          }
         }
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int64_t col = cbase + 16 * j;
-        if (col < p.N) {
-          const int64_t off = (int64_t)z * p.c_group_stride + row * p.N + col;
-          const float v = bad ? __builtin_nanf("") : acc.v[i][j][r];
-          if constexpr (OUTM == kOutBF16)
-            reinterpret_cast<uint16_t*>(p.C)[off] = f32_to_bf16_bits(v);
-          else
-            // streamed: fp32 outputs (LM-head logits, the MoE down projection's
-            // rows) are read once, by a later pass
-            __builtin_nontemporal_store(v, reinterpret_cast<float*>(p.C) + off);
-        }
+        return;
       }
     }
+  #pragma unroll
+    for (int i = 0; i < 4; ++i)
+  #pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t row = rbase + 16 * i + r;
+        if (row >= T.m_end) continue;
+        bool bad = false;
+        if constexpr (GROUPED) {
+          if (p.rows) {
+            const int64_t gr = p.rows[row];
+            bad = gr < 0 || gr >= p.a_rows;  // a malformed gather index gives a NaN row
+          }
+        }
+  #pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int64_t col = cbase + 16 * j;
+          if (col < p.N) {
+            const int64_t off = (int64_t)z * p.c_group_stride + row * p.N + col;
+            const float v = bad ? __builtin_nanf("") : acc.v[i][j][r];
+            if constexpr (OUTM == kOutBF16)
+              reinterpret_cast<uint16_t*>(p.C)[off] = f32_to_bf16_bits(v);
+            else
+              // streamed: fp32 outputs (LM-head logits, the MoE down projection's
+              // rows) are read once, by a later pass
+              __builtin_nontemporal_store(v, reinterpret_cast<float*>(p.C) + off);
+          }
+        }
+      }
+  };
+
+  for (;;) {
+    // the next tile is set up first, so that its stages follow this tile's
+    // in the ring
+    TileAddr<R::LA, R::LB> nx;
+    bool more_tiles = false;
+    const int64_t tn = tile + gridDim.x;
+    if constexpr (PERSIST_OK) {
+      if (p.persist && tn < p.ntiles && setup(tn, nx)) {
+        more_tiles = true;
+        c.nabase = nx.abase;
+        c.nbbase = nx.bbase;
+#pragma unroll
+        for (int u = 0; u < R::LA; ++u) c.naoff[u] = nx.aoff[u];
+#pragma unroll
+        for (int u = 0; u < R::LB; ++u) c.nboff[u] = nx.boff[u];
+        c.nk0 = k0;
+        c.nstages = stages;
+        c.has_next = true;
+        c.limit += stages;
+      }
+    }
+    typename Ctx::Acc acc;
+    if constexpr (SPILL > 0) {
+      float* spill = reinterpret_cast<float*>(&lds[R::NS * R::STAGE]) + wave * 64 * WN + lane;
+      run_tree<4>(c, acc);
+  #pragma unroll
+      for (int i = 0; i < 4; ++i)
+  #pragma unroll
+        for (int j = 0; j < FN; ++j)
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) spill[((i * FN + j) * 4 + r) * 64] = acc.v[i][j][r];
+      run_tree<4>(c, acc);
+  #pragma unroll
+      for (int i = 0; i < 4; ++i)
+  #pragma unroll
+        for (int j = 0; j < FN; ++j)
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) acc.v[i][j][r] = spill[((i * FN + j) * 4 + r) * 64] + acc.v[i][j][r];
+    } else {
+      run_tree<NL>(c, acc);
+    }
+    finish(cur, acc);
+    if (!more_tiles) break;
+    cur = nx;
+    tile = tn;
+  }
 }
 
 // -------------------------------------------------------------- stream kernel
@@ -1002,7 +1135,15 @@ hipError_t launch_gemm(const GemmLaunch& g, hipStream_t s) {
   p.lp_stats = g.lp_stats;
   p.lp_tlogit = g.lp_tlogit;
   p.lp_target = g.lp_target;
+  p.persist = 0;
+  p.ntiles = 0;
   const bool lp = g.lp_stats != nullptr;
+  // Persistent ring launches (8 leaves on 64-k stages, whole trees, more
+  // tiles than the chip holds): one workgroup per CU walks tiles blockIdx.x,
+  // + 256, ..., and its ring runs on from each tile into the next, so no tile
+  // pays the pipeline's fill or a workgroup launch.
+  constexpr int64_t kResident = 256;
+  const bool can_persist = g.nl == 8 && g.kl % 64 == 0 && !lp && g.groups == 1;
   if (lp && (g.offsets || g.groups != 1)) return hipErrorInvalidValue;  // statistics need whole trees
   if (g.swiglu && (!g.offsets || g.groups != 1 || g.N % 2 != 0)) return hipErrorInvalidValue;
 
@@ -1010,6 +1151,11 @@ hipError_t launch_gemm(const GemmLaunch& g, hipStream_t s) {
     const int64_t slots = g.M / 128 + g.E;
     const int64_t tiles_n = g.swiglu ? (g.N / 2 + 63) / 64 : (g.N + 127) / 128;
     dim3 grid((unsigned)(slots * tiles_n), 1u, (unsigned)g.groups);
+    if (can_persist && slots * tiles_n > kResident) {
+      p.persist = 1;
+      p.ntiles = slots * tiles_n;
+      grid.x = (unsigned)kResident;
+    }
     if (g.swiglu) return ring_dispatch<kOutSwiGLU, true>(p, grid, g.nl, s);
     return g.out_bf16 ? ring_dispatch<kOutBF16, true>(p, grid, g.nl, s)
                       : ring_dispatch<kOutF32, true>(p, grid, g.nl, s);
@@ -1031,6 +1177,11 @@ hipError_t launch_gemm(const GemmLaunch& g, hipStream_t s) {
   }
   const int64_t tiles = ((g.M + 127) / 128) * ((g.N + 127) / 128);
   dim3 grid((unsigned)tiles, 1u, (unsigned)g.groups);
+  if (can_persist && tiles > kResident) {
+    p.persist = 1;
+    p.ntiles = tiles;
+    grid.x = (unsigned)kResident;
+  }
   if (lp) return ring_dispatch<kOutLP, false>(p, grid, g.nl, s);
   return g.out_bf16 ? ring_dispatch<kOutBF16, false>(p, grid, g.nl, s) : ring_dispatch<kOutF32, false>(p, grid, g.nl, s);
 }

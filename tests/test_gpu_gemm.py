@@ -184,6 +184,32 @@ def test_odd_leaf_rank_partitions_are_bitwise_equal(inv, M):
     assert bitwise_equal(inv.tree_combine(P8, inv.contract(leaves=8)), base)
 
 
+@pytest.mark.parametrize("M,N,K,out", [(1100, 3900, 512, "bf16"), (1000, 4100, 1024, "fp32"), (2048, 2100, 768, "bf16")])
+def test_many_tiles_ragged(inv, M, N, K, out):
+    """More output tiles than resident workgroups, ragged in rows and columns:
+    every row is bitwise the same row computed in a small launch, and sampled
+    elements match the oracle's tree."""
+    X = synth.randn((M, K), 121).to(DEV)
+    W = synth.randn((N, K), 122, 0.02).to(DEV)
+    c = inv.contract(leaves=8, out=out)
+    full = inv.gemm(X, W, c)
+    for r0, r1 in ((0, 100), (M - 77, M), (512, 640)):
+        part = inv.gemm(X[r0:r1].contiguous(), W, c)
+        n, bad, dmax = mismatch_report(part, full[r0:r1])
+        assert bad == 0, f"rows {r0}:{r1}: {bad}/{n} mismatches, max {dmax}"
+    rows = np.array([0, 127, 128, 513, M - 1])
+    cols = np.sort(np.random.default_rng(7).choice(N, 64, replace=False))
+    cols[-1] = N - 1
+    Xs = X[torch.as_tensor(rows, device=DEV)].float().cpu().numpy()
+    Ws = W[torch.as_tensor(cols, device=DEV)].float().cpu().numpy()
+    ref = ogemm.gemm_tree(Xs, Ws, 8, out)
+    got = full[torch.as_tensor(rows, device=DEV)][:, torch.as_tensor(cols, device=DEV)]
+    if out == "bf16":
+        check_bf16(got, ref, f"{M}x{N}x{K} sampled")
+    else:
+        check_fp32_gemm(got, ref, f"{M}x{N}x{K} sampled")
+
+
 def test_left_fold_changes_bits(inv, dense_inputs):
     """Teeth: a different combine schedule must move some bits."""
     X, W = dense_inputs[(4096, 12288)]

@@ -190,12 +190,14 @@ def test_fused_swiglu_equals_unfused(inv, T, E, H, F, L):
     assert not torch.isnan(fused[4]).any()
 
 
-@pytest.mark.parametrize("out,K", [("fp32", 768), ("bf16", 512), ("fp32", 256)])
-def test_grouped_gemm_malformed_rows_are_nan(inv, out, K):
+@pytest.mark.parametrize("out,K,T,E,N", [("fp32", 768, 37, 8, 200), ("bf16", 512, 37, 8, 200), ("fp32", 256, 37, 8, 200),
+                                         # more row-tile slots than resident workgroups: each
+                                         # workgroup walks several tiles
+                                         ("bf16", 512, 600, 16, 2000), ("fp32", 512, 600, 16, 1000)])
+def test_grouped_gemm_malformed_rows_are_nan(inv, out, K, T, E, N):
     """A gathered index outside [0, x_rows) gives a NaN output row; every other
     row is bitwise the plain K-leaf GEMM of its gathered input row (both store
     paths of the epilogue, whole and ragged column strips)."""
-    T, E, N = 37, 8, 200
     c = inv.contract(leaves=8, out=out)
     x = synth.randn((T, K), 51).to(DEV)
     W = synth.randn((E, N, K), 52, 0.02).to(DEV)
