@@ -510,6 +510,12 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void gemm_ring_kernel(TileParam
   const uint8_t* A8 = reinterpret_cast<const uint8_t*>(p.A);
   const int cw = __builtin_amdgcn_readfirstlane(wave);
   auto setup = [&](int64_t tile, TileAddr<R::LA, R::LB>& T) -> bool {
+    // An opaque copy of the lane id: without it the compiler hoists every
+    // lane-only term of the set-up and the epilogue out of the tile loop and
+    // keeps them live through the tree (30-60 registers; the grouped fp32
+    // kernel spilled).
+    int lane = tid & 63;
+    asm volatile("" : "+v"(lane));
     int64_t m0, m_end, n0;
     const uint16_t* B = p.B;
     if constexpr (GROUPED) {
@@ -642,6 +648,8 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void gemm_ring_kernel(TileParam
 
   // Epilogue: lane holds rows 4*(lane/16)+r of each 16x16 block, column lane%16.
   auto finish = [&](const TileAddr<R::LA, R::LB>& T, typename Ctx::Acc& acc) {
+    int lane = tid & 63;
+    asm volatile("" : "+v"(lane));
     const int64_t rbase = T.m0 + wm * 64 + 4 * (lane >> 4);
     const int64_t cbase = T.n0 + wn * WN + (lane & 15);
     if constexpr (SWI) {
