@@ -109,10 +109,15 @@ constexpr int kOutF32 = 0, kOutBF16 = 1, kOutLP = 2, kOutSwiGLU = 3;
 // of bank conflicts: 4 * STRIDE / 4 steps through all 16 four-bank groups.
 constexpr int kLpStride = 68;
 
-template <int NB, int STRIDE = kLpStride>  // 16-column blocks per row held by the wave; row stride
+// SWZ: rows of 32 floats whose 16-byte granule g is stored at g ^ (row % 8)
+// (the wave's spill slice), so that 8 lanes reading the same granule of 8
+// consecutive rows hit distinct banks.
+template <int NB, int STRIDE = kLpStride, bool SWZ = false>  // 16-column blocks per row held by the wave; row stride
 __device__ __forceinline__ void lp_rows_epilogue(const TileParams& p, const float* t, int64_t row, bool row_ok,
                                                  int64_t col0, int lane) {
+  static_assert(!SWZ || STRIDE == 32, "the swizzled layout has 32-float rows");
   const float* mine = t + lane * STRIDE;
+  auto at = [&](int col) { return SWZ ? ((((col >> 2) ^ (lane & 7)) << 2) | (col & 3)) : col; };
   const int64_t nb = (p.N + 15) / 16;
   const int32_t tgt = row_ok ? p.lp_target[row] : -1;
 #pragma unroll
@@ -121,7 +126,7 @@ __device__ __forceinline__ void lp_rows_epilogue(const TileParams& p, const floa
     float v[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const float4 f = *reinterpret_cast<const float4*>(mine + 16 * j + 4 * q);
+      const float4 f = *reinterpret_cast<const float4*>(mine + at(16 * j + 4 * q));
       v[4 * q] = f.x;
       v[4 * q + 1] = f.y;
       v[4 * q + 2] = f.z;
@@ -136,7 +141,7 @@ __device__ __forceinline__ void lp_rows_epilogue(const TileParams& p, const floa
     }
   }
   if (row_ok && (int64_t)tgt >= col0 && (int64_t)tgt < col0 + 16 * NB && (int64_t)tgt < p.N)
-    p.lp_tlogit[row] = mine[tgt - col0];
+    p.lp_tlogit[row] = mine[at((int)(tgt - col0))];
 }
 
 // ---------------------------------------------------------------- ring kernel
@@ -491,7 +496,7 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void gemm_ring_kernel(TileParam
   // run on into the next tile's stages (8 leaves on 64-k stages).
   // (Odd-multiple-of-32 leaves are left out: their tree already fills the
   // registers, and carrying the next tile's addressing spills.)
-  constexpr bool PERSIST_OK = NL == 8 && BK == 64 && OUTM != kOutLP && !ODD;
+  constexpr bool PERSIST_OK = NL == 8 && BK == 64 && !ODD;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -718,17 +723,34 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void gemm_ring_kernel(TileParam
       return;
     }
     if constexpr (OUTM == kOutLP) {
-      block_barrier();  // every wave has consumed its last ring stage
-      float* t = reinterpret_cast<float*>(lds) + wave * 64 * LPS;
-  #pragma unroll
-      for (int i = 0; i < 4; ++i)
-  #pragma unroll
-        for (int j = 0; j < FN; ++j)
-  #pragma unroll
-          for (int r = 0; r < 4; ++r) t[(16 * i + 4 * (lane >> 4) + r) * LPS + 16 * j + (lane & 15)] = acc.v[i][j][r];
-      // the wave reads back only what it wrote; its LDS accesses complete in order
       const int64_t row = T.m0 + wm * 64 + lane;
-      lp_rows_epilogue<FN, LPS>(p, t, row, row < T.m_end, T.n0 + wn * WN, lane);
+      if constexpr (SPILL > 0) {
+        // the wave's own spill slice, 64 rows of 32 floats, granules swizzled
+        // by the row (free once the tree is summed; no barrier)
+        static_assert(WN == 32, "32-float rows");
+        float* t = reinterpret_cast<float*>(&lds[R::NS * R::STAGE]) + wave * 64 * WN;
+  #pragma unroll
+        for (int i = 0; i < 4; ++i)
+  #pragma unroll
+          for (int j = 0; j < FN; ++j)
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int rr = 16 * i + 4 * (lane >> 4) + r, col = 16 * j + (lane & 15);
+              t[rr * 32 + ((((col >> 2) ^ (rr & 7)) << 2) | (col & 3))] = acc.v[i][j][r];
+            }
+        lp_rows_epilogue<FN, 32, true>(p, t, row, row < T.m_end, T.n0 + wn * WN, lane);
+      } else {
+        block_barrier();  // every wave has consumed its last ring stage
+        float* t = reinterpret_cast<float*>(lds) + wave * 64 * LPS;
+  #pragma unroll
+        for (int i = 0; i < 4; ++i)
+  #pragma unroll
+          for (int j = 0; j < FN; ++j)
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) t[(16 * i + 4 * (lane >> 4) + r) * LPS + 16 * j + (lane & 15)] = acc.v[i][j][r];
+        // the wave reads back only what it wrote; its LDS accesses complete in order
+        lp_rows_epilogue<FN, LPS>(p, t, row, row < T.m_end, T.n0 + wn * WN, lane);
+      }
       return;
     }
     if constexpr (OUTM == kOutBF16 || OUTM == kOutF32) {
@@ -1151,7 +1173,7 @@ hipError_t launch_gemm(const GemmLaunch& g, hipStream_t s) {
   // + 256, ..., and its ring runs on from each tile into the next, so no tile
   // pays the pipeline's fill or a workgroup launch.
   constexpr int64_t kResident = 256;
-  const bool can_persist = g.nl == 8 && g.kl % 64 == 0 && !lp && g.groups == 1;
+  const bool can_persist = g.nl == 8 && g.kl % 64 == 0 && g.groups == 1;
   if (lp && (g.offsets || g.groups != 1)) return hipErrorInvalidValue;  // statistics need whole trees
   if (g.swiglu && (!g.offsets || g.groups != 1 || g.N % 2 != 0)) return hipErrorInvalidValue;
 
