@@ -71,6 +71,11 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
 #endif
 }
 
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 template <int CH>
 __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a, float scale) {
   using Cfg = AttnCfg<CH>;
@@ -139,33 +144,45 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a, float scal
 #pragma unroll
   for (int db = 0; db < 8; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t c = c0; c < c1; ++c) {
-    const int64_t kbase = c * CH;  // position of the chunk's first key
-    // ---- K fragments (A operand: key rows, k = d)
-    bf16x8 kf[Cfg::KB][4];
+  // Loads of chunk c + 1 are issued while chunk c computes: its K fragments
+  // right after the score MFMAs have read chunk c's (same registers), its V
+  // rows right after the P.V reads of chunk c's (same LDS buffer). Keys past
+  // L read a clamped valid key: score row j of the MFMA below depends only
+  // on key row j, and those rows' scores are set to -inf; a clamped V row's
+  // p is exactly 0 and its values are finite cache data. K and V are read
+  // once per (sequence, kv head, split): streaming loads.
+  bf16x8 kf[Cfg::KB][4];
+  auto load_k = [&](int64_t cc) {
 #pragma unroll
     for (int kb = 0; kb < Cfg::KB; ++kb) {
-      // Keys past L read a clamped valid key: score row j of the MFMA below
-      // depends only on key row j, and those rows' scores are set to -inf.
-      // K and V are read once per (sequence, kv head, split): streaming loads.
-      const int64_t pos = min(kbase + kb * 16 + c16, L - 1);
+      const int64_t pos = min(cc * CH + kb * 16 + c16, L - 1);
       const uint16_t* kp = K + (start + pos) * kv_row + (int64_t)kvh * kD + 8 * g4;
 #pragma unroll
       for (int ds = 0; ds < 4; ++ds)
         kf[kb][ds] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + ds * 32)));
     }
-    // ---- V rows straight into LDS (keys past L load a clamped valid key:
-    //      their p is exactly 0, and the key's values are finite cache data)
+  };
+  auto load_v = [&](int64_t cc) {
 #if defined(__HIP_DEVICE_COMPILE__)
 #pragma unroll
     for (int i = 0; i < Cfg::VDMA; ++i) {
       const int key = 4 * i + (lane >> 4);
       const int slot = lane & 15;
-      const int64_t pos = min(kbase + key, L - 1);
+      const int64_t pos = min(cc * CH + key, L - 1);
       const uint8_t* src = Vb + ((start + pos) * kv_row + (int64_t)kvh * kD) * 2 + vswz(key, slot) * 16;
       __builtin_amdgcn_global_load_lds(src, &vs[i * 1024], 16, 0, kNT);
     }
+#else
+    (void)cc;
 #endif
+  };
+  if (c0 < c1) {
+    load_k(c0);
+    load_v(c0);
+  }
+  for (int64_t c = c0; c < c1; ++c) {
+    const int64_t kbase = c * CH;  // position of the chunk's first key
+    const bool more = c + 1 < c1;   // uniform
     // ---- S^T = K Q^T: lane holds keys kb*16 + 4*g4 + r for head c16
     f32x4 st[Cfg::KB];
 #pragma unroll
@@ -175,6 +192,7 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a, float scal
       for (int ds = 0; ds < 4; ++ds) acc = mfma16(kf[kb][ds], qf[ds], acc);
       st[kb] = acc;
     }
+    if (more) load_k(c + 1);
     float cmax = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < Cfg::KB; ++kb)
@@ -221,7 +239,10 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a, float scal
     for (int db = 0; db < 8; ++db)
 #pragma unroll
       for (int r = 0; r < 4; ++r) o[db][r] = o[db][r] * al[r];
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's V rows are in LDS
+    // this wave's V rows of chunk c are in LDS once at most the next chunk's
+    // K loads (issued after them) are outstanding
+    if (more) wait_vm<Cfg::KB * 4>();
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
     for (int t = 0; t < Cfg::PV; ++t) {
       // A operand: head c16, keys {32t + 4 g4 + e} (e < 4) and {32t + 16 + 4 g4 + e - 4}
@@ -254,6 +275,7 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a, float scal
       }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // V reads done before the next chunk's loads land
+    if (more) load_v(c + 1);
   }
 
   // ---- split state: o (rows = heads 4 g4 + r, col d = 16 db + c16), m, l (head c16)
