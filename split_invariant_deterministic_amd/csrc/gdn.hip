@@ -664,14 +664,19 @@ __global__ __launch_bounds__(256) void gdn_output_kernel(GdnArgs a) {
   float S[8][8];
   load_state(S, a.bstates + (c * a.H + h) * plane, T);
   const int64_t ta = t0 + j * C, tb = min(t0 + (j + 1) * C, t0 + len);
-  TokIn cur, nxt;
-  load_tok(cur, a, ta, h, T);
-  for (int64_t t = ta; t < tb; ++t) {
-    if (t + 1 < tb) load_tok(nxt, a, t + 1, h, T);
+  // Two token buffers in turn (the loop is unrolled by two), each loaded one
+  // token ahead: no register copies between steps.
+  TokIn ta_in, tb_in;
+  load_tok(ta_in, a, ta, h, T);
+  for (int64_t t = ta; t < tb; t += 2) {
+    if (t + 1 < tb) load_tok(tb_in, a, t + 1, h, T);
     float o8[8];
-    rec_step(S, cur.k8, cur.q8, cur.v8, cur.a, cur.b, o8);
+    rec_step(S, ta_in.k8, ta_in.q8, ta_in.v8, ta_in.a, ta_in.b, o8);
     store_out<OUT_BF16>(a.out, (t * a.H + h) * kD, o8, T);
-    if (t + 1 < tb) cur = nxt;
+    if (t + 1 >= tb) break;
+    if (t + 2 < tb) load_tok(ta_in, a, t + 2, h, T);
+    rec_step(S, tb_in.k8, tb_in.q8, tb_in.v8, tb_in.a, tb_in.b, o8);
+    store_out<OUT_BF16>(a.out, ((t + 1) * a.H + h) * kD, o8, T);
   }
   // the open chunk of the last slot continues in decode
   if (a.cache && tb == t0 + len && len % C != 0) {
