@@ -163,6 +163,15 @@ __device__ __forceinline__ void lp_rows_epilogue(const TileParams& p, const floa
 // Rows past M and columns past N load a clamped valid row instead of zeros;
 // row m of an MFMA result depends only on row m of A (and column n only on
 // row n of B), so those rows never touch a stored output.
+//
+// With 8 leaves (64-k stages) and more tiles than the 256 CUs hold, the
+// launch is persistent: workgroup b walks tiles b, b + 256, ...; the next
+// tile's addressing is set up before the current tree runs, and the issue
+// side of the ring switches to it after the current tile's last stage, so
+// the next tile's first stages load while the tree and the epilogue finish.
+// The epilogue then transposes through the wave's own spill slice instead
+// of the ring. Every output element's chain and tree are the same as in a
+// one-tile-per-workgroup launch.
 
 // Waves per ring workgroup: 8 waves, each 64 rows x 32 columns of the
 // 128 x 128 tile (4 x 2 MFMA blocks of 16 x 16).
