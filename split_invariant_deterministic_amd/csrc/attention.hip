@@ -150,7 +150,10 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a, float scal
   // L read a clamped valid key: score row j of the MFMA below depends only
   // on key row j, and those rows' scores are set to -inf; a clamped V row's
   // p is exactly 0 and its values are finite cache data. K and V are read
-  // once per (sequence, kv head, split): streaming loads.
+  // once per (sequence, kv head, split). V's direct loads (1 KB of whole
+  // lines each) stream past the caches; K's fragment loads take 64 bytes of
+  // each 128-byte line per instruction, the other half one instruction
+  // later, so they keep the default policy and the second half hits.
   bf16x8 kf[Cfg::KB][4];
   auto load_k = [&](int64_t cc) {
 #pragma unroll
@@ -159,7 +162,7 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a, float scal
       const uint16_t* kp = K + (start + pos) * kv_row + (int64_t)kvh * kD + 8 * g4;
 #pragma unroll
       for (int ds = 0; ds < 4; ++ds)
-        kf[kb][ds] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + ds * 32)));
+        kf[kb][ds] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kp + ds * 32));
     }
   };
   auto load_v = [&](int64_t cc) {
