@@ -24,6 +24,16 @@ synthetic input, every stage in the library's HIP kernels:
           the MoE layer run as 4 and 16 contiguous token splits; the LM head +
           logprob at M = 1 and 64 (fused, unfused and the fast path); a 1 GiB copy
 
+After the timed steps (never inside them): an ``invariance`` report, GPU
+against GPU and counted element by element -- batch size (prefixes and
+single rows against the 4096-token batch), emulated rank partitions of the
+GEMM leaves and of the key splits, prefill against decode (attention and
+Gated DeltaNet), MoE token splits, and 20 more whole steps against the last
+timed one; a ``device`` record (CU count, clocks, and the MFMA ceiling: a
+register-only loop of the path's MFMA instruction with the shader clock it
+held); and ``cpu_oracle_configs``, the oracle timed per configuration on
+bounded samples beside ``cpu_baseline``.
+
 Inputs are resident in HBM before the timed region. ``value`` is the
 invariant GEMM throughput of the dense stage (its FLOPs over the time of its
 two GEMM launches, HIP events on the launch stream); the logprob tokens/s,
@@ -55,6 +65,9 @@ def parse():
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--invariance-repeats", type=int, default=20,
+                   help="whole steps repeated after the timed ones and compared bitwise with the last "
+                        "(-1 skips the invariance report)")
     p.add_argument("--stages", default="dense,norm,attn,moe,lmhead,gdn,sweep",
                    help="comma list of dense,norm,attn,moe,lmhead,gdn,sweep (all by default); "
                         "'copy' adds a plain 1 GiB device copy used only to calibrate traffic counters")
@@ -228,7 +241,7 @@ def sweep(torch, inv, synth, X, W_up, W_down, gamma, att, moe, lm, c8, cn, ca, d
     return out
 
 
-def cpu_baseline(dense_X, W_up, W_down, target_s=15.0):
+def cpu_baseline(dense_X, W_up, W_down, target_s=12.0):
     """The oracle's 8-leaf GEMM schedule on a bounded row sample of both dense
     projections (TFLOP/s of useful GEMM work, the unit of ``value``). A 32-row
     probe sizes the sample to about ``target_s`` seconds of host work."""
@@ -260,6 +273,282 @@ def cpu_baseline(dense_X, W_up, W_down, target_s=15.0):
             "sample": f"{reps} pass(es) of {rows} of {dense_X.shape[0]} token rows through both dense "
                       f"projections (4096->12288->4096), 8-leaf fp32 tree schedule with float64 leaf "
                       f"sums, {dt:.1f} s"}
+
+
+def _cmp(torch, a, b):
+    """(elements compared, mismatched elements, max |a - b|) of two tensors of
+    one dtype, bit patterns compared (NaN equals NaN only with the same bits)."""
+    if a.dtype == torch.bfloat16:
+        neq = a.view(torch.int16) != b.view(torch.int16)
+    elif a.dtype == torch.float32:
+        neq = a.view(torch.int32) != b.view(torch.int32)
+    else:
+        neq = a != b
+    d = (a.float() - b.float()).abs().nan_to_num(0.0)
+    return int(a.numel()), int(neq.sum()), float(d.max()) if a.numel() else 0.0
+
+
+class Tally:
+    """Mismatch counts per invariance check, summed over its comparisons."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.rows = {}
+
+    def add(self, name, a, b, what=""):
+        n, bad, dmax = _cmp(self.torch, a, b)
+        r = self.rows.setdefault(name, {"compared": 0, "mismatched": 0, "max_abs_diff": 0.0, "cases": []})
+        r["compared"] += n
+        r["mismatched"] += bad
+        r["max_abs_diff"] = max(r["max_abs_diff"], dmax)
+        if what and what not in r["cases"]:
+            r["cases"].append(what)
+
+    def report(self):
+        tot = sum(r["compared"] for r in self.rows.values())
+        bad = sum(r["mismatched"] for r in self.rows.values())
+        return {"elements_compared": tot, "elements_mismatched": bad, "checks": self.rows}
+
+
+def invariance(torch, inv, synth, step, last, ctx, stages, repeats=20):
+    """Bitwise invariance of the step's outputs, GPU against GPU, counted:
+    batch size (prefixes and single rows vs the 4096-token batch), emulated
+    rank partitions of the GEMM leaves, split-KV rank partitions, prefill vs
+    decode, MoE token splits, and ``repeats`` more whole steps against the
+    timed run's last step."""
+    tl = Tally(torch)
+    dev = ctx["dev"]
+    if "lmhead" in stages:
+        lm, gamma, lp_full = ctx["lm"], ctx["gamma"], last["logprob"]
+        c8f, c64, cn = inv.contract(leaves=8, out="fp32"), inv.contract(leaves=64), inv.contract(leaves=1)
+        for M in (1, 7, 64, 512):
+            hn = inv.rmsnorm(lm["h"][:M].contiguous(), gamma, cn)
+            lg = inv.gemm(hn, lm["W"], c8f)
+            tl.add("logprob_batch_vs_4096", inv.logprob(lg, lm["targets"][:M].contiguous(), c64), lp_full[:M],
+                   f"M={M} prefix")
+            del lg
+        for i in (1000, 4095):
+            hn = inv.rmsnorm(lm["h"][i:i + 1].contiguous(), gamma, cn)
+            lg = inv.gemm(hn, lm["W"], c8f)
+            tl.add("logprob_batch_vs_4096", inv.logprob(lg, lm["targets"][i:i + 1].contiguous(), c64),
+                   lp_full[i:i + 1], f"row {i} alone")
+    if "dense" in stages:
+        X, W_up, W_down, gamma, b_full = ctx["X"], ctx["W_up"], ctx["W_down"], ctx["gamma"], last["dense"]
+        cn = inv.contract(leaves=1)
+        yx = inv.rmsnorm(X, gamma, cn)
+        a_full = inv.gemm(yx, W_up, inv.contract(leaves=8))
+        for R in (2, 4, 8):
+            cr = inv.contract(leaves=8, ranks=R)
+            tl.add("dense_gemm_rank_partitions", inv.gemm(yx, W_up, cr), a_full, f"R={R} (4096x12288x4096)")
+            tl.add("dense_gemm_rank_partitions", inv.gemm(a_full, W_down, cr), b_full, f"R={R} (4096x4096x12288)")
+        for M in (1, 7, 64, 512):
+            am = inv.gemm(yx[:M].contiguous(), W_up, inv.contract(leaves=8))
+            tl.add("dense_batch_vs_4096", inv.gemm(am, W_down, inv.contract(leaves=8)), b_full[:M], f"M={M} prefix")
+        del yx, a_full
+    if "attn" in stages:
+        att, ca, o_full = ctx["att"], ctx["ca"], last["attn"]
+        for R in (2, 4, 8):
+            ws = inv.attn_workspace(att["q"], ca)
+            for r in range(R):
+                inv.attn_splits(att["q"], att["k"], att["v"], att["cu_seqlens"], att["q_seq"], att["q_pos"],
+                                r * 16 // R, (r + 1) * 16 // R, ca, ws)
+            tl.add("attn_split_kv_rank_partitions", inv.attn_combine(ws, att["q"].shape[0], 32, 128, ca), o_full,
+                   f"R={R}")
+        cu = att["cu_seqlens"]
+        for B in (1, 8, 64):
+            L = int(cu[B])
+            o = inv.decode_attn(att["q"][:B].contiguous(), att["k"][:L], att["v"][:L], cu[:B + 1], att["q_seq"][:B],
+                                att["q_pos"][:B], ca)
+            tl.add("attn_batch_vs_256", o, o_full[:B], f"B={B} prefix")
+        # prefill vs decode: each of 8 sequences as a prefill block of its last 48 positions (the last row's
+        # query is the decode query); the decode rows must equal the prefill block's last rows
+        qp_all, seq_all, q_all = [], [], []
+        for sidx in range(8):
+            Ls = int(cu[sidx + 1] - cu[sidx])
+            pos = torch.arange(max(0, Ls - 48), Ls, dtype=torch.int32, device=dev)
+            qb = synth.randn((pos.numel(), 32, 128), 777 + sidx, device=dev)
+            qb[-1] = att["q"][sidx]
+            q_all.append(qb)
+            qp_all.append(pos)
+            seq_all.append(torch.full_like(pos, sidx))
+        qpre = torch.cat(q_all).contiguous()
+        opre = inv.decode_attn(qpre, att["k"], att["v"], cu, torch.cat(seq_all), torch.cat(qp_all), ca)
+        lastrow = torch.cumsum(torch.tensor([q.shape[0] for q in q_all], device=dev), 0) - 1
+        tl.add("attn_prefill_vs_decode", opre[lastrow], o_full[:8], "8 sequences, 48-row prefill blocks")
+    if "moe" in stages:
+        moe, m_full = ctx["moe"], last["moe"]
+        c8 = inv.contract(leaves=8)
+        T = moe["x"].shape[0]
+        for S in (4, 16):
+            n = T // S
+            parts = [inv.moe_layer(moe["x"][i * n:(i + 1) * n].contiguous(),
+                                   moe["logits"][i * n:(i + 1) * n].contiguous(), moe["W1"], moe["W2"], c8, c8)
+                     for i in range(S)]
+            tl.add("moe_token_splits", torch.cat(parts), m_full, f"{S} splits vs 1")
+            del parts
+    if "gdn" in stages:
+        cg = inv.contract(kv_chunk=64, out="bf16")
+        gd = synth.gdn([2048] * 2, H=16, seed=3, device=dev)
+        full = inv.gdn_prefill(gd["q"], gd["k"], gd["v"], gd["g"], gd["beta"], gd["cu_seqlens"], cg)
+        for P in (1000, 1024):   # prefill P tokens of each sequence, then decode the rest token by token
+            cu2 = torch.tensor([0, P, 2 * P], dtype=torch.int32, device=dev)
+            idx = torch.cat([torch.arange(0, P, device=dev), torch.arange(2048, 2048 + P, device=dev)])
+            cache = inv.gdn_cache(cg, 2, 16, dev)
+            inv.gdn_prefill(gd["q"][idx].contiguous(), gd["k"][idx].contiguous(), gd["v"][idx].contiguous(),
+                            gd["g"][idx].contiguous(), gd["beta"][idx].contiguous(), cu2, cg, cache=cache)
+            outs = []
+            for t in range(P, P + 64):
+                ti = torch.tensor([t, 2048 + t], device=dev)
+                pos = torch.full((2,), t, dtype=torch.int32, device=dev)
+                outs.append(inv.gdn_decode(gd["q"][ti].contiguous(), gd["k"][ti].contiguous(),
+                                           gd["v"][ti].contiguous(), gd["g"][ti].contiguous(),
+                                           gd["beta"][ti].contiguous(), pos, cache, cg))
+            dec = torch.stack(outs, 1)  # [2, 64, H, 128]
+            ref = torch.stack([full[P:P + 64], full[2048 + P:2048 + P + 64]])
+            tl.add("gdn_prefill_then_decode_vs_prefill", dec, ref, f"prefill {P} + 64 decode tokens")
+    base = {k: v.clone() for k, v in last.items()}
+    for _ in range(repeats):
+        o = step()
+        for k in base:
+            tl.add("repeated_steps", o[k], base[k], f"{repeats} more steps: {', '.join(sorted(base))}")
+    torch.cuda.synchronize()
+    rep = tl.report()
+    rep["repeats"] = repeats
+    return rep
+
+
+def cpu_oracle_configs(ctx, stages, budget_s=3.0):
+    """The oracle as it stands, timed end to end per configuration on bounded
+    samples of the same inputs (each about ``budget_s`` seconds or one pass)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import attention as oatt
+    from oracle import gemm as ogemm
+    from oracle import logprob as olp
+    from oracle import moe as omoe
+    from oracle import rmsnorm as orms
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    out = {"cores": threads, "kind": "oracle"}
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        n = 0
+        while True:
+            fn()
+            n += 1
+            dt = time.perf_counter() - t0
+            if dt >= budget_s or n >= 20:
+                return dt / n
+
+    if "dense" in stages or "norm" in stages:
+        x = ctx["X"][:512].float().cpu().numpy()
+        g = ctx["gamma"].float().cpu().numpy()
+        t = timed(lambda: orms.rmsnorm(x, g, 1e-6))
+        out["rmsnorm"] = {"tokens_per_s": round(512 / t, 1), "gbs": round(512 * 4 * 4096 / t / 1e9, 4),
+                          "sample": "512 rows x 4096, fp64 definition + bf16 cast"}
+    if "lmhead" in stages:
+        lm = ctx["lm"]
+        W = lm["W"]
+        V, K = W.shape
+        h = lm["h"][:4].float().cpu().numpy()
+        blk = 16384
+        Wb = W[:blk].float().cpu().numpy()
+        t = timed(lambda: ogemm.gemm_tree(h, Wb, 8, "fp32"))
+        per_tok = t * V / blk / 4
+        out["lm_head_gemm"] = {"tokens_per_s": round(1.0 / per_tok, 4),
+                               "tflops": round(2.0 * 4 * blk * K / t / 1e12, 5),
+                               "sample": f"4 rows x {blk} of {V} vocabulary rows, 8-leaf fp32 tree schedule "
+                                         f"(float64 leaves); per-token rate scaled to the full vocabulary"}
+        rng = np.random.default_rng(0)
+        lg = rng.normal(size=(64, V)) * 1.3
+        tg = rng.integers(0, V, size=64)
+        t = timed(lambda: (olp.logprob(lg, tg), olp.merge_tree(*olp.chunk_stats(lg, 64))))
+        out["logprob"] = {"tokens_per_s": round(64 / t, 2), "gbs": round(64 * 4.0 * V / t / 1e9, 4),
+                          "sample": f"64 rows x {V} logits: plain fp64 definition + the 64-chunk tree"}
+    if "attn" in stages:
+        att = ctx["att"]
+        cu = att["cu_seqlens"].cpu()
+        B = 2
+        L = int(cu[B])
+        q = att["q"][:B].float().cpu().numpy()
+        k = att["k"][:L].float().cpu().numpy()
+        v = att["v"][:L].float().cpu().numpy()
+        t = timed(lambda: oatt.attention(q, k, v, cu[:B + 1].numpy(), att["q_seq"][:B].cpu().numpy(),
+                                         att["q_pos"][:B].cpu().numpy(), 8))
+        out["decode_attn"] = {"kv_tokens_per_s": round(L / t, 1), "gbs": round(4096.0 * L / t / 1e9, 4),
+                              "sample": f"decode rows of the first {B} sequences ({L} keys), fp64 softmax"}
+    if "moe" in stages:
+        moe = ctx["moe"]
+        Tm = 16
+
+        class _E:
+            def __init__(self, W):
+                self.W, self.shape = W, tuple(W.shape)
+
+            def __getitem__(self, e):
+                return self.W[int(e)].float().cpu().numpy().astype(np.float64)
+        x = moe["x"][:Tm].float().cpu().numpy().astype(np.float64)
+        lg = moe["logits"][:Tm].double().cpu().numpy()
+        t = timed(lambda: omoe.moe_layer(x, lg, _E(moe["W1"]), _E(moe["W2"]), 8))
+        out["moe_layer"] = {"tokens_per_s": round(Tm / t, 2),
+                            "tflops": round(2.0 * Tm * 8 * (1536 * 2048 + 2048 * 768) / t / 1e12, 5),
+                            "sample": f"{Tm} tokens through route, expert FFNs and combine (fp64)"}
+    return out
+
+
+def device_record(torch, inv):
+    """CU count, clocks and the MFMA ceiling of the device the run used."""
+    import subprocess
+    p = torch.cuda.get_device_properties(0)
+    rec = {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
+           "hbm_gib": round(p.total_memory / 2 ** 30, 1)}
+    for cmd, key in ((["rocm-smi", "--showclocks"], "rocm_smi_clocks"), (["rocminfo"], "rocminfo")):
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=30)
+            lines = r.stdout.splitlines()
+            if key == "rocminfo":
+                # the GPU agent's section (rocminfo lists the host CPUs first)
+                sec, secs = [], []
+                for l in lines:
+                    if l.startswith("Agent "):
+                        secs.append(sec)
+                        sec = []
+                    sec.append(l)
+                secs.append(sec)
+                for sec in secs:
+                    if any("gfx950" in l for l in sec):
+                        for l in sec:
+                            if "Max Clock Freq" in l:
+                                rec["max_clock_mhz"] = l.split(":", 1)[1].strip()
+                            if "Compute Unit" in l:
+                                rec["rocminfo_compute_units"] = l.split(":", 1)[1].strip()
+                        break
+            else:
+                rec[key] = [l.strip() for l in lines if "sclk" in l or "mclk" in l or "fclk" in l][:6]
+        except Exception as e:  # the record is context; its absence is reported, not fatal
+            rec[key] = f"unavailable: {type(e).__name__}"
+    # the MFMA ceiling: register-only chains of the path's bf16 instruction, 4 workgroups per CU
+    groups, iters = 4 * p.multi_processor_count, 20000
+    best = None
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        clk, fl = inv.bench_mfma_loop(iters, groups)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        c = clk.cpu().double()
+        mhz = float((c[:, 0] / c[:, 1]).median() * 100.0)
+        if best is None or ms < best[0]:
+            best = (ms, fl, mhz)
+    ms, fl, mhz = best
+    rec["mfma_ceiling"] = {"tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                           "frac_of_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                           "shader_clock_mhz_during_loop": round(mhz, 1),
+                           "kernel": "8 waves per workgroup, 8 independent v_mfma_f32_16x16x32_bf16 chains "
+                                     "per wave, register operands only"}
+    return rec
 
 
 def recorded_traffic():
@@ -337,6 +626,7 @@ def main():
     b = torch.empty((M, Hd), dtype=torch.bfloat16, device=dev)
 
     def step():
+        outs = {}
         if "dense" in stages:
             T.start("rmsnorm")
             inv.rmsnorm(X, gamma, cn, out=y)
@@ -345,6 +635,7 @@ def main():
             inv.gemm(y, W_up, c8, out=a)
             inv.gemm(a, W_down, c8, out=b)
             T.stop("gemm_dense")
+            outs["dense"] = b
         if "norm" in stages:
             T.start("rmsnorm_bw")
             inv.rmsnorm(xn, gamma, cn, out=yn)
@@ -355,12 +646,12 @@ def main():
             T.stop("copy")
         if "attn" in stages:
             T.start("attn")
-            inv.decode_attn(att["q"], att["k"], att["v"], att["cu_seqlens"], att["q_seq"], att["q_pos"], ca,
-                            ws=att_ws)
+            outs["attn"] = inv.decode_attn(att["q"], att["k"], att["v"], att["cu_seqlens"], att["q_seq"],
+                                           att["q_pos"], ca, ws=att_ws)
             T.stop("attn")
         if "moe" in stages:
             T.start("moe")
-            inv.moe_layer(moe["x"], moe["logits"], moe["W1"], moe["W2"], c8, c8)
+            outs["moe"] = inv.moe_layer(moe["x"], moe["logits"], moe["W1"], moe["W2"], c8, c8)
             T.stop("moe")
         if "lmhead" in stages:
             T.start("lm_rmsnorm")
@@ -370,8 +661,9 @@ def main():
             inv.gemm(hn, lm["W"], c8f, out=logits)
             T.stop("gemm_lmhead")
             T.start("logprob")
-            inv.logprob(logits, lm["targets"], c64)
+            outs["logprob"] = inv.logprob(logits, lm["targets"], c64)
             T.stop("logprob")
+        return outs
 
     for _ in range(args.warmup):
         step()
@@ -381,7 +673,7 @@ def main():
     t0 = time.perf_counter()
     for _ in range(args.steps):
         T.start("step")
-        step()
+        last = step()
         T.stop("step")
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -452,6 +744,21 @@ def main():
                    moe if "moe" in stages else None, lm if "lmhead" in stages else None, c8, cn,
                    ca if "attn" in stages else None, dev)
         log("shape sweep done")
+
+    # ------------------------------------------------------------ invariance (outside the timed steps)
+    ctx = {"dev": dev, "X": X, "W_up": W_up, "W_down": W_down, "gamma": gamma}
+    if "lmhead" in stages:
+        ctx["lm"] = lm
+    if "attn" in stages:
+        ctx.update(att=att, ca=ca)
+    if "moe" in stages:
+        ctx["moe"] = moe
+    inv_rep = None
+    if args.invariance_repeats >= 0:
+        inv_rep = invariance(torch, inv, synth, step, last, ctx, stages, repeats=args.invariance_repeats)
+        log(f"invariance: {inv_rep['elements_mismatched']} of {inv_rep['elements_compared']} elements differ")
+    dev_rec = device_record(torch, inv)
+    log("device record and MFMA ceiling done")
 
     # ------------------------------------------------------------ fast paths
     Tf = Timer(torch)
@@ -574,6 +881,9 @@ def main():
     result["rooflines"] = rl
     if sw is not None:
         result["sweep"] = sw
+    if inv_rep is not None:
+        result["invariance"] = inv_rep
+    result["device"] = dev_rec
     result["stage_ms"] = {k: round(v, 4) for k, v in ms.items()}
     result["fast_ms"] = {k: round(v, 4) for k, v in fast.items()}
     result["overhead_vs_fast"] = {k: round(v, 3) for k, v in overhead.items()}
@@ -581,6 +891,8 @@ def main():
     if not args.no_cpu_baseline and "dense" in stages:
         log("timing the CPU oracle on a row sample")
         result["cpu_baseline"] = cpu_baseline(X, W_up, W_down)
+        log("timing the CPU oracle per configuration")
+        result["cpu_oracle_configs"] = cpu_oracle_configs(ctx, stages)
     print(json.dumps(result), flush=True)
 
 

@@ -213,7 +213,8 @@ inv_status inv_sha256(const void* data, size_t bytes, uint8_t digest[32]);
  *
  * A [M,K] bf16, B [N,K] bf16 (the weight, K contiguous: logical K x N),
  * C [M,N] out_dtype (bf16 by round-to-nearest-even, or fp32).
- * Leaf l covers k in [l*K/L, (l+1)*K/L); K % L == 0 and (K/L) % 32 == 0.
+ * Leaf l covers k in [l*K/L, (l+1)*K/L); K % L == 0 and (K/L) % 32 == 0;
+ * K < 2^24 (else INV_E_UNSUPPORTED; this holds for every GEMM entry point).
  * Inside a leaf the sum runs in ascending steps of 32 k on one fixed MFMA
  * instruction (v_mfma_f32_16x16x32_bf16) with one fixed k-to-lane map, for
  * every M, N, tile shape and rank split; the leaves are then combined by the
@@ -353,8 +354,9 @@ inv_status inv_attn_combine(const inv_contract* c, const void* ws, size_t ws_byt
 
 /* ------------------------------------------------------------------------
  * Mixture-of-experts layer ([IsoExec] "Unified model": deterministic routing
- * and combination; [IsoExec] "Parallelism-invariant kernels": expert outputs
- * combined in a fixed routing order, not rank order; [IsoExec] "Unified
+ * and combination; [IsoExec] "Parallelism-invariant kernels": a token's
+ * expert results are summed in an order set by the routing, independent of
+ * which rank computed them; [IsoExec] "Unified
  * execution contract", the moe.combine entry with 8 fp32 leaves; [RLK]
  * section 7, packed gate/up GEMM, SwiGLU and down GEMM as separate stages)
  * ------------------------------------------------------------------------ */
@@ -420,11 +422,12 @@ inv_status inv_logprob_block16(const inv_contract* c, const float* logits, int64
  * Gated DeltaNet under the chunkwise-parallel recurrent (CPR) schedule.
  *
  * [IsoExec] "Chunkwise-parallel recurrent (CPR) GDN" ([NovaSky] "Solving the
- * linear-attention headache"): the recurrence is the function; a first pass
- * computes the state at every chunk boundary, a parallel pass runs the
- * recurrence inside each chunk from its boundary state, and decode runs the
- * recurrence but resynchronises to the boundary state every C tokens, so
- * prefill, training forward and decode share one rounding schedule. The
+ * linear-attention headache"). The token recurrence defines the layer.
+ * Prefill obtains the state at each multiple of C with a separate boundary
+ * pass and evaluates the chunks' tokens independently, each chunk from its
+ * opening state; decode steps the recurrence and, when a chunk completes,
+ * swaps its running state for the boundary state. Prefill, training forward
+ * and decode thus round identically. The
  * layer (the gated delta rule, restated; the pages give no formulas), per
  * head with key and value width D = 128:
  *   k^ = k / sqrt(sum k^2 + 1e-6), q^ = q / sqrt(sum q^2 + 1e-6) / sqrt(128)
@@ -516,6 +519,23 @@ inv_status inv_swiglu(const inv_contract* c, const void* GU, void* Aout, int64_t
 inv_status inv_moe_combine(const inv_contract* c, const float* Y, const float* w,
                            const int32_t* slot, int64_t y_rows, void* out, int64_t T, int64_t H,
                            hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Measurement helper (not a step of the forward path): the MFMA ceiling of
+ * the chip and the shader clock it runs at, as context for the GEMMs'
+ * fraction of the published peak.
+ *
+ * Launches `groups` workgroups of 8 waves; every wave runs `iters` steps of
+ * 8 independent v_mfma_f32_16x16x32_bf16 accumulator chains on register
+ * operands (no memory traffic): groups * 8 * 8 * iters * 16384 flops.
+ * clk [groups, 2] uint64 (device) receives, per workgroup, the elapsed
+ * shader-clock cycles and the elapsed ticks of the constant 100 MHz
+ * real-time counter over the loop; sink [groups * 512] fp32 (device)
+ * receives values that keep the results live. groups <= 2^20; zero iters or
+ * groups returns INV_OK without a launch.
+ * ------------------------------------------------------------------------ */
+inv_status inv_bench_mfma_loop(int64_t iters, int32_t groups, uint64_t* clk, float* sink,
+                               hipStream_t stream);
 
 #ifdef __cplusplus
 }

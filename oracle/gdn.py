@@ -1,15 +1,16 @@
 """Gated DeltaNet under the chunkwise-parallel recurrent (CPR) schedule (oracle side).
 
 [IsoExec] "Chunkwise-parallel recurrent (CPR) GDN" and [NovaSky] "Solving the
-linear-attention headache": the chunkwise-parallel form (training, prefill)
-and the recurrent form (decode) of Gated DeltaNet are the same function with
-different rounding. CPR keeps the recurrence as the function but evaluates it
-in parallel across chunks: a first pass computes the state at every chunk
-boundary, a parallel recurrent scan computes the outputs inside each chunk
-from its boundary state, and decode runs the recurrence but resynchronises
-the state at every chunk boundary, so all three see one rounding schedule.
-The composition example of [IsoExec] "Unified execution contract" names the
-regions gdn.core, gdn.gating and norms.l2.
+linear-attention headache": Gated DeltaNet's chunk-parallel form (used for
+training and prefill) and its token-recurrent form (used for decode) compute
+the same function but round differently. Under CPR the token recurrence is
+the definition. Prefill obtains the state at each multiple of the chunk size
+with a separate pass and then evaluates every chunk's tokens independently,
+starting from that chunk's opening state. Decode steps the recurrence token
+by token and, each time a chunk completes, replaces its running state with
+the chunk-boundary state, so prefill, training forward and decode follow one
+rounding schedule. [IsoExec] "Unified execution contract" lists gdn.core,
+gdn.gating and norms.l2 among its example regions.
 
 The pages give no formulas for the layer. Readings taken (the gated delta
 rule of Gated DeltaNet, restated; one head, key and value width 128):
@@ -97,7 +98,7 @@ def cpr(qh, kh, v, alpha, beta, C):
     Returns (o [L, dv], boundaries [n+1, dk, dv], running state after the
     last token): boundary b_{j+1} = chunk_update(b_j, chunk j); outputs of
     chunk j by the recurrence from b_j. When L is a multiple of C the running
-    state is the last boundary (what decode resynchronises to)."""
+    state is the last boundary (the state decode switches to there)."""
     kh = np.asarray(kh, dtype=np.float64)
     L, dk = kh.shape
     dv = np.asarray(v).shape[1]

@@ -61,6 +61,16 @@ def lse(logits):
     return m + np.log(np.sum(np.exp(x - m[:, None]), axis=1))
 
 
+def _stats(blk):
+    """(max, sum of exp(x - max)) per row of a block. An element equal to -inf
+    adds exactly 0, so a block whose elements are all -inf (a masked range of
+    the vocabulary) is the merge identity (-inf, 0) rather than NaN."""
+    m = blk.max(axis=1)
+    with np.errstate(invalid="ignore"):
+        e = np.where(blk == -np.inf, 0.0, np.exp(blk - m[:, None]))
+    return m, np.sum(e, axis=1)
+
+
 def chunk_stats(logits, C):
     """(m_j, s_j) per row and chunk in float64, arrays [M, C]."""
     x = np.asarray(logits, dtype=np.float64)
@@ -68,9 +78,7 @@ def chunk_stats(logits, C):
     ms = np.empty((M, C))
     ss = np.empty((M, C))
     for j, (a, b) in enumerate(chunk_bounds(V, C)):
-        blk = x[:, a:b]
-        ms[:, j] = blk.max(axis=1)
-        ss[:, j] = np.sum(np.exp(blk - ms[:, j:j + 1]), axis=1)
+        ms[:, j], ss[:, j] = _stats(x[:, a:b])
     return ms, ss
 
 
@@ -105,9 +113,7 @@ def block_stats(logits, width=16):
     ms = np.empty((M, len(bounds)))
     ss = np.empty((M, len(bounds)))
     for j, (a, b) in enumerate(bounds):
-        blk = x[:, a:b]
-        ms[:, j] = blk.max(axis=1)
-        ss[:, j] = np.sum(np.exp(blk - ms[:, j:j + 1]), axis=1)
+        ms[:, j], ss[:, j] = _stats(x[:, a:b])
     return ms, ss
 
 

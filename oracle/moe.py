@@ -2,8 +2,9 @@
 
 [IsoExec] "Unified model": deterministic MoE routing and combination.
 [IsoExec] "Parallelism-invariant kernels" / [NovaSky] "Making kernels
-parallelism-invariant": expert outputs are combined in a fixed routing order,
-not in rank order. [IsoExec] "Unified execution contract": the moe.combine
+parallelism-invariant": under expert parallelism the order in which a token's
+expert results are summed is tied to the routing, never to which rank
+produced them. [IsoExec] "Unified execution contract": the moe.combine
 region is pinned to a leaf tree with 8 leaves of fp32. [RLK] sections 6 and 7
 (FFN module): packed gate/up GEMM, SwiGLU and down GEMM run as separate,
 fixed stages.

@@ -42,6 +42,9 @@ inv_status check_gemm_contract(const inv_contract* c, int64_t K) {
   if (c->tree != INV_TREE_BALANCED) return INV_E_CONTRACT;  // the in-kernel tree is balanced only
   if (c->leaves > 8) return INV_E_UNSUPPORTED;
   if (K < 0) return INV_E_ARG;
+  // the ring kernel addresses a tile's 128 operand rows by 32-bit byte
+  // offsets (row * K * 2): K < 2^24 keeps every one of them in range
+  if (K >= ((int64_t)1 << 24)) return INV_E_UNSUPPORTED;
   if (K % c->leaves != 0) return INV_E_CONTRACT;
   if ((K / c->leaves) % 32 != 0) return INV_E_CONTRACT;
   if (K == 0) return INV_E_CONTRACT;
@@ -565,6 +568,15 @@ inv_status inv_attn_combine(const inv_contract* c, const void* ws, size_t ws_byt
   if (!ws || ws_bytes < need) return INV_E_WORKSPACE;
   return hip_status(inv::launch_attn_combine(static_cast<const float*>(ws), out, Tq, Hq, D, (int)c->split_kv,
                                              c->tree == INV_TREE_LEFT_FOLD, stream));
+}
+
+// ----------------------------------------------------------- measurement
+
+inv_status inv_bench_mfma_loop(int64_t iters, int32_t groups, uint64_t* clk, float* sink, hipStream_t stream) {
+  if (iters < 0 || groups < 0 || groups > (1 << 20)) return INV_E_ARG;
+  if (iters == 0 || groups == 0) return INV_OK;
+  if (!clk || !sink) return INV_E_ARG;
+  return hip_status(inv::launch_mfma_loop(iters, groups, clk, sink, stream));
 }
 
 // ------------------------------------------------------------------- MoE

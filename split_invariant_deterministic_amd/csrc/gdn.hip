@@ -1,14 +1,14 @@
 // Gated DeltaNet under the chunkwise-parallel recurrent (CPR) schedule, gfx950.
 //
 // IsoExec blog, "Chunkwise-parallel recurrent (CPR) GDN" (and the NovaSky
-// write-up, "Solving the linear-attention headache"): the recurrence is the
-// function; a first pass computes the state at every chunk boundary, a
-// parallel pass runs the recurrence inside every chunk from its boundary
-// state, and decode runs the recurrence but resynchronises to the boundary
-// state every C tokens. Prefill and decode therefore share one rounding
-// schedule: the same device functions below (rec_step for a token,
-// chunk_coeffs and chunk_state for a boundary), on the same thread layouts,
-// in both.
+// write-up, "Solving the linear-attention headache"). The token recurrence
+// defines the layer. Prefill obtains the state at each multiple of C with a
+// separate boundary pass and then evaluates all chunks' tokens independently,
+// each from its own opening state; decode steps the recurrence and, whenever
+// a chunk completes, swaps its running state for that chunk's boundary
+// state. Both paths run the same device functions below (rec_step for a
+// token, chunk_coeffs and chunk_state for a boundary) on the same thread
+// layouts, so they round identically.
 //
 // Layer (gated delta rule, one head, width 128, restated):
 //   k^ = k / sqrt(sum k^2 + eps), q^ = q / sqrt(sum q^2 + eps) * 128^(-1/2)

@@ -128,6 +128,12 @@ struct GdnDecodeArgs {
 hipError_t launch_gdn_prefill(const GdnArgs& a, int C, bool out_bf16, hipStream_t s);
 hipError_t launch_gdn_decode(const GdnDecodeArgs& a, int C, bool out_bf16, hipStream_t s);
 
+// ---- measurement ---------------------------------------------------------------
+// groups workgroups of 8 waves, each wave 8 independent MFMA chains of iters
+// steps; clk [groups, 2]: shader-clock cycles and 100 MHz ticks of the loop;
+// sink [groups * 512] keeps the results live.
+hipError_t launch_mfma_loop(int64_t iters, int groups, uint64_t* clk, float* sink, hipStream_t s);
+
 // ---- MoE --------------------------------------------------------------------
 hipError_t launch_moe_route(const float* logits, int32_t* ids, float* w, int64_t T, int E, int k,
                             hipStream_t s);

@@ -67,7 +67,10 @@ __device__ __forceinline__ MS chunk_reduce(const ChunkRegs<ROWS>& c, int n, int 
   for (int i = 0; i < ROWS - 1; ++i) s = s + exp_shifted(c.v[i], m);
   const float e = exp_shifted(c.v[ROWS - 1], m);
   if (last_ok) s = s + e;
-  return MS{m, wave_sum_butterfly(s)};
+  s = wave_sum_butterfly(s);
+  // A chunk whose logits are all -inf (a masked vocabulary range) is the
+  // merge identity (-inf, 0): its exp terms would be exp2(-inf - -inf) = NaN.
+  return MS{m, m == -INFINITY ? 0.0f : s};
 }
 
 // Longer chunks: two passes over memory with the same per-lane order.
@@ -78,7 +81,8 @@ __device__ __forceinline__ MS chunk_stats_long(const float* __restrict__ x, int6
   m = wave_max(m);
   float s = 0.0f;
   for (int64_t e = lane; e < len; e += 64) s = s + exp_shifted(x[lo + e], m);
-  return MS{m, wave_sum_butterfly(s)};
+  s = wave_sum_butterfly(s);
+  return MS{m, m == -INFINITY ? 0.0f : s};  // an all -inf chunk is the identity
 }
 
 // Tree over st[0..C) in LDS; returns the root in every thread. C is a power

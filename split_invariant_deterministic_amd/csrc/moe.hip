@@ -1,8 +1,8 @@
 // Mixture-of-experts stages around the K-leaf grouped GEMM, for gfx950.
 //
 // IsoExec blog, "Unified model": MoE routing and combination are made
-// deterministic; "Parallelism-invariant kernels": expert outputs are combined
-// in a fixed routing order instead of rank order; "Unified execution
+// deterministic; "Parallelism-invariant kernels": the summation order of a
+// token's expert results follows the routing, not the producing rank; "Unified execution
 // contract": the moe.combine region is a leaf tree of 8 fp32 leaves.
 // RL-Kernel write-up, sections 6 and 7: packed gate/up GEMM, SwiGLU and down
 // GEMM run as separate fixed stages.

@@ -94,6 +94,7 @@ _SIGS = {
     "inv_logprob_block16": [_CP, _P, _I64, _P, _P, _I64, _I64, _P, _SZ, _P],
     "inv_gdn_prefill": [_CP, _P, _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _P, _P, _P, _SZ, _P],
     "inv_gdn_decode": [_CP, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P],
+    "inv_bench_mfma_loop": [_I64, _I32, _P, _P, _P],
 }
 for _name, _args in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -231,6 +232,14 @@ def _need(t, dtype, name, ndim=None):
     return t
 
 
+def _shape(t, shape, name):
+    """Raises before any launch if t's shape is not ``shape`` (a wrong-sized
+    buffer would be read or written out of bounds by the kernels)."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
 def _out_torch_dtype(c):
     return torch.bfloat16 if c.out_dtype == BF16 else torch.float32
 
@@ -267,9 +276,12 @@ def gemm_rank(A, B, rank, c, out=None):
     _need(B, torch.bfloat16, "B", 2)
     M, K = A.shape
     N = B.shape[0]
+    if B.shape[1] != K:
+        raise ValueError("A and B disagree on K")
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=A.device)
     _need(out, torch.float32, "out", 2)
+    _shape(out, (M, N), "out")
     _call("inv_gemm_rank", ctypes.byref(c), _ptr(A), _ptr(B), _ptr(out), M, N, K, rank, _stream())
     return out
 
@@ -280,9 +292,12 @@ def gemm_leaves(A, B, leaf_lo, leaf_hi, c, out=None):
     _need(B, torch.bfloat16, "B", 2)
     M, K = A.shape
     N = B.shape[0]
+    if B.shape[1] != K:
+        raise ValueError("A and B disagree on K")
     if out is None:
         out = torch.empty((leaf_hi - leaf_lo, M, N), dtype=torch.float32, device=A.device)
     _need(out, torch.float32, "out", 3)
+    _shape(out, (leaf_hi - leaf_lo, M, N), "out")
     _call("inv_gemm_leaves", ctypes.byref(c), _ptr(A), _ptr(B), _ptr(out), M, N, K, leaf_lo, leaf_hi,
           _stream())
     return out
@@ -295,6 +310,7 @@ def tree_combine(P, c, out=None):
     if out is None:
         out = torch.empty((M, N), dtype=_out_torch_dtype(c), device=P.device)
     _need(out, _out_torch_dtype(c), "out", 2)
+    _shape(out, (M, N), "out")
     _call("inv_tree_combine", ctypes.byref(c), _ptr(P), cnt, _ptr(out), M, N, _stream())
     return out
 
@@ -304,6 +320,7 @@ def cast_bf16(x, out=None):
     if out is None:
         out = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
     _need(out, torch.bfloat16, "out")
+    _shape(out, x.shape, "out")
     _call("inv_cast_bf16", _ptr(x), _ptr(out), x.numel(), _stream())
     return out
 
@@ -319,6 +336,7 @@ def rmsnorm(x, gamma, c, out=None):
     if out is None:
         out = torch.empty_like(x)
     _need(out, torch.bfloat16, "out", 2)
+    _shape(out, (M, H), "out")
     _call("inv_rmsnorm", ctypes.byref(c), _ptr(x), _ptr(gamma), _ptr(out), M, H, _stream())
     return out
 
@@ -337,9 +355,11 @@ def logprob(logits, target, c, out=None):
     ldl = _logits_ld(logits)
     M, V = logits.shape
     _need(target, torch.int32, "target", 1)
+    _shape(target, (M,), "target")
     if out is None:
         out = torch.empty(M, dtype=torch.float32, device=logits.device)
     _need(out, torch.float32, "out", 1)
+    _shape(out, (M,), "out")
     _call("inv_logprob", ctypes.byref(c), _ptr(logits), ldl, _ptr(target), _ptr(out), M, V, _stream())
     return out
 
@@ -354,6 +374,9 @@ def logprob_partials(logits, target, chunk_lo, chunk_hi, c, stats=None, tlogit=N
         tlogit = torch.full((M,), float("nan"), dtype=torch.float32, device=logits.device)
     _need(stats, torch.float32, "stats", 3)
     _need(tlogit, torch.float32, "tlogit", 1)
+    _shape(target, (M,), "target")
+    _shape(stats, (M, c.leaves, 2), "stats")
+    _shape(tlogit, (M,), "tlogit")
     _call("inv_logprob_partials", ctypes.byref(c), _ptr(logits), ldl, _ptr(target), _ptr(stats),
           _ptr(tlogit), M, V, chunk_lo, chunk_hi, _stream())
     return stats, tlogit
@@ -364,8 +387,13 @@ def logprob_combine(stats, tlogit, target, V, c, out=None):
     _need(tlogit, torch.float32, "tlogit", 1)
     _need(target, torch.int32, "target", 1)
     M = stats.shape[0]
+    _shape(stats, (M, c.leaves, 2), "stats")
+    _shape(tlogit, (M,), "tlogit")
+    _shape(target, (M,), "target")
     if out is None:
         out = torch.empty(M, dtype=torch.float32, device=stats.device)
+    _need(out, torch.float32, "out", 1)
+    _shape(out, (M,), "out")
     _call("inv_logprob_combine", ctypes.byref(c), _ptr(stats), _ptr(tlogit), _ptr(target), _ptr(out), M, V,
           _stream())
     return out
@@ -396,6 +424,8 @@ def lmhead_logprob(h, W, target, c, out=None, ws=None):
         raise ValueError("h, W and target disagree")
     if out is None:
         out = torch.empty(M, dtype=torch.float32, device=h.device)
+    _need(out, torch.float32, "out", 1)
+    _shape(out, (M,), "out")
     if ws is None:
         ws = block16_workspace(M, V, h.device)
     _call("inv_lmhead_logprob", ctypes.byref(c), _ptr(h), _ptr(W), _ptr(target), _ptr(out), M, V, K, _ptr(ws),
@@ -408,8 +438,11 @@ def logprob_block16(logits, target, c, out=None, ws=None):
     _need(target, torch.int32, "target", 1)
     ldl = _logits_ld(logits)
     M, V = logits.shape
+    _shape(target, (M,), "target")
     if out is None:
         out = torch.empty(M, dtype=torch.float32, device=logits.device)
+    _need(out, torch.float32, "out", 1)
+    _shape(out, (M,), "out")
     if ws is None:
         ws = block16_workspace(M, V, logits.device)
     _call("inv_logprob_block16", ctypes.byref(c), _ptr(logits), ldl, _ptr(target), _ptr(out), M, V, _ptr(ws),
@@ -436,8 +469,18 @@ def gdn_prefill(q, k, v, g, beta, cu_seqlens, c, out=None, cache=None, ws=None):
     _need(cu_seqlens, torch.int32, "cu_seqlens", 1)
     T, H, D = q.shape
     S = cu_seqlens.shape[0] - 1
+    _shape(k, q.shape, "k")
+    _shape(v, q.shape, "v")
+    _shape(g, (T, H), "g")
+    _shape(beta, (T, H), "beta")
     if out is None:
         out = torch.empty((T, H, D), dtype=_out_torch_dtype(c), device=q.device)
+    _need(out, _out_torch_dtype(c), "out", 3)
+    _shape(out, (T, H, D), "out")
+    if cache is not None:
+        _need(cache, torch.float32, "cache", 1)
+        if cache.numel() * 4 < S * _lib.inv_gdn_cache_bytes(ctypes.byref(c), H):
+            raise ValueError("cache: smaller than S decode caches")
     if ws is None:
         ws = torch.empty(workspace_bytes(c, OP_GDN_PREFILL, T, H, S), dtype=torch.uint8, device=q.device)
     _call("inv_gdn_prefill", ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), S,
@@ -449,13 +492,34 @@ def gdn_decode(q, k, v, g, beta, pos, cache, c, out=None):
     """One decode token per sequence (inv_gdn_decode); cache is updated in place."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, torch.bfloat16, n, 3)
+    _need(g, torch.float32, "g", 2)
+    _need(beta, torch.float32, "beta", 2)
     _need(pos, torch.int32, "pos", 1)
     B, H, D = q.shape
+    _shape(k, q.shape, "k")
+    _shape(v, q.shape, "v")
+    _shape(g, (B, H), "g")
+    _shape(beta, (B, H), "beta")
+    _shape(pos, (B,), "pos")
+    _need(cache, torch.float32, "cache", 1)
+    if cache.numel() * 4 < B * _lib.inv_gdn_cache_bytes(ctypes.byref(c), H):
+        raise ValueError("cache: smaller than B decode caches")
     if out is None:
         out = torch.empty((B, H, D), dtype=_out_torch_dtype(c), device=q.device)
+    _need(out, _out_torch_dtype(c), "out", 3)
+    _shape(out, (B, H, D), "out")
     _call("inv_gdn_decode", ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(pos), B, H, D,
           _ptr(out), _ptr(cache), _stream())
     return out
+
+
+def bench_mfma_loop(iters, groups, device="cuda"):
+    """Measurement helper (inv_bench_mfma_loop): returns (clk [groups, 2]
+    int64 cycles / 100 MHz ticks, flops) of a register-only MFMA loop."""
+    clk = torch.zeros((groups, 2), dtype=torch.int64, device=device)
+    sink = torch.empty(groups * 512, dtype=torch.float32, device=device)
+    _call("inv_bench_mfma_loop", iters, groups, _ptr(clk), _ptr(sink), _stream())
+    return clk, float(groups) * 8 * 8 * iters * 16384
 
 
 def _attn_args(q, k, v, cu_seqlens, q_seq, q_pos):
@@ -467,6 +531,10 @@ def _attn_args(q, k, v, cu_seqlens, q_seq, q_pos):
     _need(q_pos, torch.int32, "q_pos", 1)
     Tq, Hq, D = q.shape
     Hkv = k.shape[1]
+    if k.shape[2] != D or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("q, k and v disagree on the head width, or k and v differ in shape")
+    _shape(q_seq, (Tq,), "q_seq")
+    _shape(q_pos, (Tq,), "q_pos")
     return Tq, Hq, Hkv, D, cu_seqlens.shape[0] - 1
 
 
@@ -483,6 +551,7 @@ def decode_attn(q, k, v, cu_seqlens, q_seq, q_pos, c, ws=None, out=None):
     if out is None:
         out = torch.empty_like(q)
     _need(out, torch.bfloat16, "out", 3)
+    _shape(out, q.shape, "out")
     _call("inv_decode_attn", ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), S, _ptr(q_seq),
           _ptr(q_pos), _ptr(out), Tq, Hq, Hkv, D, _ptr(ws), ws.numel() * 4, _stream())
     return out
@@ -498,6 +567,8 @@ def attn_splits(q, k, v, cu_seqlens, q_seq, q_pos, split_lo, split_hi, c, ws):
 def attn_combine(ws, Tq, Hq, D, c, out=None, device=None):
     if out is None:
         out = torch.empty((Tq, Hq, D), dtype=torch.bfloat16, device=ws.device)
+    _need(out, torch.bfloat16, "out", 3)
+    _shape(out, (Tq, Hq, D), "out")
     _call("inv_attn_combine", ctypes.byref(c), _ptr(ws), ws.numel() * 4, _ptr(out), Tq, Hq, D, _stream())
     return out
 
@@ -533,9 +604,13 @@ def moe_gemm(X, rows, offsets, W, R, c, out=None):
     E, N, K = W.shape
     if X.shape[1] != K:
         raise ValueError("X and W disagree on K")
+    _shape(offsets, (E + 1,), "offsets")
     if out is None:
         out = torch.empty((R, N), dtype=_out_torch_dtype(c), device=X.device)
     _need(out, _out_torch_dtype(c), "out", 2)
+    _shape(out, (R, N), "out")
+    if rows is not None and rows.shape[0] < R:
+        raise ValueError("rows: fewer entries than grouped rows R")
     _call("inv_moe_gemm", ctypes.byref(c), _ptr(X), X.shape[0], _ptr(rows), _ptr(offsets), _ptr(W), _ptr(out), R,
           E, N, K, _stream())
     return out
@@ -554,9 +629,13 @@ def moe_gemm_swiglu(X, rows, offsets, W, R, c, out=None):
     if X.shape[1] != K or N2 % 2:
         raise ValueError("X and W disagree on K, or W has an odd number of rows")
     F = N2 // 2
+    _shape(offsets, (E + 1,), "offsets")
     if out is None:
         out = torch.empty((R, F), dtype=torch.bfloat16, device=X.device)
     _need(out, torch.bfloat16, "out", 2)
+    _shape(out, (R, F), "out")
+    if rows is not None and rows.shape[0] < R:
+        raise ValueError("rows: fewer entries than grouped rows R")
     _call("inv_moe_gemm_swiglu", ctypes.byref(c), _ptr(X), X.shape[0], _ptr(rows), _ptr(offsets), _ptr(W), _ptr(out),
           R, E, F, K, _stream())
     return out
@@ -565,9 +644,13 @@ def moe_gemm_swiglu(X, rows, offsets, W, R, c, out=None):
 def swiglu(GU, c, out=None):
     _need(GU, torch.bfloat16, "GU", 2)
     R, F2 = GU.shape
+    if F2 % 2:
+        raise ValueError("GU: odd number of columns")
     F = F2 // 2
     if out is None:
         out = torch.empty((R, F), dtype=torch.bfloat16, device=GU.device)
+    _need(out, torch.bfloat16, "out", 2)
+    _shape(out, (R, F), "out")
     _call("inv_swiglu", ctypes.byref(c), _ptr(GU), _ptr(out), R, F, _stream())
     return out
 
@@ -578,8 +661,12 @@ def moe_combine(Y, w, slot, c, out=None):
     _need(slot, torch.int32, "slot", 2)
     T = w.shape[0]
     H = Y.shape[1]
+    _shape(w, (T, c.leaves), "w")
+    _shape(slot, (T, c.leaves), "slot")
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=Y.device)
+    _need(out, torch.bfloat16, "out", 2)
+    _shape(out, (T, H), "out")
     _call("inv_moe_combine", ctypes.byref(c), _ptr(Y), _ptr(w), _ptr(slot), Y.shape[0], _ptr(out), T, H,
           _stream())
     return out

@@ -114,6 +114,18 @@ def test_entry_points_reject_before_any_launch():
     # ranks > 1 without workspace: rejected (misaligned pointers are caught first, so use aligned fakes)
     fake = ctypes.c_void_p(1 << 20)
     assert lib.inv_gemm(by(c2), fake, fake, fake, 4, 4, 4096, null, 0, null) == inv.E_WORKSPACE
+    # K >= 2^24 would wrap the ring kernel's 32-bit operand offsets: rejected on every GEMM entry point
+    kbig = 1 << 24
+    assert inv.contract_check(c, inv.OP_GEMM, kbig) == inv.E_UNSUPPORTED
+    assert inv.contract_check(c, inv.OP_GEMM, kbig - 256) == inv.OK
+    assert lib.inv_gemm(by(c), fake, fake, fake, 4096, 4096, kbig, null, 0, null) == inv.E_UNSUPPORTED
+    assert lib.inv_gemm_rank(by(c2), fake, fake, fake, 4096, 4096, kbig, 0, null) == inv.E_UNSUPPORTED
+    assert lib.inv_gemm_leaves(by(c), fake, fake, fake, 4096, 4096, kbig, 0, 8, null) == inv.E_UNSUPPORTED
+    assert lib.inv_moe_gemm(by(c), fake, 4, null, fake, fake, fake, 4, 2, 64, kbig, null) == inv.E_UNSUPPORTED
+    assert lib.inv_moe_gemm_swiglu(by(c), fake, 4, null, fake, fake, fake, 4, 2, 64, kbig, null) \
+        == inv.E_UNSUPPORTED
+    assert lib.inv_lmhead_logprob(by(inv.contract(out="fp32")), fake, fake, fake, fake, 4, 512, kbig, fake,
+                                  1 << 30, null) == inv.E_UNSUPPORTED
     assert lib.inv_gemm_leaves(by(c), fake, fake, fake, 4, 4, 4096, 3, 3, null) == inv.E_ARG
     assert lib.inv_gemm_leaves(by(c), fake, fake, fake, 4, 4, 4096, 0, 9, null) == inv.E_ARG
     assert lib.inv_gemm_rank(by(c2), fake, fake, fake, 4, 4, 4096, 2, null) == inv.E_ARG

@@ -145,3 +145,24 @@ def test_block_merge_left_fold_changes_bits(inv, lm):
     fold = inv.logprob_block16(logits, t, inv.contract(leaves=8, tree="left_fold"))
     _, bad, dmax = mismatch_report(bal, fold)
     assert bad > 0 and dmax < 1e-4
+
+
+def test_unfused_lm_head_chain_batch_invariance_full_size(inv, lm):
+    """The unfused chain at the full LM-head shape (inv_gemm 4096x151936x4096
+    with fp32 logits, then the 64-chunk inv_logprob): batch 1 and the prefixes
+    give, bit for bit, the rows of batch 4096 -- logits and logprobs."""
+    h, W, t = lm["h"], lm["W"], lm["targets"]
+    c = inv.contract(leaves=8, out="fp32")
+    c64 = inv.contract(leaves=64)
+    logits = inv.gemm(h, W, c)
+    full = inv.logprob(logits, t, c64)
+    for i in (0, 1, 2047, 4095):
+        l1 = inv.gemm(h[i:i + 1].contiguous(), W, c)
+        assert bitwise_equal(l1[0], logits[i]), i
+        assert bitwise_equal(inv.logprob(l1, t[i:i + 1].contiguous(), c64)[0], full[i]), i
+    for M in (7, 64, 512):
+        lm_ = inv.gemm(h[:M].contiguous(), W, c)
+        assert bitwise_equal(lm_, logits[:M]), M
+        assert bitwise_equal(inv.logprob(lm_, t[:M].contiguous(), c64), full[:M]), M
+        del lm_
+    del logits

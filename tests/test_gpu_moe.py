@@ -272,3 +272,42 @@ def test_combine_vector_and_scalar_paths(inv, H, offset):
     out = inv.moe_combine(Y, w, slot, inv.contract(leaves=8))
     ref = omoe.combine(Y.cpu().numpy()[slot.cpu().numpy()], w.cpu().numpy())
     assert np.array_equal(_np(out), ref.astype(np.float32))
+
+
+def test_moe_full_size_sampled_tokens_against_oracle(inv, moe_full):
+    """The full 8192-token layer (persistent multi-tile grouped launches, about
+    512 grouped rows per expert), checked stage by stage against the oracle on
+    16 sampled tokens: every grouped row of their 8 experts (gate/up, SwiGLU,
+    down) and their combined outputs, replayed bit for bit."""
+    d = moe_full
+    c = inv.contract(leaves=8)
+    st = {}
+    out = inv.moe_layer(d["x"], d["logits"], d["W1"], d["W2"], c, c, out_stage=st)
+    toks = np.linspace(0, 8191, 16).astype(int)
+    ids = st["ids"].cpu().numpy()
+    slot = st["slot"].cpu().numpy()
+    rows = st["rows"].cpu().numpy()
+    offs = st["offsets"].cpu().numpy()
+    oid, ow = omoe.route(d["logits"][toks].double().cpu().numpy(), 8)
+    assert np.array_equal(ids[toks], oid)
+    assert np.allclose(st["w"][toks].cpu().numpy(), ow, rtol=1e-6, atol=0)
+    W1, W2 = _Experts(d["W1"]), _Experts(d["W2"])
+    GU, A, Y = st["GU"], st["A"], st["Y"]
+    for t in toks:   # each (token, expert) pair sits in its expert's group and gathers its token
+        for j in range(8):
+            e, r = ids[t, j], slot[t, j]
+            assert offs[e] <= r < offs[e + 1] and rows[r] == t
+    deep = 0
+    for e in np.unique(ids[toks]):
+        gr = np.sort(slot[toks][ids[toks] == e])    # grouped rows of the sampled tokens
+        deep += int(np.sum(gr - offs[e] >= 128)) if offs[e + 1] - offs[e] >= 500 else 0
+        gi = torch.as_tensor(gr, device=DEV)
+        xr = _np(d["x"][torch.as_tensor(rows[gr], device=DEV).long()]).astype(np.float64)
+        gu = _np(GU[gi])
+        check_bf16(gu, omoe.gate_up(xr, W1[e]), f"gate/up e={e}")
+        check_bf16(A[gi], omoe.swiglu(gu), f"swiglu e={e}")
+        check_fp32_gemm(Y[gi].cpu().numpy(), omoe.down(_np(A[gi]).astype(np.float64), W2[e]), f"down e={e}")
+    assert deep >= 16, deep   # rows past the first 128-row tile of well-filled experts were compared
+    Yn = Y.cpu().numpy()
+    ref = omoe.combine(Yn[slot[toks]], st["w"][toks].cpu().numpy())
+    assert np.array_equal(_np(out[toks]), ref.astype(np.float32))

@@ -192,3 +192,31 @@ def test_logprob_sum_to_one(inv):
         lp = inv.logprob(xs, torch.arange(V, dtype=torch.int32, device=DEV), c)
         tot.append(math.fsum(np.exp(lp.double().cpu().numpy())))
     assert np.allclose(tot, 1.0, rtol=0, atol=2e-5)
+
+
+@pytest.mark.parametrize("V,C", [(9000, 16), (151936, 64), (3000, 1)])
+def test_logprob_masked_chunks(inv, V, C):
+    """-inf logits (a masked vocabulary range): a fully masked chunk is the
+    merge identity (-inf, 0) and scattered -inf entries add nothing, so the
+    result stays finite and within the bar of the oracle's plain definition;
+    the 16-column block schedule agrees within the same bar."""
+    x = _rand_logits(4, V, 12)
+    if C > 1:
+        a, e = olp.chunk_bounds(V, C)[1]
+        x[0, a:e] = float("-inf")                                # chunk 1 fully masked
+    x[1, ::7] = float("-inf")                                    # scattered
+    x[2, : (V // 2)] = float("-inf")                             # the first half of the row
+    x[3, -17:] = float("-inf")                                   # a ragged tail
+    t = torch.tensor([3, 5, V - 1, 0], dtype=torch.int32)
+    xd = x.double().numpy()
+    ora = olp.logprob(xd, t.numpy())
+    assert np.all(np.isfinite(ora))
+    c = inv.contract(leaves=C)
+    lp = inv.logprob(x.to(DEV), t.to(DEV), c)
+    check_logprob(lp, ora, f"masked {V}/{C}", lse=olp.lse(xd))
+    if C > 1:
+        stats, _ = inv.logprob_partials(x.to(DEV), t.to(DEV), 0, C, c)
+        s = stats.cpu()
+        assert s[0, 1, 0].item() == float("-inf") and s[0, 1, 1].item() == 0.0
+    lb = inv.logprob_block16(x.to(DEV), t.to(DEV), inv.contract(out="fp32"))
+    check_logprob(lb, ora, f"masked block16 {V}", lse=olp.lse(xd))

@@ -247,6 +247,49 @@ def test_lse_merge_identity_and_halves():
     assert abs(mm[0] + np.log(ssum[0]) - olp.lse(x)[0]) < 1e-14
 
 
+def test_chunk_bounds_floor_rule_hand_values():
+    """Chunk j = [floor(jV/C), floor((j+1)V/C)): hand-derived boundaries that
+    the other plausible splits (ceil-first as numpy.array_split, remainder to
+    the last chunk) get wrong."""
+    assert olp.chunk_bounds(10, 4) == [(0, 2), (2, 5), (5, 7), (7, 10)]
+    # the LM-head vocabulary: 151936 = 64 * 2374, every chunk 2374 long
+    b = olp.chunk_bounds(151936, 64)
+    assert [e - a for a, e in b] == [2374] * 64 and b[-1] == (151936 - 2374, 151936)
+    # one logit more: floor((j+1)(64*2374+1)/64) - floor(j(64*2374+1)/64) = 2374 + [j = 63]
+    assert [e - a for a, e in olp.chunk_bounds(151937, 64)] == [2374] * 63 + [2375]
+    # one logit less: only chunk 0 is short (floor(-1/64) = -1)
+    assert [e - a for a, e in olp.chunk_bounds(151935, 64)] == [2373] + [2374] * 63
+    # the statistics follow the same boundaries: zero logits give s_j = chunk length
+    ms, ss = olp.chunk_stats(np.zeros((1, 10)), 4)
+    assert ss[0].tolist() == [2.0, 3.0, 2.0, 3.0] and np.all(ms == 0.0)
+
+
+def test_masked_chunks_are_the_merge_identity():
+    """A chunk whose logits are all -inf (a masked vocabulary range) has the
+    statistics (-inf, 0), the exact identity of the merge, so the chunked LSE
+    equals the plain one; scattered -inf entries add exactly nothing."""
+    rng = np.random.default_rng(21)
+    x = rng.normal(size=(3, 40))
+    x[0, 10:20] = -np.inf          # chunk 1 of 4 fully masked
+    x[1, ::3] = -np.inf            # scattered
+    x[2, 30:40] = -np.inf
+    x[2, 0:10] = -np.inf
+    ms, ss = olp.chunk_stats(x, 4)
+    assert ms[0, 1] == -np.inf and ss[0, 1] == 0.0
+    assert ms[2, 0] == -np.inf and ss[2, 0] == 0.0 and ss[2, 3] == 0.0
+    assert not np.any(np.isnan(ss))
+    for sch in (otree.BALANCED, otree.LEFT_FOLD):
+        assert np.allclose(olp.merge_tree(ms, ss, sch), olp.lse(x), rtol=0, atol=1e-13)
+    # the plain value: the masked entries drop out of the sum
+    keep = np.isfinite(x[1])
+    assert abs(olp.lse(x)[1] - np.log(np.sum(np.exp(x[1][keep])))) < 1e-13
+    bm, bs = olp.block_stats(x)
+    assert not np.any(np.isnan(bs))
+    assert np.allclose(olp.merge_tree_padded(bm, bs), olp.lse(x), rtol=0, atol=1e-13)
+    t = np.array([5, 1, 25])
+    assert np.allclose(olp.logprob_blocks(x, t), olp.logprob(x, t), rtol=0, atol=1e-13)
+
+
 def test_logprob_bad_target_is_nan():
     x = np.zeros((3, 10))
     lp = olp.logprob(x, np.array([-1, 10, 3]))
@@ -354,6 +397,78 @@ def test_moe_identical_experts_equal_one_expert():
     assert np.array_equal(out, single)
 
 
+def _rne_rational(q, bits):
+    """Round an exact rational to the nearest value with ``bits`` significant
+    bits (8: bf16, 24: fp32), ties to even, computed on the rational itself
+    (normal range only; these tests stay far from over- and underflow)."""
+    if q == 0:
+        return 0.0
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()  # 2**e <= a < 2**(e+2)
+    if a < Fraction(2) ** e:
+        e -= 1
+    elif a >= Fraction(2) ** (e + 1):
+        e += 1
+    assert Fraction(2) ** e <= a < Fraction(2) ** (e + 1) and -120 < e < 120
+    ulp = Fraction(2) ** (e - bits + 1)
+    n = a / ulp
+    f = n.numerator // n.denominator
+    r = n - f
+    if r > Fraction(1, 2) or (r == Fraction(1, 2) and f % 2 == 1):
+        f += 1
+    return float((f * ulp) if q > 0 else -(f * ulp))
+
+
+def test_rne_rational_helper_hand_cases():
+    # the helper itself, on hand-checked values
+    assert _rne_rational(Fraction(1) + Fraction(1, 256), 8) == 1.0              # tie -> even
+    assert _rne_rational(Fraction(1) + Fraction(3, 256), 8) == 1.0 + 2.0 ** -6  # tie -> even (up)
+    assert _rne_rational(Fraction(-3, 7), 24) == float(np.float32(-3.0 / 7.0))
+    assert _rne_rational(Fraction(1, 3), 8) == 0.333984375                       # 0x3EAB
+
+
+def test_moe_gate_up_and_down_against_exact_rationals():
+    """gate_up = bf16(x W1^T) and down = fp32(a W2^T) on a non-square shape
+    (x 3x24, W1 10x24, W2 24x5): every entry is the exact rational sum
+    rounded once at the boundary. A transposed operand fails on the shapes, a
+    dropped boundary rounding or a wrong index on the values."""
+    gen = torch.Generator().manual_seed(31)
+    x = torch.randn(3, 24, generator=gen).to(torch.bfloat16).double().numpy()
+    W1 = (torch.randn(10, 24, generator=gen) * 0.3).to(torch.bfloat16).double().numpy()
+    W2 = (torch.randn(24, 5, generator=gen) * 0.3).to(torch.bfloat16).double().numpy()
+    gu = omoe.gate_up(x, W1)
+    assert gu.shape == (3, 10)
+    for i in range(3):
+        for j in range(10):
+            ex = sum((Fraction(float(x[i, k])) * Fraction(float(W1[j, k])) for k in range(24)), Fraction(0))
+            assert gu[i, j] == _rne_rational(ex, 8), (i, j)
+    a = omoe.swiglu(gu)
+    assert a.shape == (3, 5)
+    y = omoe.down(a, W2)
+    assert y.shape == (3, 24) and y.dtype == np.float32
+    for i in range(3):
+        for h in range(24):
+            ex = sum((Fraction(float(a[i, f])) * Fraction(float(W2[h, f])) for f in range(5)), Fraction(0))
+            assert float(y[i, h]) == _rne_rational(ex, 24), (i, h)
+    # the rounding is really exercised: the unrounded sums differ from the results
+    assert not np.array_equal(gu, x @ W1.T) and not np.array_equal(y.astype(np.float64), a @ W2.T)
+
+
+def test_moe_ffn_integer_closed_form():
+    """Small integers: g, u, a and y are exact, so gate_up is the integer
+    product, the SwiGLU of g = 0 is 0, and down reproduces a W2^T exactly."""
+    rng = np.random.default_rng(32)
+    x = rng.integers(-3, 4, size=(4, 24)).astype(np.float64)
+    W1 = rng.integers(-2, 3, size=(10, 24)).astype(np.float64)
+    gu = omoe.gate_up(x, W1)
+    assert np.array_equal(gu, x @ W1.T)          # |entries| <= 144 < 256: bf16-exact
+    a = rng.integers(-4, 5, size=(4, 5)).astype(np.float64)
+    W2 = rng.integers(-4, 5, size=(24, 5)).astype(np.float64)
+    assert np.array_equal(omoe.down(a, W2), (a @ W2.T).astype(np.float32))
+    gz = np.concatenate([np.zeros((2, 5)), np.ones((2, 5)) * 7.0], axis=1)
+    assert np.all(omoe.swiglu(gz) == 0.0)       # silu(0) * u = 0
+
+
 # ---------------------------------------------------------------- Gated DeltaNet (CPR)
 
 def _gdn_case(L, dk=16, dv=12, seed=0, gscale=0.2):
@@ -387,6 +502,37 @@ def test_gdn_cpr_equals_the_recurrence(L, C):
     for j in range(1, L // C + 1):   # every boundary is the recurrence's state there
         _, Sj = ogdn.recurrent(qh[:j * C], kh[:j * C], v[:j * C], alpha[:j * C], beta[:j * C])
         assert np.allclose(b[j], Sj, rtol=0, atol=1e-12)
+
+
+def test_gdn_layer_packed_equals_per_sequence_recurrence():
+    """gdn_layer over packed ragged sequences (lengths 1, 63, 64, 65, 130;
+    2 heads; chunk 64 and 16) equals, per sequence and head, the plain token
+    recurrence run on that sequence alone from a zero state; the order in
+    which sequences are packed does not change any sequence's outputs."""
+    lengths = [1, 63, 64, 65, 130]
+    rng = np.random.default_rng(33)
+    T, H, D = sum(lengths), 2, 16
+    q = rng.normal(size=(T, H, D))
+    k = rng.normal(size=(T, H, D))
+    v = rng.normal(size=(T, H, D))
+    g = -0.5 * rng.uniform(size=(T, H))
+    beta = rng.uniform(size=(T, H))
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    for C in (64, 16):
+        o = ogdn.gdn_layer(q, k, v, g, beta, cu, C)
+        assert o.shape == (T, H, D)
+        for s in range(len(lengths)):
+            a, e = cu[s], cu[s + 1]
+            for h in range(H):
+                qh, kh, al = ogdn.prep(q[a:e, h], k[a:e, h], g[a:e, h])
+                ref, _ = ogdn.recurrent(qh, kh, v[a:e, h], al, beta[a:e, h])
+                assert np.allclose(o[a:e, h], ref, rtol=0, atol=1e-12), (C, s, h)
+    # reversed packing order: same per-sequence outputs
+    order = list(range(len(lengths)))[::-1]
+    idx = np.concatenate([np.arange(cu[s], cu[s + 1]) for s in order])
+    cu2 = np.concatenate([[0], np.cumsum([lengths[s] for s in order])])
+    o2 = ogdn.gdn_layer(q[idx], k[idx], v[idx], g[idx], beta[idx], cu2, 64)
+    assert np.allclose(o2, ogdn.gdn_layer(q, k, v, g, beta, cu, 64)[idx], rtol=0, atol=1e-12)
 
 
 def test_gdn_delta_rule_closed_forms():
