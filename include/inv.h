@@ -234,6 +234,25 @@ inv_status inv_gemm(const inv_contract* c, const void* A, const void* B, void* C
                     int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes,
                     hipStream_t stream);
 
+/* inv_gemm for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): no
+ * workspace argument, and the call allocates nothing. The fp32 partials that
+ * inv_gemm would keep in a caller workspace (the R rank planes when
+ * ranks > 1; the leaf groups of a single rank when M >= 8 and the 128 x 128
+ * tiles alone would leave compute units idle) go to a library-owned scratch
+ * array of 16 MiB per GPU, allocated when the library is loaded on that GPU
+ * and held until the process ends. Every single-rank shape fits; with
+ * ranks > 1 a call needing R*M*N*4 bytes above 16 MiB returns
+ * INV_E_WORKSPACE before any launch. The result is bitwise inv_gemm's for
+ * the same arguments (same kernels, same tree). All calls on one GPU share
+ * that GPU's scratch and each call leaves its partials there: calls that
+ * overlap in time on one GPU (concurrent streams, or host threads) race and
+ * must be serialised by the caller. The first call on a device looks up the
+ * scratch address for it (hipGetSymbolAddress); a failure there returns
+ * INV_E_HIP. */
+inv_status inv_gemm_noalloc(const inv_contract* c, const void* A, const void* B, void* C,
+                            int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
 /* One rank's share of inv_gemm: P_r [M,N] fp32 = the balanced subtree over
  * leaves [rank*L/R, (rank+1)*L/R). A and B are the full operands; only the
  * rank's K slice is read. */

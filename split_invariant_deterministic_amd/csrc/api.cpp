@@ -260,6 +260,29 @@ inv_status inv_gemm(const inv_contract* c, const void* A, const void* B, void* C
                                              stream));
 }
 
+inv_status inv_gemm_noalloc(const inv_contract* c, const void* A, const void* B, void* C, int64_t M, int64_t N,
+                            int64_t K, hipStream_t stream) {
+  inv_status s = check_gemm_contract(c, K);
+  if (s != INV_OK) return s;
+  if ((s = gemm_shape_check(A, B, C, M, N, K)) != INV_OK) return s;
+  if (M == 0 || N == 0) return INV_OK;
+  const int L = (int)c->leaves, R = (int)c->ranks;
+  const int kl = (int)(K / L);
+  // the partials inv_gemm keeps in its workspace: R rank planes, or (one rank)
+  // the G leaf groups it uses when given enough workspace
+  const int G = R > 1 ? R : gemm_split_groups(c, M, N);
+  if (G == 1) return hip_status(inv::launch_gemm(gemm_launch(A, B, C, M, N, K, kl, 0, L, 1, out_is_bf16(c)), stream));
+  const size_t need = (size_t)G * (size_t)M * (size_t)N * sizeof(float);
+  if (need > inv::kScratchBytes) return INV_E_WORKSPACE;  // more partials than the fixed scratch holds
+  void* ws = nullptr;
+  if (inv::scratch_device_ptr(&ws) != hipSuccess) return INV_E_HIP;
+  // every partial plane is written in full before the combine reads it: nothing needs clearing
+  hipError_t e = inv::launch_gemm(gemm_launch(A, B, ws, M, N, K, kl, 0, L / G, G, false), stream);
+  if (e != hipSuccess) return INV_E_HIP;
+  return hip_status(
+      inv::launch_tree_combine(static_cast<const float*>(ws), G, M * N, C, out_is_bf16(c), false, stream));
+}
+
 inv_status inv_gemm_rank(const inv_contract* c, const void* A, const void* B, float* P_r, int64_t M, int64_t N,
                          int64_t K, uint32_t rank, hipStream_t stream) {
   inv_status s = check_gemm_contract(c, K);

@@ -128,6 +128,15 @@ struct GdnDecodeArgs {
 hipError_t launch_gdn_prefill(const GdnArgs& a, int C, bool out_bf16, hipStream_t s);
 hipError_t launch_gdn_decode(const GdnDecodeArgs& a, int C, bool out_bf16, hipStream_t s);
 
+// ---- library-owned scratch (no-allocation entry points) -------------------------
+// Bytes of the per-device scratch array: the largest leaf-group workspace any
+// single-rank GEMM asks for (G * M * N fp32 with tiles * G <= 256 tiles of
+// 128 x 128) is 256 * 128 * 128 * 4 bytes = 16 MiB.
+constexpr size_t kScratchBytes = size_t{16} << 20;
+// The current device's address of the scratch array (looked up once per
+// device with that device current).
+hipError_t scratch_device_ptr(void** out);
+
 // ---- measurement ---------------------------------------------------------------
 // groups workgroups of 8 waves, each wave 8 independent MFMA chains of iters
 // steps; clk [groups, 2]: shader-clock cycles and 100 MHz ticks of the loop;

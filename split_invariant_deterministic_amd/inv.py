@@ -73,6 +73,7 @@ _SIGS = {
     "inv_contract_check": [_CP, ctypes.c_int, _I64],
     "inv_gemm": [_CP, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P],
     "inv_gemm_rank": [_CP, _P, _P, _P, _I64, _I64, _I64, _U32, _P],
+    "inv_gemm_noalloc": [_CP, _P, _P, _P, _I64, _I64, _I64, _P],
     "inv_gemm_leaves": [_CP, _P, _P, _P, _I64, _I64, _I64, _U32, _U32, _P],
     "inv_tree_combine": [_CP, _P, _U32, _P, _I64, _I64, _P],
     "inv_cast_bf16": [_P, _P, _I64, _P],
@@ -267,6 +268,21 @@ def gemm(A, B, c, out=None, ws=None, use_ws=True):
         ws = torch.empty(nbytes, dtype=torch.uint8, device=A.device)
     wsz = ws.numel() * ws.element_size() if ws is not None else 0
     _call("inv_gemm", ctypes.byref(c), _ptr(A), _ptr(B), _ptr(out), M, N, K, _ptr(ws), wsz, _stream())
+    return out
+
+
+def gemm_noalloc(A, B, c, out):
+    """inv_gemm_noalloc: inv_gemm with the partials in the library's fixed
+    per-GPU scratch; the caller passes the output, nothing is allocated."""
+    _need(A, torch.bfloat16, "A", 2)
+    _need(B, torch.bfloat16, "B", 2)
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K:
+        raise ValueError("A and B disagree on K")
+    _need(out, _out_torch_dtype(c), "out", 2)
+    _shape(out, (M, N), "out")
+    _call("inv_gemm_noalloc", ctypes.byref(c), _ptr(A), _ptr(B), _ptr(out), M, N, K, _stream())
     return out
 
 
