@@ -437,14 +437,12 @@ struct RingCtx {
     if (more) issue_done();
     ++g;
   }
-  // Two consecutive leaves (spl = 2m+1 substeps each) into a and b.
+  // Two consecutive leaves (spl = 2m+1 substeps each, m >= 1: leaves of 96,
+  // 160, ... k; leaves of exactly 32 run on 32-k stages, see ring_dispatch)
+  // into a and b.
   __device__ __forceinline__ void leaf_pair(Acc& a, Acc& b) {
     static_assert(ODD && BK == 64, "odd leaves on 64-k stages");
     const int m = (spl - 1) / 2;
-    if (m == 0) {
-      split_stage<true>(a, b);
-      return;
-    }
     stage64<true>(a);
 #pragma clang loop unroll(disable)
     for (int s = 1; s < m; ++s) stage64<false>(a);
@@ -502,10 +500,9 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void gemm_ring_kernel(TileParam
   constexpr int LDS_BYTES = R::NS * R::STAGE + SPILL > LP_BYTES ? R::NS * R::STAGE + SPILL : LP_BYTES;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
   // Persistent launches take several tiles per workgroup and let the ring
-  // run on into the next tile's stages (8 leaves on 64-k stages).
-  // (Odd-multiple-of-32 leaves are left out: their tree already fills the
-  // registers, and carrying the next tile's addressing spills.)
-  constexpr bool PERSIST_OK = NL == 8 && BK == 64 && !ODD;
+  // run on into the next tile's stages (8 leaves on 64-k stages, odd
+  // multiples of 32 included).
+  constexpr bool PERSIST_OK = NL == 8 && BK == 64;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -533,8 +530,69 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void gemm_ring_kernel(TileParam
     int64_t m0, m_end, n0;
     const uint16_t* B = p.B;
     if constexpr (GROUPED) {
-      // slot -> (expert, rows): experts own consecutive runs of ceil(count_e / BM)
-      // row tiles, in expert order; every row tile spans all column tiles
+     if (p.E <= 128) {
+      // XCD-aware order over the real tiles: items are (expert, column tile,
+      // row tile) in that order (column-major inside an expert), and XCD x
+      // (workgroups are dealt round-robin to the 8 XCDs) takes the contiguous
+      // eighth [x I / 8, (x+1) I / 8) of the I items, its workgroups walking it
+      // in order. Workgroups resident on one XCD at a time then share an
+      // expert's weight panels and its gathered row tiles in their L2.
+      // The experts' row-tile counts are prefix-summed across the wave (lane
+      // l holds experts l and l + 64; temporaries of the set-up only: kept
+      // across the tile loop they cost the main loop 30 registers).
+      int gt_incl[2], running = 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int ee = 64 * h + lane;
+        int nt = 0;
+        if (ee < p.E) {  // offsets come from device memory: clamped into [0, M]
+          const int a0 = (int)min(max((int64_t)p.offsets[ee], (int64_t)0), p.M);
+          const int a1 = (int)min(max((int64_t)p.offsets[ee + 1], (int64_t)a0), p.M);
+          nt = (a1 - a0 + R::BM - 1) / R::BM;
+        }
+        int incl = nt;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int v = __shfl_up(incl, off, 64);
+          if (lane >= off) incl += v;
+        }
+        incl += running;
+        running = __shfl(incl, 63, 64);
+        gt_incl[h] = incl;
+      }
+      const int64_t I = (int64_t)__builtin_amdgcn_readfirstlane(running) * tiles_n;
+      const int x = (int)(tile % 8);
+      const int64_t item = x * I / 8 + tile / 8;
+      if (item >= (x + 1) * I / 8) return false;  // past this XCD's range (uniform)
+      // item < incl * tiles_n <=> item / tiles_n < incl (incl * tiles_n is a multiple of tiles_n)
+      const int iq = (int)(item / tiles_n);
+      int e = -1, incl = 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (e >= 0) continue;  // uniform
+        const uint64_t hit = __ballot(64 * h + lane < p.E && iq < gt_incl[h]);
+        if (hit) {
+          const int f = __ffsll((unsigned long long)hit) - 1;
+          e = 64 * h + f;
+          incl = __shfl(gt_incl[h], f, 64);
+        }
+      }
+      if (e < 0) return false;
+      e = __builtin_amdgcn_readfirstlane(e);
+      // the expert's rows, clamped as when the counts were taken
+      const int r0 = (int)min(max((int64_t)p.offsets[e], (int64_t)0), p.M);
+      const int r1 = (int)min(max((int64_t)p.offsets[e + 1], (int64_t)r0), p.M);
+      const int nt = (r1 - r0 + R::BM - 1) / R::BM;
+      const int excl = __builtin_amdgcn_readfirstlane(incl) - nt;
+      const int64_t local = item - (int64_t)excl * tiles_n;
+      n0 = (local / nt) * TN;
+      m0 = r0 + (local % nt) * R::BM;
+      m_end = r1;
+      B += (int64_t)e * p.b_expert_stride;
+     } else {
+      // more than 128 experts: slot -> (expert, rows), experts owning
+      // consecutive runs of ceil(count_e / BM) row tiles in expert order,
+      // every row tile spanning all column tiles
       const int t = (int)(tile / tiles_n);
       n0 = (int64_t)(tile % tiles_n) * TN;
       // The tile counts are prefix-summed 64 experts at a time across the
@@ -573,6 +631,7 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void gemm_ring_kernel(TileParam
       m0 = r0 + (int64_t)(t - tstart) * R::BM;
       m_end = r1;
       B += (int64_t)e * p.b_expert_stride;
+     }
     } else {
       // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so
       // give XCD x a contiguous run of tile ids, and walk tile ids in bands
@@ -1096,11 +1155,22 @@ __global__ __launch_bounds__(256) void cast_bf16_kernel(const float* __restrict_
   break;
 
 // Leaves that are a multiple of 64 run on 64-k stages; leaves that are an odd
-// multiple of 32 run on 64-k stages as 32-wide substeps when the leaf count
-// is even, else (one leaf) on 32-k stages.
+// multiple of 32 from 96 on run on 64-k stages as 32-wide substeps when the
+// leaf count is even; one odd leaf, and leaves of exactly 32, run on 32-k
+// stages. The chain of every element is the same in all of them.
 template <int OUTM, bool GROUPED>
 hipError_t ring_dispatch(const TileParams& p, dim3 grid, int nl, hipStream_t s) {
   const bool bk64 = p.kl % 64 == 0;
+  if (p.kl == 32) {
+    switch (nl) {
+      case 1: INV_RING_CASE(1, 32, false)
+      case 2: INV_RING_CASE(2, 32, false)
+      case 4: INV_RING_CASE(4, 32, false)
+      case 8: INV_RING_CASE(8, 32, false)
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (nl * 2 + (bk64 ? 1 : 0)) {
     case 2: INV_RING_CASE(1, 32, false)
     case 3: INV_RING_CASE(1, 64, false)
@@ -1182,17 +1252,21 @@ hipError_t launch_gemm(const GemmLaunch& g, hipStream_t s) {
   // + 256, ..., and its ring runs on from each tile into the next, so no tile
   // pays the pipeline's fill or a workgroup launch.
   constexpr int64_t kResident = 256;
-  const bool can_persist = g.nl == 8 && g.kl % 64 == 0 && g.groups == 1;
+  // (8 leaves of 64 k or more: the 64-k stage kernels)
+  const bool can_persist = g.nl == 8 && g.kl >= 64 && g.groups == 1;
   if (lp && (g.offsets || g.groups != 1)) return hipErrorInvalidValue;  // statistics need whole trees
   if (g.swiglu && (!g.offsets || g.groups != 1 || g.N % 2 != 0)) return hipErrorInvalidValue;
 
   if (g.offsets) {  // grouped: row-tile slots = an upper bound on sum_e ceil(count_e / 128)
     const int64_t slots = g.M / 128 + g.E;
     const int64_t tiles_n = g.swiglu ? (g.N / 2 + 63) / 64 : (g.N + 127) / 128;
-    dim3 grid((unsigned)(slots * tiles_n), 1u, (unsigned)g.groups);
-    if (can_persist && slots * tiles_n > kResident) {
+    // walk positions: with the XCD-aware order (<= 128 experts) every XCD
+    // walks at most ceil(items / 8) positions, so round up to a multiple of 8
+    const int64_t walk = (slots * tiles_n + 7) / 8 * 8;
+    dim3 grid((unsigned)walk, 1u, (unsigned)g.groups);
+    if (can_persist && walk > kResident) {
       p.persist = 1;
-      p.ntiles = slots * tiles_n;
+      p.ntiles = walk;
       grid.x = (unsigned)kResident;
     }
     if (g.swiglu) return ring_dispatch<kOutSwiGLU, true>(p, grid, g.nl, s);

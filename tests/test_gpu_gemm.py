@@ -239,3 +239,21 @@ def test_empty_and_ragged(inv):
     full = inv.gemm(A, B, c)
     for M in (1, 16, 17, 64):
         assert bitwise_equal(inv.gemm(A[:M].contiguous(), B, c), full[:M]), M
+
+
+@pytest.mark.parametrize("M", [9, 300, 2100])
+def test_leaves_of_32_rank_partitions_and_oracle(inv, M):
+    """K = 256, 8 leaves of 32 k: one MFMA step per leaf, on 32-k stages for
+    every leaf count; rank partitions and per-leaf launches give the bits of
+    the single launch, and sampled elements match the oracle."""
+    X = synth.randn((M, 256), 141).to(DEV)
+    W = synth.randn((2000, 256), 142, 0.05).to(DEV)
+    base = inv.gemm(X, W, inv.contract(leaves=8))
+    assert bitwise_equal(inv.gemm(X, W, inv.contract(leaves=8), use_ws=False), base)
+    for R in (2, 4, 8):
+        assert bitwise_equal(inv.gemm(X, W, inv.contract(leaves=8, ranks=R)), base), R
+    P8 = inv.gemm_leaves(X, W, 0, 8, inv.contract(leaves=8, out="fp32"))
+    assert bitwise_equal(inv.tree_combine(P8, inv.contract(leaves=8)), base)
+    rows = np.array([0, M // 2, M - 1])
+    ref = ogemm.gemm_tree(X[torch.as_tensor(rows, device=DEV)].float().cpu().numpy(), W.float().cpu().numpy(), 8, "bf16")
+    check_bf16(base[torch.as_tensor(rows, device=DEV)], ref, f"leaves of 32, M={M}")

@@ -194,7 +194,9 @@ def test_fused_swiglu_equals_unfused(inv, T, E, H, F, L):
                                          # more row-tile slots than resident workgroups: each
                                          # workgroup walks several tiles
                                          ("bf16", 512, 600, 16, 2000), ("fp32", 512, 600, 16, 1000),
-                                         ("fp32", 768, 600, 16, 2000)])
+                                         ("fp32", 768, 600, 16, 2000),
+                                         # more than 128 experts: the expert table is searched per tile
+                                         ("bf16", 512, 600, 160, 300), ("fp32", 768, 300, 200, 256)])
 def test_grouped_gemm_malformed_rows_are_nan(inv, out, K, T, E, N):
     """A gathered index outside [0, x_rows) gives a NaN output row; every other
     row is bitwise the plain K-leaf GEMM of its gathered input row (both store
