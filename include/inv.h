@@ -172,8 +172,8 @@ typedef enum inv_digest_kind {
   INV_DIGEST_DEPLOYMENT = 3
 } inv_digest_kind;
 
-/* Canonical JSON of a composition of n entries (each region at most once, in
- * any order; written sorted by region): compact, fixed key order, integers
+/* Canonical JSON of a composition of n >= 1 entries (each region at most
+ * once, in any order; written sorted by region): compact, fixed key order, integers
  * and ASCII strings only, floats as IEEE-754 bit patterns, so one
  * composition has one byte sequence. Layout:
  *   {"ExecutionContract":{"cases":[..],"composition":[..],"claims":{..},

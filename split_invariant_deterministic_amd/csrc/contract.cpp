@@ -124,7 +124,7 @@ void sha256(const uint8_t* data, size_t n, uint8_t out[32]) {
   // padding: 0x80, zeros, then the bit length as a 64-bit big-endian integer
   uint8_t tail[128] = {0};
   const size_t rem = n - i;
-  std::memcpy(tail, data + i, rem);
+  if (rem) std::memcpy(tail, data + i, rem);  // data may be NULL when n == 0
   tail[rem] = 0x80;
   const size_t tl = rem + 1 + 8 <= 64 ? 64 : 128;
   const uint64_t bits = (uint64_t)n * 8u;
