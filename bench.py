@@ -497,12 +497,15 @@ def cpu_oracle_configs(ctx, stages, budget_s=3.0):
     return out
 
 
-def device_record(torch, inv):
-    """CU count, clocks and the MFMA ceiling of the device the run used."""
+def host_device_query():
+    """rocminfo / rocm-smi facts (GPU CU count, max clock, current clocks), read
+    by child processes before this process touches the GPU. Skipped under a
+    profiler's preloaded tool, which would initialise the GPU in the children."""
     import subprocess
-    p = torch.cuda.get_device_properties(0)
-    rec = {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
-           "hbm_gib": round(p.total_memory / 2 ** 30, 1)}
+    rec = {}
+    if "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF") for k in os.environ):
+        rec["rocm_smi_clocks"] = rec["rocminfo"] = "skipped under a profiler"
+        return rec
     for cmd, key in ((["rocm-smi", "--showclocks"], "rocm_smi_clocks"), (["rocminfo"], "rocminfo")):
         try:
             r = subprocess.run(cmd, capture_output=True, text=True, timeout=30)
@@ -528,8 +531,17 @@ def device_record(torch, inv):
                 rec[key] = [l.strip() for l in lines if "sclk" in l or "mclk" in l or "fclk" in l][:6]
         except Exception as e:  # the record is context; its absence is reported, not fatal
             rec[key] = f"unavailable: {type(e).__name__}"
+    return rec
+
+
+def device_record(torch, inv, host_rec):
+    """CU count, clocks and the MFMA ceiling of the device the run used."""
+    p = torch.cuda.get_device_properties(0)
+    rec = {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
+           "hbm_gib": round(p.total_memory / 2 ** 30, 1)}
+    rec.update(host_rec)
     # the MFMA ceiling: register-only chains of the path's bf16 instruction, 4 workgroups per CU
-    groups, iters = 4 * p.multi_processor_count, 20000
+    groups, iters = 4 * p.multi_processor_count, 6000
     best = None
     for _ in range(3):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -581,6 +593,7 @@ def main():
         print(json.dumps({"error": "this library runs on one GPU only; multi-GPU sharding is a design "
                                    "note (no collectives are built), run with --gpus 1"}))
         sys.exit(2)
+    host_rec = host_device_query()  # child processes, before this process initialises the GPU
     import torch
     import torch.nn.functional as F
 
@@ -757,7 +770,7 @@ def main():
     if args.invariance_repeats >= 0:
         inv_rep = invariance(torch, inv, synth, step, last, ctx, stages, repeats=args.invariance_repeats)
         log(f"invariance: {inv_rep['elements_mismatched']} of {inv_rep['elements_compared']} elements differ")
-    dev_rec = device_record(torch, inv)
+    dev_rec = device_record(torch, inv, host_rec)
     log("device record and MFMA ceiling done")
 
     # ------------------------------------------------------------ fast paths
