@@ -177,10 +177,10 @@ __device__ __forceinline__ void lp_rows_epilogue(const TileParams& p, const floa
 // 128 x 128 tile (4 x 2 MFMA blocks of 16 x 16).
 constexpr int kRingWaves = 8;
 
-template <int BK, int RING = 131072>
+template <int BK, int RING = 131072, int BM_ = 128>
 struct Ring {
   static constexpr int NW = kRingWaves;
-  static constexpr int BM = 128, BN = 128;
+  static constexpr int BM = BM_, BN = 128;
   static constexpr int ROWB = BK * 2;          // bytes per staged row
   static constexpr int CPR = BK / 8;           // 16-byte chunks per row
   static constexpr int RPW = 16 / CPR;         // rows per 256-byte bank window
@@ -190,6 +190,7 @@ struct Ring {
   static constexpr int LB = BBYTES / (1024 * NW);
   static constexpr int LOADS = LA + LB;
   static constexpr int NS = RING / STAGE;      // stages in the ring
+  static_assert(LA * 1024 * NW == ABYTES && LB * 1024 * NW == BBYTES, "whole 1 KB loads per wave");
   static __device__ __forceinline__ int slot(int r, int c) { return c ^ ((r / RPW) % CPR); }
   static __device__ __forceinline__ int off(int r, int c) { return r * ROWB + (slot(r, c) << 4); }
 };
@@ -223,11 +224,12 @@ __device__ __forceinline__ void wait_vm_rem(int rem) {
 
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-template <int BK, int RING, bool ODD = false>
+template <int BK, int RING, bool ODD = false, int BM_ = 128>
 struct RingCtx {
-  using R = Ring<BK, RING>;
+  using R = Ring<BK, RING, BM_>;
   static constexpr int NW = R::NW;
-  static constexpr int WN = 128 / (NW / 2);  // wave tile: 64 rows x WN columns
+  static constexpr int WCOLS = NW / (R::BM / 64);  // waves across the tile's columns
+  static constexpr int WN = R::BN / WCOLS;         // wave tile: 64 rows x WN columns
   static constexpr int FN = WN / 16;
   using Acc = AccT<4, FN>;
   static constexpr int USED = R::NS * R::STAGE;  // ring bytes in use
@@ -278,6 +280,15 @@ struct RingCtx {
       __builtin_amdgcn_global_load_lds(bbase + iss_k * 2 + boff[u - R::LA],
                                        &dst[R::ABYTES + (wave + NW * (u - R::LA)) * 1024], 16, 0, 0);
 #endif
+  }
+  // The stage's loads spread evenly over the 4 * F MFMAs of a k substep:
+  // before MFMA q go the loads u with ceil(q L / T) <= u < ceil((q+1) L / T)
+  // (T = 4F MFMAs, L loads), so the first MFMA always has one before it.
+  template <int F>
+  __device__ __forceinline__ void issue_before(int q) {
+    constexpr int T = 4 * F, L = R::LOADS;
+#pragma unroll
+    for (int u = (q * L + T - 1) / T; u < ((q + 1) * L + T - 1) / T; ++u) issue_one(u);
   }
   __device__ __forceinline__ void issue_done() {
     iss_k += BK;
@@ -377,15 +388,12 @@ struct RingCtx {
     // MFMAs of substep 1 with the loads of stage g+NS (into stage g's slot)
     // spread between them
     const bool more = issued < limit;
-    constexpr int LPI = R::LOADS / 4;  // loads per operand row block
-    static_assert(LPI * 4 == R::LOADS && FN % LPI == 0, "interleave");
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int h = 0; h < LPI; ++h) {
-        if (more) issue_one(LPI * i + h);
-#pragma unroll
-        for (int j = h * FN / LPI; j < (h + 1) * FN / LPI; ++j) acc.v[i][j] = mfma16(fa1[i], fb1[j], acc.v[i][j]);
+      for (int j = 0; j < FN; ++j) {
+        if (more) issue_before<FN>(i * FN + j);
+        acc.v[i][j] = mfma16(fa1[i], fb1[j], acc.v[i][j]);
       }
     if (more) issue_done();
     ++g;
@@ -423,16 +431,12 @@ struct RingCtx {
     rd_off = next_slot(rd_off);
     read_frags(rd_off, 0, fa0, fb0);
     const bool more = issued < limit;
-    constexpr int LPI = R::LOADS / 4;
-    static_assert(LPI * 4 == R::LOADS && FN % LPI == 0, "interleave");
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int h = 0; h < LPI; ++h) {
-        if (more) issue_one(LPI * i + h);
-#pragma unroll
-        for (int j = h * FN / LPI; j < (h + 1) * FN / LPI; ++j)
-          b.v[i][j] = mfma16(fa1[i], fb1[j], f32x4{0.f, 0.f, 0.f, 0.f});  // the second leaf starts at +0
+      for (int j = 0; j < FN; ++j) {
+        if (more) issue_before<FN>(i * FN + j);
+        b.v[i][j] = mfma16(fa1[i], fb1[j], f32x4{0.f, 0.f, 0.f, 0.f});  // the second leaf starts at +0
       }
     if (more) issue_done();
     ++g;
@@ -472,13 +476,23 @@ struct RingCtx {
 // the finished left half (leaves 0-3) then waits in LDS (64 KB for the 8
 // waves, each lane its own values) while the right half runs in registers,
 // and the ring shrinks to 96 KB. The arithmetic is the same tree.
-template <int NL>
-constexpr int ring_bytes() { return NL == 8 ? 98304 : 131072; }
+//
+// Tiles of 64 rows (M <= 64, 64-k stages): 8 waves side by side, each 64 x 16
+// (4 x 1 MFMA blocks). A stage is then 8 KB of A and 16 KB of weights
+// instead of 16 + 16 KB, so the same LDS holds twice the weight bytes in
+// flight, and no MFMA runs on padding rows. Four 16-register sets hold the
+// 8-leaf tree, so there is no spill; the ring takes 5 stages (120 KB) and
+// each wave transposes its result through a 5 KB slice of its own, which
+// lets every 64-row launch run persistent.
+template <int NL, int BM>
+constexpr int ring_bytes() { return BM == 64 ? 122880 : NL == 8 ? 98304 : 131072; }
 
 // Position and operand addressing of one output tile of the ring kernel.
 template <int LA, int LB>
 struct TileAddr {
   int64_t m0, m_end, n0;
+  int64_t k0;  // first k of the tile's leaves (64-row tiles)
+  int z;       // leaf group, the partial plane of C (64-row tiles)
   const uint8_t* abase;
   const uint8_t* bbase;
   uint32_t aoff[LA];
@@ -487,22 +501,30 @@ struct TileAddr {
 
 // ODD: leaves that are an odd multiple of 32 on 64-k stages (NL even, so the
 // range is whole stages).
-template <int NL, int BK, int OUTM, bool GROUPED, bool ODD = false>
+// BM: tile rows, 128 or 64. A 64-row launch folds the leaf groups into the
+// tile index (tile = group * tiles + position), so that it can run
+// persistent over all of them.
+template <int NL, int BK, int OUTM, bool GROUPED, bool ODD = false, int BM = 128>
 __global__ __launch_bounds__(64 * kRingWaves, 1) void gemm_ring_kernel(TileParams p) {
-  constexpr int RING = ring_bytes<NL>();
-  constexpr int SPILL = NL == 8 ? 65536 : 0;
-  using R = Ring<BK, RING>;
-  using Ctx = RingCtx<BK, RING, ODD>;
+  static_assert(BM == 128 || (BM == 64 && BK == 64 && !ODD && !GROUPED), "64-row tiles: plain launches, 64-k stages");
+  constexpr int RING = ring_bytes<NL, BM>();
+  constexpr int SPILL = BM == 128 && NL == 8 ? 65536 : 0;
+  using R = Ring<BK, RING, BM>;
+  using Ctx = RingCtx<BK, RING, ODD, BM>;
   static_assert(!ODD || (BK == 64 && NL % 2 == 0), "odd leaves pair up into 64-k stages");
   constexpr int NW = Ctx::NW, WN = Ctx::WN, FN = Ctx::FN;
   constexpr int LPS = WN + 4;  // row stride of the transposed tile (floats)
+  // 64-row tiles: each wave's own transpose slice after the ring
+  constexpr int EPI = BM == 64 ? NW * 64 * LPS * 4 : 0;
   constexpr int LP_BYTES = OUTM == kOutLP ? NW * 64 * LPS * 4 : 0;
-  constexpr int LDS_BYTES = R::NS * R::STAGE + SPILL > LP_BYTES ? R::NS * R::STAGE + SPILL : LP_BYTES;
+  constexpr int LDS_USED = R::NS * R::STAGE + SPILL + EPI;
+  constexpr int LDS_BYTES = LDS_USED > LP_BYTES ? LDS_USED : LP_BYTES;
+  static_assert(LDS_BYTES <= 163840, "160 KB of LDS");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
   // Persistent launches take several tiles per workgroup and let the ring
   // run on into the next tile's stages (8 leaves on 64-k stages, odd
-  // multiples of 32 included).
-  constexpr bool PERSIST_OK = NL == 8 && BK == 64;
+  // multiples of 32 included; every 64-row launch).
+  constexpr bool PERSIST_OK = (NL == 8 && BK == 64) || BM == 64;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -528,6 +550,7 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void gemm_ring_kernel(TileParam
     int lane = tid & 63;
     asm volatile("" : "+v"(lane));
     int64_t m0, m_end, n0;
+    int z = blockIdx.z;
     const uint16_t* B = p.B;
     if constexpr (GROUPED) {
      if (p.E <= 128) {
@@ -639,6 +662,10 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void gemm_ring_kernel(TileParam
       // B panels in its L2.
       const int tiles_m = (int)((p.M + R::BM - 1) / R::BM);
       const int nb = tiles_m * tiles_n;
+      if constexpr (BM == 64) {
+        z = (int)(tile / nb);
+        tile -= (int64_t)z * nb;
+      }
       int t = (int)tile;
       if (nb % 8 == 0) t = (t % 8) * (nb / 8) + t / 8;
       constexpr int GM = 4;
@@ -680,13 +707,17 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void gemm_ring_kernel(TileParam
     T.m0 = m0;
     T.m_end = m_end;
     T.n0 = n0;
+    T.z = z;
+    T.k0 = (int64_t)(p.leaf_lo + z * NL) * p.kl;
     return true;
   };
   TileAddr<R::LA, R::LB> cur;
   int64_t tile = blockIdx.x;
   if (!setup(tile, cur)) return;  // uniform exit before any barrier
-  const int z = blockIdx.z;
-  const int leaf0 = p.leaf_lo + z * NL;
+  // 128-row tiles: one leaf group per launch row (blockIdx.z), the same for
+  // every tile of the workgroup
+  const int zg = blockIdx.z;
+  const int64_t kg = (int64_t)(p.leaf_lo + zg * NL) * p.kl;
 
   Ctx c;
   c.lds = lds;
@@ -696,7 +727,7 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void gemm_ring_kernel(TileParam
   c.rd_off = 0;
   c.spl = ODD ? p.kl / 32 : p.kl / BK;
   c.g = 0;
-  const int wm = c.wave / (NW / 2), wn = c.wave % (NW / 2);  // wave tile (row, column) in the tile
+  const int wm = c.wave / Ctx::WCOLS, wn = c.wave % Ctx::WCOLS;  // wave tile (row, column) in the tile
   {
     const int g4 = lane >> 4, r16 = lane & 15;
 #pragma unroll
@@ -706,14 +737,13 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void gemm_ring_kernel(TileParam
     }
   }
   const int stages = ODD ? NL * p.kl / 64 : c.spl * NL;  // per tile
-  const int64_t k0 = (int64_t)leaf0 * p.kl;
   c.abase = cur.abase;
   c.bbase = cur.bbase;
 #pragma unroll
   for (int u = 0; u < R::LA; ++u) c.aoff[u] = cur.aoff[u];
 #pragma unroll
   for (int u = 0; u < R::LB; ++u) c.boff[u] = cur.boff[u];
-  c.iss_k = k0;
+  c.iss_k = BM == 64 ? cur.k0 : kg;
   c.iss_end = stages;
   c.limit = stages;
   c.has_next = false;
@@ -723,6 +753,7 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void gemm_ring_kernel(TileParam
   auto finish = [&](const TileAddr<R::LA, R::LB>& T, typename Ctx::Acc& acc) {
     int lane = tid & 63;
     asm volatile("" : "+v"(lane));
+    const int z = BM == 64 ? T.z : zg;
     const int64_t rbase = T.m0 + wm * 64 + 4 * (lane >> 4);
     const int64_t cbase = T.n0 + wn * WN + (lane & 15);
     if constexpr (SWI) {
@@ -808,8 +839,10 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void gemm_ring_kernel(TileParam
             }
         lp_rows_epilogue<FN, 32, true>(p, t, row, row < T.m_end, T.n0 + wn * WN, lane);
       } else {
-        block_barrier();  // every wave has consumed its last ring stage
-        float* t = reinterpret_cast<float*>(lds) + wave * 64 * LPS;
+        // 64-row tiles: the wave's own slice after the ring; else the ring,
+        // once every wave has consumed its last stage
+        if constexpr (EPI == 0) block_barrier();
+        float* t = reinterpret_cast<float*>(lds + (EPI > 0 ? R::NS * R::STAGE : 0)) + wave * 64 * LPS;
   #pragma unroll
         for (int i = 0; i < 4; ++i)
   #pragma unroll
@@ -837,11 +870,12 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void gemm_ring_kernel(TileParam
       // floats, free once the tree is summed, touched by no other wave; in a
       // persistent launch the ring already holds the next tile's stages), else
       // the ring once every wave has left it.
+      // (64-row tiles: the wave's own slice after the ring)
       constexpr int LPX = SPILL > 0 ? WN : LPS;
-      if constexpr (SPILL == 0) block_barrier();  // every wave has consumed its last ring stage
+      if constexpr (SPILL == 0 && EPI == 0) block_barrier();  // every wave has consumed its last ring stage
       if (whole) {
         float* t = SPILL > 0 ? reinterpret_cast<float*>(&lds[R::NS * R::STAGE]) + wave * 64 * WN
-                             : reinterpret_cast<float*>(lds) + wave * 64 * LPS;
+                             : reinterpret_cast<float*>(lds + (EPI > 0 ? R::NS * R::STAGE : 0)) + wave * 64 * LPS;
   #pragma unroll
         for (int i = 0; i < 4; ++i)
   #pragma unroll
@@ -922,7 +956,7 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void gemm_ring_kernel(TileParam
         for (int u = 0; u < R::LA; ++u) c.naoff[u] = nx.aoff[u];
 #pragma unroll
         for (int u = 0; u < R::LB; ++u) c.nboff[u] = nx.boff[u];
-        c.nk0 = k0;
+        c.nk0 = BM == 64 ? nx.k0 : kg;
         c.nstages = stages;
         c.has_next = true;
         c.limit += stages;
@@ -1186,6 +1220,19 @@ hipError_t ring_dispatch(const TileParams& p, dim3 grid, int nl, hipStream_t s) 
 }
 #undef INV_RING_CASE
 
+// 64-row tiles (plain launches, leaves a multiple of 64)
+template <int OUTM>
+hipError_t ring64_dispatch(const TileParams& p, dim3 grid, int nl, hipStream_t s) {
+  switch (nl) {
+    case 1: hipLaunchKernelGGL((gemm_ring_kernel<1, 64, OUTM, false, false, 64>), grid, dim3(64 * kRingWaves), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((gemm_ring_kernel<2, 64, OUTM, false, false, 64>), grid, dim3(64 * kRingWaves), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((gemm_ring_kernel<4, 64, OUTM, false, false, 64>), grid, dim3(64 * kRingWaves), 0, s, p); break;
+    case 8: hipLaunchKernelGGL((gemm_ring_kernel<8, 64, OUTM, false, false, 64>), grid, dim3(64 * kRingWaves), 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <int FM, int OUTM>
 hipError_t stream_dispatch_nw(const TileParams& p, dim3 grid, int nw, hipStream_t s) {
   switch (nw) {
@@ -1287,6 +1334,19 @@ hipError_t launch_gemm(const GemmLaunch& g, hipStream_t s) {
     dim3 grid((unsigned)((g.N + 15) / 16), 1u, (unsigned)g.groups);
     if (lp) return stream_dispatch<kOutLP>(p, fm, grid, g.nl, s);
     return g.out_bf16 ? stream_dispatch<kOutBF16>(p, fm, grid, g.nl, s) : stream_dispatch<kOutF32>(p, fm, grid, g.nl, s);
+  }
+  if (g.M <= 64 && g.kl % 64 == 0) {
+    // 64-row tiles, the leaf groups folded into the tile index; persistent
+    // whenever there are more tiles than CUs
+    const int64_t items = ((g.N + 127) / 128) * g.groups;
+    dim3 grid((unsigned)items);
+    if (items > kResident) {
+      p.persist = 1;
+      p.ntiles = items;
+      grid.x = (unsigned)kResident;
+    }
+    if (lp) return ring64_dispatch<kOutLP>(p, grid, g.nl, s);
+    return g.out_bf16 ? ring64_dispatch<kOutBF16>(p, grid, g.nl, s) : ring64_dispatch<kOutF32>(p, grid, g.nl, s);
   }
   const int64_t tiles = ((g.M + 127) / 128) * ((g.N + 127) / 128);
   dim3 grid((unsigned)tiles, 1u, (unsigned)g.groups);

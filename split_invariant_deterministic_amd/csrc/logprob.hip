@@ -247,44 +247,41 @@ __global__ __launch_bounds__(256) void block16_stats_kernel(const float* __restr
   }
 }
 
-// Balanced tree over the B blocks [j0, j0+B) (identity past nb), in registers.
-template <int B>
-__device__ __forceinline__ MS block_subtree(const float* __restrict__ st, int64_t j0, int64_t nb) {
-  MS v[B];
-#pragma unroll
-  for (int i = 0; i < B; ++i) {
-    const int64_t j = j0 + i;
-    if (j < nb) {
-      const float2 q = *reinterpret_cast<const float2*>(st + 2 * j);
-      v[i] = MS{q.x, q.y};
-    } else {
-      v[i] = MS{-INFINITY, 0.0f};
-    }
-  }
-#pragma unroll
-  for (int w = B; w > 1; w /= 2)
-#pragma unroll
-    for (int k = 0; k < w / 2; ++k) v[k] = lse_merge(v[2 * k], v[2 * k + 1]);
-  return v[0];
-}
-
 // One workgroup per row. P = 2^ceil(log2 nb) leaves; thread t reduces the
-// aligned block of B = max(1, P/256) leaves, then an LDS tree joins the
-// T = P/B thread results pairwise, level by level: together one balanced
-// tree over the P leaves.
+// aligned block of B = max(1, P/256) leaves [tB, tB+B) by the balanced tree
+// over it, then an LDS tree joins the T = P/B thread results pairwise, level
+// by level: together one balanced tree over the P leaves, leaves past nb
+// being the merge identity (-inf, 0).
+//
+// The leaves reach the threads through LDS in pieces of PB = min(B, 16)
+// leaves per thread, so that the global reads are whole 128-byte lines
+// (16 lanes read one thread's 16 consecutive (m, s) pairs) instead of one
+// 8-byte pair per lane 8B bytes apart. In LDS, leaf i of thread t's piece
+// sits at i * S + t (S odd, at least the threads in use), so the staging
+// writes spread over the banks and each thread's reads are consecutive
+// across the wave. A thread's B leaves are NP = B / PB aligned pieces: the
+// subtree over each piece, then the balanced tree over the pieces, is the
+// balanced tree over the B leaves.
+constexpr int kMergePiece = 16;
+constexpr int kMergeStride = 257;  // odd, >= 256 threads
+
 template <int B>
 __global__ __launch_bounds__(256) void block16_merge_kernel(const float* __restrict__ stats,
                                                             const float* __restrict__ tlogit,
                                                             const int32_t* __restrict__ target,
                                                             float* __restrict__ out, int64_t V, int T, int fold) {
+  constexpr int PB = B < kMergePiece ? B : kMergePiece;
+  constexpr int NP = B / PB;
   __shared__ MS part[256];
+  __shared__ float2 stage[PB * kMergeStride];
   const int64_t row = blockIdx.x;
   const int64_t nb = (V + 15) / 16;
   const float* st = stats + 2 * row * nb;
+  const int tid = threadIdx.x;
   MS root;
   if (fold) {
     __shared__ MS r0;
-    if (threadIdx.x == 0) {
+    if (tid == 0) {
       MS a{st[0], st[1]};
       for (int64_t j = 1; j < nb; ++j) a = lse_merge(a, MS{st[2 * j], st[2 * j + 1]});
       r0 = a;
@@ -292,10 +289,56 @@ __global__ __launch_bounds__(256) void block16_merge_kernel(const float* __restr
     __syncthreads();
     root = r0;
   } else {
-    if ((int)threadIdx.x < T) part[threadIdx.x] = block_subtree<B>(st, (int64_t)threadIdx.x * B, nb);
+    // threads holding at least one real leaf; the rest reduce identities only
+    const int TU = (int)((nb + B - 1) / B);
+    // Every piece's global loads are issued up front (at most 16 pairs per
+    // thread per piece: TU * PB <= 256 * 16), so a lone row pays one memory
+    // latency, not one per piece.
+    float2 ld[NP][kMergePiece];
+#pragma unroll
+    for (int q = 0; q < NP; ++q)
+#pragma unroll
+      for (int r = 0; r < kMergePiece; ++r) {
+        const int e = tid + 256 * r;
+        const int t = e / PB, i = e % PB;
+        const int64_t j = (int64_t)t * B + q * PB + i;
+        ld[q][r] = make_float2(-INFINITY, 0.0f);
+        if (e < TU * PB && j < nb) ld[q][r] = *reinterpret_cast<const float2*>(st + 2 * j);
+      }
+    MS pv[NP];
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+      if (q > 0) __syncthreads();  // every thread has read the previous piece
+#pragma unroll
+      for (int r = 0; r < kMergePiece; ++r) {
+        const int e = tid + 256 * r;
+        if (e < TU * PB) stage[(e % PB) * kMergeStride + e / PB] = ld[q][r];
+      }
+      __syncthreads();
+      MS v[PB];
+#pragma unroll
+      for (int i = 0; i < PB; ++i) {
+        if (tid < TU) {
+          const float2 f = stage[i * kMergeStride + tid];
+          v[i] = MS{f.x, f.y};
+        } else {
+          v[i] = MS{-INFINITY, 0.0f};
+        }
+      }
+#pragma unroll
+      for (int w = PB; w > 1; w /= 2)
+#pragma unroll
+        for (int k = 0; k < w / 2; ++k) v[k] = lse_merge(v[2 * k], v[2 * k + 1]);
+      pv[q] = v[0];
+    }
+#pragma unroll
+    for (int w = NP; w > 1; w /= 2)
+#pragma unroll
+      for (int k = 0; k < w / 2; ++k) pv[k] = lse_merge(pv[2 * k], pv[2 * k + 1]);
+    if (tid < T) part[tid] = pv[0];
     __syncthreads();
     for (int n = T; n > 1; n >>= 1) {
-      const int j = threadIdx.x;
+      const int j = tid;
       MS r{0.f, 0.f};
       if (j < n / 2) r = lse_merge(part[2 * j], part[2 * j + 1]);
       __syncthreads();
@@ -304,7 +347,7 @@ __global__ __launch_bounds__(256) void block16_merge_kernel(const float* __restr
     }
     root = part[0];
   }
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     const int32_t t = target[row];
     const float lse = root.m + log2_hw(root.s) * kLn2;
     out[row] = (t >= 0 && t < V) ? tlogit[row] - lse : __builtin_nanf("");

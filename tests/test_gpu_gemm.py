@@ -152,7 +152,7 @@ def test_dense_batch_invariance_and_sampled_oracle(inv, dense_inputs, K, N):
 
 
 @pytest.mark.parametrize("K,N", DENSE)
-@pytest.mark.parametrize("M", [7, 512])
+@pytest.mark.parametrize("M", [7, 33, 512])
 def test_rank_partitions_are_bitwise_equal(inv, dense_inputs, K, N, M):
     X, W = dense_inputs[(K, N)]
     X = X[:M].contiguous()
