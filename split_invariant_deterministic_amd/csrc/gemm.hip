@@ -295,17 +295,24 @@ struct RingCtx {
     iss_off += R::STAGE;
     if (iss_off == USED) iss_off = 0;
     ++issued;
-    if (issued == iss_end && has_next) {  // wave-uniform
-      abase = nabase;
-      bbase = nbbase;
+    if (issued == iss_end && has_next) take_next();  // wave-uniform
+  }
+  // The issue side moves on to the next tile's operands. Called when the
+  // current tile's last stage has been issued and the next tile is set up,
+  // whichever of the two comes last: with fewer stages per tile than the
+  // ring holds, every stage of a tile can be issued before that tile's own
+  // turn in the loop sets up its successor (issued never passes limit,
+  // which ends at iss_end until then).
+  __device__ __forceinline__ void take_next() {
+    abase = nabase;
+    bbase = nbbase;
 #pragma unroll
-      for (int u = 0; u < R::LA; ++u) aoff[u] = naoff[u];
+    for (int u = 0; u < R::LA; ++u) aoff[u] = naoff[u];
 #pragma unroll
-      for (int u = 0; u < R::LB; ++u) boff[u] = nboff[u];
-      iss_k = nk0;
-      iss_end += nstages;
-      has_next = false;
-    }
+    for (int u = 0; u < R::LB; ++u) boff[u] = nboff[u];
+    iss_k = nk0;
+    iss_end += nstages;
+    has_next = false;
   }
   __device__ __forceinline__ void issue_next() {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -960,6 +967,7 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void gemm_ring_kernel(TileParam
         c.nstages = stages;
         c.has_next = true;
         c.limit += stages;
+        if (c.issued == c.iss_end) c.take_next();  // this tile's stages were all issued already
       }
     }
     typename Ctx::Acc acc;

@@ -257,3 +257,34 @@ def test_leaves_of_32_rank_partitions_and_oracle(inv, M):
     rows = np.array([0, M // 2, M - 1])
     ref = ogemm.gemm_tree(X[torch.as_tensor(rows, device=DEV)].float().cpu().numpy(), W.float().cpu().numpy(), 8, "bf16")
     check_bf16(base[torch.as_tensor(rows, device=DEV)], ref, f"leaves of 32, M={M}")
+
+
+@pytest.mark.parametrize("M,N,K,out", [(9, 1000, 1024, "bf16"), (40, 515, 2048, "fp32"), (64, 130, 512, "bf16"),
+                                       (33, 16400, 1024, "fp32")])  # 129 column tiles x 2 groups: persistent
+def test_small_m_64_row_tiles(inv, M, N, K, out):
+    """8 <= M <= 64 runs on 64-row tiles (8 waves of 64 x 16), persistent when
+    the (column tile, leaf group) items outnumber the CUs. Ragged columns,
+    leaf groups, emulated ranks and per-leaf launches all give the bits of the
+    128-row tiles (the same rows inside a 65-row launch), and the result
+    matches the oracle element by element. The last case's ranks 4 and 8
+    walk 516 and 1032 persistent items of 4 and 2 stages, fewer than the
+    5-stage ring holds: every stage of an item is issued before the item's
+    own turn sets up its successor (the issue side then switches tiles at
+    that set-up)."""
+    X = synth.randn((65, K), 151).to(DEV)
+    W = synth.randn((N, K), 152, 0.02).to(DEV)
+    c = inv.contract(leaves=8, out=out)
+    big = inv.gemm(X, W, c)  # 65 rows: 128-row tiles
+    Xm = X[:M].contiguous()
+    base = inv.gemm(Xm, W, c, use_ws=False)
+    assert bitwise_equal(base, big[:M])
+    assert bitwise_equal(inv.gemm(Xm, W, c), base)  # with the leaf-group workspace
+    for R in (2, 4, 8):
+        assert bitwise_equal(inv.gemm(Xm, W, inv.contract(leaves=8, ranks=R, out=out)), base), R
+    P8 = inv.gemm_leaves(Xm, W, 0, 8, inv.contract(leaves=8, out="fp32"))
+    assert bitwise_equal(inv.tree_combine(P8, c), base)
+    ref = ogemm.gemm_tree(Xm.float().cpu().numpy(), W.float().cpu().numpy(), 8, out)
+    if out == "bf16":
+        check_bf16(base, ref, f"64-row tiles M={M} N={N} K={K}")
+    else:
+        check_fp32_gemm(base, ref, f"64-row tiles M={M} N={N} K={K}")
