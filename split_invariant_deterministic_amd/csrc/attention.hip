@@ -33,6 +33,8 @@
 // takes as its A operand. V rows go straight from HBM into LDS (direct
 // loads) and the P.V B operand is read back transposed with the gfx950
 // transpose read, holding the same 8 keys in the same slots.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -71,9 +73,16 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
 #endif
 }
 
+// s_waitcnt vmcnt(N) (N < 64), expcnt and lgkmcnt not waited on, through
+// the builtin: the compiler then knows which loads have landed (in
+// particular the direct-to-LDS loads older than the last N), and does not
+// add a wait for every outstanding load before the LDS reads that follow.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
 }
 
 template <int CH>
@@ -179,15 +188,15 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a, float scal
     (void)cc;
 #endif
   };
-  if (c0 < c1) {
-    load_k(c0);
-    load_v(c0);
-  }
-  for (int64_t c = c0; c < c1; ++c) {
-    const int64_t kbase = c * CH;  // position of the chunk's first key
-    const bool more = c + 1 < c1;   // uniform
-    // ---- S^T = K Q^T: lane holds keys kb*16 + 4*g4 + r for head c16
-    f32x4 st[Cfg::KB];
+  // ---- S^T = K Q^T: lane holds keys kb*16 + 4*g4 + r for head c16
+  f32x4 st[Cfg::KB];
+  auto scores = [&]() {
+    // The fragments pass through an empty asm statement, so that the score
+    // MFMAs are not scheduled above the wait that precedes this call.
+#pragma unroll
+    for (int kb = 0; kb < Cfg::KB; ++kb)
+#pragma unroll
+      for (int ds = 0; ds < 4; ++ds) asm volatile("" : "+v"(kf[kb][ds]));
 #pragma unroll
     for (int kb = 0; kb < Cfg::KB; ++kb) {
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -195,7 +204,24 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a, float scal
       for (int ds = 0; ds < 4; ++ds) acc = mfma16(kf[kb][ds], qf[ds], acc);
       st[kb] = acc;
     }
-    if (more) load_k(c + 1);
+  };
+  // The loop is rotated and its last chunk peeled: a chunk with a successor
+  // loads that successor's K fragments at its start and its V rows once the
+  // P.V reads are done, then turns the fragments into the successor's
+  // scores. No register load is then carried across the back edge and the
+  // loop body has no branch, so the only waits are the explicit ones below;
+  // the compiler otherwise waited for every outstanding load at the loop
+  // head, the V rows just prefetched into LDS included.
+  if (c0 < c1) {
+    load_k(c0);
+    load_v(c0);
+    wait_vm<Cfg::VDMA>();  // the K fragments, issued before the V rows
+    scores();
+  }
+  auto chunk = [&](int64_t c, auto has_next) {
+    constexpr bool MORE = decltype(has_next)::value;
+    const int64_t kbase = c * CH;  // position of the chunk's first key
+    if constexpr (MORE) load_k(c + 1);
     float cmax = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < Cfg::KB; ++kb)
@@ -244,8 +270,7 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a, float scal
       for (int r = 0; r < 4; ++r) o[db][r] = o[db][r] * al[r];
     // this wave's V rows of chunk c are in LDS once at most the next chunk's
     // K loads (issued after them) are outstanding
-    if (more) wait_vm<Cfg::KB * 4>();
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_vm<MORE ? Cfg::KB * 4 : 0>();
 #pragma unroll
     for (int t = 0; t < Cfg::PV; ++t) {
       // A operand: head c16, keys {32t + 4 g4 + e} (e < 4) and {32t + 16 + 4 g4 + e - 4}
@@ -277,9 +302,15 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a, float scal
         o[db] = mfma16(pfl, vf, o[db]);  // then the low parts, in this fixed order
       }
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // V reads done before the next chunk's loads land
-    if (more) load_v(c + 1);
-  }
+    if constexpr (MORE) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // V reads done before the next chunk's rows land
+      load_v(c + 1);
+      wait_vm<Cfg::VDMA>();  // chunk c + 1's K fragments, issued before its V rows
+      scores();
+    }
+  };
+  for (int64_t c = c0; c + 1 < c1; ++c) chunk(c, std::true_type{});
+  if (c0 < c1) chunk(c1 - 1, std::false_type{});
 
   // ---- split state: o (rows = heads 4 g4 + r, col d = 16 db + c16), m, l (head c16)
   float* ws = a.ws;
