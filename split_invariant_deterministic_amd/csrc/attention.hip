@@ -25,14 +25,15 @@
 // m = max(m1,m2), l = l1 f1 + l2 f2, o = o1 f1 + o2 f2 (f = exp2((m_i - m)
 // log2e)), and out = bf16(o / l).
 //
-// One wave computes one (row, kv head, split) for the whole GQA group of
-// query heads (rows of the MFMA tile), so a row's bits depend only on its q,
-// its visible keys and L: a decode row equals the same position's row in a
-// multi-row (prefill) launch. Scores are produced transposed (keys x heads):
-// each lane then holds the 8 probabilities of one head that the P.V MFMA
-// takes as its A operand. V rows go straight from HBM into LDS (direct
-// loads) and the P.V B operand is read back transposed with the gfx950
-// transpose read, holding the same 8 keys in the same slots.
+// One workgroup of NW waves computes one (row, kv head, split) for the whole
+// GQA group of query heads (columns of the score MFMA), so a row's bits
+// depend only on its q, its visible keys and L: a decode row equals the same
+// position's row in a multi-row (prefill) launch, and a batch of one row
+// equals its row in a batch of 256. Scores are produced transposed (keys x
+// heads): each lane then holds the probabilities of one head that the P.V
+// MFMA takes as its A operand. The P.V B operand is read back from an LDS
+// stage of V with the gfx950 transpose read, holding the same keys in the
+// same slots.
 #include <type_traits>
 
 #include "common.h"
@@ -42,14 +43,6 @@ namespace inv {
 namespace {
 
 constexpr int kD = 128;
-
-template <int CH>
-struct AttnCfg {
-  static constexpr int KB = CH / 16;        // 16-key blocks per chunk
-  static constexpr int PV = CH / 32;        // 32-key MFMA steps per chunk
-  static constexpr int ROWB = kD * 2;       // bytes per staged V row (one key)
-  static constexpr int VDMA = CH / 4;       // 1 KB (4-key) direct loads per chunk
-};
 
 // V rows are staged in LDS in their own layout (key-major, d contiguous),
 // 16-byte chunk c of key k stored at chunk c ^ (2 * (k % 4)). The P.V MFMA
@@ -73,24 +66,44 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
 #endif
 }
 
-// s_waitcnt vmcnt(N) (N < 64), expcnt and lgkmcnt not waited on, through
-// the builtin: the compiler then knows which loads have landed (in
-// particular the direct-to-LDS loads older than the last N), and does not
-// add a wait for every outstanding load before the LDS reads that follow.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt");
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-  asm volatile("" ::: "memory");
-}
+// Work split inside the workgroup: wave w computes the scores and
+// probabilities of the chunk's 16-key blocks [w KBW, (w+1) KBW) and the P.V
+// products of the output's 16-wide d blocks [w DBW, (w+1) DBW). Block maxima
+// and the packed probabilities pass through LDS, two barriers per chunk. The
+// order of every reduction is that of the schedule above, whichever wave
+// holds the operands: the chunk max is a max over the same set (exact, and a
+// zero max is made +0), wave 0 rebuilds each lane's probability sum from the
+// packed parts in (block, row) order, and each output d block sees the
+// schedule's MFMA chain. Several waves per item keep the chip busy at decode
+// batches of a few rows, where one wave per item left most CUs idle and each
+// wave bound by its own issue rate.
+//
+// K and V are read through buffer descriptors whose range ends at the chunk's
+// last visible key, so keys past L read as zero without a per-lane clamp and
+// a chunk's addressing is one scalar base; offsets are 32-bit, so CH keys of
+// all kv heads must span less than 2 GiB (checked by the host). V goes
+// through registers into a double-buffered LDS stage: every outstanding load
+// is then a register load whose count the compiler tracks exactly, and the
+// next chunk's loads stay in flight across the exchange reads.
+template <int CH>
+struct AttnCfg {
+  static constexpr int KB = CH / 16;         // 16-key blocks per chunk
+  static constexpr int NW = KB < 4 ? KB : 4;  // waves per (row, kv head, split)
+  static constexpr int KBW = KB / NW;         // 16-key blocks per wave
+  static constexpr int DBW = 8 / NW;          // 16-wide output d blocks per wave
+  static constexpr int PV = CH / 32;          // 32-key MFMA steps per chunk
+  static constexpr int VLD = CH / 4 / NW;     // 1 KB (4-key) V loads per wave per chunk
+};
 
 template <int CH>
-__global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a, float scale) {
+__global__ __launch_bounds__(AttnCfg<CH>::NW * 64) void attn_split_kernel(AttnLaunch a, float scale) {
   using Cfg = AttnCfg<CH>;
-  __shared__ __attribute__((aligned(1024))) uint8_t vs[CH * Cfg::ROWB];
+  constexpr int NW = Cfg::NW, KBW = Cfg::KBW, DBW = Cfg::DBW, VLD = Cfg::VLD;
+  __shared__ __attribute__((aligned(1024))) uint8_t vs[2][CH * kD * 2];
+  __shared__ u32x4 pex[Cfg::KB][64];  // per block and lane: p_hi pairs, then p_lo pairs
+  __shared__ float mex[NW][16];       // per wave: its blocks' max per head
 
-  const int lane = threadIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g4 = lane >> 4, c16 = lane & 15;
   const int nsplit = a.split_hi - a.split_lo;
   int64_t idx = blockIdx.x;
@@ -101,9 +114,6 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a, float scal
   const int grp = a.Hq / a.Hkv;
   const int S = a.split_kv;
 
-  // Row indices come from device memory: a sequence id outside [0, num_seqs)
-  // or a position outside that sequence makes the row's state NaN (the
-  // combine then returns NaN) instead of reading outside the key buffers.
   const int seq = a.q_seq[row];
   bool valid = seq >= 0 && seq < a.num_seqs;
   int64_t start = 0, L = 1;
@@ -114,30 +124,37 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a, float scal
     valid = p >= 0 && p < len;
     L = p + 1;
   }
-  if (!valid) {  // uniform over the block (one wave, one row)
-    float* ws = a.ws;
-    const int64_t hb = row * a.Hq + (int64_t)kvh * grp;
-    for (int h = 0; h < grp; ++h) {
-      float* st = ws + ((hb + h) * S + j) * (kD + 2);
-      st[lane] = __builtin_nanf("");
-      st[lane + 64] = __builtin_nanf("");
-      if (lane < 2) st[kD + lane] = __builtin_nanf("");
+  if (!valid) {  // uniform over the block
+    if (wave == 0) {
+      float* ws = a.ws;
+      const int64_t hb = row * a.Hq + (int64_t)kvh * grp;
+      for (int h = 0; h < grp; ++h) {
+        float* st = ws + ((hb + h) * S + j) * (kD + 2);
+        st[lane] = __builtin_nanf("");
+        st[lane + 64] = __builtin_nanf("");
+        if (lane < 2) st[kD + lane] = __builtin_nanf("");
+      }
     }
     return;
   }
   const int64_t n = (L + CH - 1) / CH;
   const int64_t c0 = ((int64_t)j * n) / S, c1 = ((int64_t)(j + 1) * n) / S;
 
-  const uint16_t* Q = static_cast<const uint16_t*>(a.q);
-  const uint16_t* K = static_cast<const uint16_t*>(a.k);
-  const uint8_t* Vb = static_cast<const uint8_t*>(a.v);
-  const int64_t kv_row = (int64_t)a.Hkv * kD;  // elements between consecutive keys
+  const int64_t rowB = (int64_t)a.Hkv * kD * 2;  // bytes between consecutive keys
+  const uint32_t rb = (uint32_t)rowB;
+  const uint8_t* Kh = static_cast<const uint8_t*>(a.k) + (start * a.Hkv + kvh) * (kD * 2);
+  const uint8_t* Vh = static_cast<const uint8_t*>(a.v) + (start * a.Hkv + kvh) * (kD * 2);
+  // chunk cc of this head's keys, as a range that ends with the chunk's last visible key
+  auto chunk_rsrc = [&](const uint8_t* base, int64_t cc) {
+    const int64_t rem = L - cc * CH;  // visible keys from the chunk's first (>= 1)
+    const uint32_t bytes = rem >= CH ? (uint32_t)(CH * rowB) : (uint32_t)((rem - 1) * rowB + kD * 2);
+    return make_rsrc(base + cc * CH * rowB, bytes);
+  };
 
-  // Q^T as the B operand: column = head c16 of the group, k = d.
   bf16x8 qf[4];
   {
     const bool hv = c16 < grp;
-    const uint16_t* qp = Q + (row * a.Hq + (int64_t)kvh * grp + (hv ? c16 : 0)) * kD;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (row * a.Hq + (int64_t)kvh * grp + (hv ? c16 : 0)) * kD;
 #pragma unroll
     for (int ds = 0; ds < 4; ++ds) {
       u32x4 v = *reinterpret_cast<const u32x4*>(qp + ds * 32 + 8 * g4);
@@ -145,174 +162,159 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a, float scal
       qf[ds] = __builtin_bit_cast(bf16x8, v);
     }
   }
-  // transpose-read lane roles: source lane s = q + 4m of each 16-lane group
   const int tr_m = (lane & 15) >> 2, tr_q = lane & 3;
+  const uint32_t kvo = (uint32_t)c16 * rb + 16u * g4;  // K: key c16 of a block, d = 8 g4 (+ 32 ds)
+  const uint32_t vvo = (uint32_t)g4 * rb + 16u * c16;  // V: key g4 of a 4-key group, 16-byte slot c16
+  const int vlds = g4 * (kD * 2) + vswz(g4, c16) * 16;  // that slot's place in the stage
 
-  float m_run = -INFINITY, l_run = 0.0f;  // per head c16 (identical in the 4 lanes of a head)
-  f32x4 o[8];
-#pragma unroll
-  for (int db = 0; db < 8; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // Loads of chunk c + 1 are issued while chunk c computes: its K fragments
-  // right after the score MFMAs have read chunk c's (same registers), its V
-  // rows right after the P.V reads of chunk c's (same LDS buffer). Keys past
-  // L read a clamped valid key: score row j of the MFMA below depends only
-  // on key row j, and those rows' scores are set to -inf; a clamped V row's
-  // p is exactly 0 and its values are finite cache data. K and V are read
-  // once per (sequence, kv head, split). V's direct loads (1 KB of whole
-  // lines each) stream past the caches; K's fragment loads take 64 bytes of
-  // each 128-byte line per instruction, the other half one instruction
-  // later, so they keep the default policy and the second half hits.
-  bf16x8 kf[Cfg::KB][4];
+  bf16x8 kf[KBW][4];
   auto load_k = [&](int64_t cc) {
+    const buf_rsrc r = chunk_rsrc(Kh, cc);
 #pragma unroll
-    for (int kb = 0; kb < Cfg::KB; ++kb) {
-      const int64_t pos = min(cc * CH + kb * 16 + c16, L - 1);
-      const uint16_t* kp = K + (start + pos) * kv_row + (int64_t)kvh * kD + 8 * g4;
+    for (int kb = 0; kb < KBW; ++kb) {
+      const uint32_t so = (uint32_t)((wave * KBW + kb) * 16) * rb;
 #pragma unroll
-      for (int ds = 0; ds < 4; ++ds)
-        kf[kb][ds] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kp + ds * 32));
+      for (int ds = 0; ds < 4; ++ds) kf[kb][ds] = __builtin_bit_cast(bf16x8, buf_load16(r, kvo + 64u * ds, so));
     }
   };
+  u32x4 vr[VLD];
   auto load_v = [&](int64_t cc) {
-#if defined(__HIP_DEVICE_COMPILE__)
+    const buf_rsrc r = chunk_rsrc(Vh, cc);
 #pragma unroll
-    for (int i = 0; i < Cfg::VDMA; ++i) {
-      const int key = 4 * i + (lane >> 4);
-      const int slot = lane & 15;
-      const int64_t pos = min(cc * CH + key, L - 1);
-      const uint8_t* src = Vb + ((start + pos) * kv_row + (int64_t)kvh * kD) * 2 + vswz(key, slot) * 16;
-      __builtin_amdgcn_global_load_lds(src, &vs[i * 1024], 16, 0, kNT);
+    for (int i = 0; i < VLD; ++i) {
+      const uint32_t so = (uint32_t)(4 * (wave * VLD + i)) * rb;
+      vr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, vvo, so, kNT));
     }
-#else
-    (void)cc;
-#endif
   };
-  // ---- S^T = K Q^T: lane holds keys kb*16 + 4*g4 + r for head c16
-  f32x4 st[Cfg::KB];
+  auto store_v = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < VLD; ++i) *reinterpret_cast<u32x4*>(&vs[buf][(wave * VLD + i) * 1024 + vlds]) = vr[i];
+  };
+  f32x4 st[KBW];
   auto scores = [&]() {
-    // The fragments pass through an empty asm statement, so that the score
-    // MFMAs are not scheduled above the wait that precedes this call.
 #pragma unroll
-    for (int kb = 0; kb < Cfg::KB; ++kb)
-#pragma unroll
-      for (int ds = 0; ds < 4; ++ds) asm volatile("" : "+v"(kf[kb][ds]));
-#pragma unroll
-    for (int kb = 0; kb < Cfg::KB; ++kb) {
+    for (int kb = 0; kb < KBW; ++kb) {
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ds = 0; ds < 4; ++ds) acc = mfma16(kf[kb][ds], qf[ds], acc);
       st[kb] = acc;
     }
   };
-  // The loop is rotated and its last chunk peeled: a chunk with a successor
-  // loads that successor's K fragments at its start and its V rows once the
-  // P.V reads are done, then turns the fragments into the successor's
-  // scores. No register load is then carried across the back edge and the
-  // loop body has no branch, so the only waits are the explicit ones below;
-  // the compiler otherwise waited for every outstanding load at the loop
-  // head, the V rows just prefetched into LDS included.
+
+  float m_run = -INFINITY, l_run = 0.0f;
+  f32x4 o[DBW];
+#pragma unroll
+  for (int db = 0; db < DBW; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
   if (c0 < c1) {
-    load_k(c0);
     load_v(c0);
-    wait_vm<Cfg::VDMA>();  // the K fragments, issued before the V rows
+    load_k(c0);
+    store_v((int)(c0 & 1));
     scores();
   }
+  // A chunk with a successor issues the successor's V and K loads first and
+  // stages them (V into the other LDS buffer, K into scores) at its end.
   auto chunk = [&](int64_t c, auto has_next) {
     constexpr bool MORE = decltype(has_next)::value;
-    const int64_t kbase = c * CH;  // position of the chunk's first key
-    if constexpr (MORE) load_k(c + 1);
-    float cmax = -INFINITY;
+    if constexpr (MORE) {
+      load_v(c + 1);
+      load_k(c + 1);
+    }
+    float bmax = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < Cfg::KB; ++kb)
+    for (int kb = 0; kb < KBW; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t pos = kbase + kb * 16 + 4 * g4 + r;
         float s = st[kb][r] * scale;
-        if (pos >= L) s = -INFINITY;
+        if constexpr (!MORE) {  // only a split's last chunk can hold keys past L
+          const int64_t pos = c * CH + (wave * KBW + kb) * 16 + 4 * g4 + r;
+          if (pos >= L) s = -INFINITY;
+        }
         st[kb][r] = s;
-        cmax = fmaxf(cmax, s);
+        bmax = fmaxf(bmax, s);
       }
-    cmax = fmaxf(cmax, shfl_xor(cmax, 16));
-    cmax = fmaxf(cmax, shfl_xor(cmax, 32));
-    const float m_new = fmaxf(m_run, cmax);
-    const float alpha = exp_shifted(m_run, m_new);
-    float psum = 0.0f;
-    uint32_t pw[Cfg::KB][2];  // bf16 high parts of p, packed pairs
-    uint32_t pl[Cfg::KB][2];  // bf16 low parts: p - high, rounded
+    bmax = fmaxf(bmax, shfl_xor(bmax, 16));
+    bmax = fmaxf(bmax, shfl_xor(bmax, 32));
+    if (g4 == 0) mex[wave][c16] = bmax;
+    __syncthreads();
+    float cmax = mex[0][c16];
 #pragma unroll
-    for (int kb = 0; kb < Cfg::KB; ++kb) {
+    for (int w = 1; w < NW; ++w) cmax = fmaxf(cmax, mex[w][c16]);
+    const float m_new = fmaxf(m_run, cmax) + 0.0f;  // + 0: a zero max is +0 whatever the order
+    const float alpha = exp_shifted(m_run, m_new);
+#pragma unroll
+    for (int kb = 0; kb < KBW; ++kb) {
       float ph[4], plo[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float p = exp_shifted(st[kb][r], m_new);
         ph[r] = bf16_bits_to_f32(f32_to_bf16_bits(p));
-        plo[r] = bf16_bits_to_f32(f32_to_bf16_bits(p - ph[r]));  // p - ph is exact in fp32
-        psum = psum + (ph[r] + plo[r]);                          // exact: at most 16 significant bits
+        plo[r] = bf16_bits_to_f32(f32_to_bf16_bits(p - ph[r]));
       }
-      pw[kb][0] = pack_bf16x2(ph[0], ph[1]);
-      pw[kb][1] = pack_bf16x2(ph[2], ph[3]);
-      pl[kb][0] = pack_bf16x2(plo[0], plo[1]);
-      pl[kb][1] = pack_bf16x2(plo[2], plo[3]);
+      pex[wave * KBW + kb][lane] =
+          u32x4{pack_bf16x2(ph[0], ph[1]), pack_bf16x2(ph[2], ph[3]), pack_bf16x2(plo[0], plo[1]),
+                pack_bf16x2(plo[2], plo[3])};
     }
-    psum = psum + shfl_xor(psum, 16);
-    psum = psum + shfl_xor(psum, 32);
-    l_run = l_run * alpha + psum;
     m_run = m_new;
-
-    // ---- o = P V, started from o * alpha. Output rows = heads 4*g4 + r.
+    __syncthreads();
+    u32x4 px[Cfg::KB];
+#pragma unroll
+    for (int kb = 0; kb < Cfg::KB; ++kb) px[kb] = pex[kb][lane];
+    if (wave == 0) {  // the running sum, in the schedule's (block, row) order
+      float psum = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < Cfg::KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t wh = px[kb][r >> 1], wl = px[kb][2 + (r >> 1)];
+          const float ph = (r & 1) ? bf16_hi(wh) : bf16_lo(wh);
+          const float pl = (r & 1) ? bf16_hi(wl) : bf16_lo(wl);
+          psum = psum + (ph + pl);
+        }
+      psum = psum + shfl_xor(psum, 16);
+      psum = psum + shfl_xor(psum, 32);
+      l_run = l_run * alpha + psum;
+    }
     float al[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) al[r] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((4 * g4 + r) << 2, __builtin_bit_cast(int, alpha)));
+    for (int r = 0; r < 4; ++r)
+      al[r] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((4 * g4 + r) << 2, __builtin_bit_cast(int, alpha)));
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
+    for (int db = 0; db < DBW; ++db)
 #pragma unroll
       for (int r = 0; r < 4; ++r) o[db][r] = o[db][r] * al[r];
-    // this wave's V rows of chunk c are in LDS once at most the next chunk's
-    // K loads (issued after them) are outstanding
-    wait_vm<MORE ? Cfg::KB * 4 : 0>();
+    const uint8_t* vb = vs[c & 1];
 #pragma unroll
     for (int t = 0; t < Cfg::PV; ++t) {
-      // A operand: head c16, keys {32t + 4 g4 + e} (e < 4) and {32t + 16 + 4 g4 + e - 4}
-      u32x4 pa, pb;
-      pa[0] = pw[2 * t][0];
-      pa[1] = pw[2 * t][1];
-      pa[2] = pw[2 * t + 1][0];
-      pa[3] = pw[2 * t + 1][1];
-      pb[0] = pl[2 * t][0];
-      pb[1] = pl[2 * t][1];
-      pb[2] = pl[2 * t + 1][0];
-      pb[3] = pl[2 * t + 1][1];
+      const u32x4 pa = u32x4{px[2 * t][0], px[2 * t][1], px[2 * t + 1][0], px[2 * t + 1][1]};
+      const u32x4 pb = u32x4{px[2 * t][2], px[2 * t][3], px[2 * t + 1][2], px[2 * t + 1][3]};
       const bf16x8 pf = __builtin_bit_cast(bf16x8, pa);
       const bf16x8 pfl = __builtin_bit_cast(bf16x8, pb);
-      // B operand: the same keys for d = 16 db + c16, by two transpose reads
       const int k0 = 32 * t + 4 * g4 + tr_m, k1 = k0 + 16;
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
+      for (int d = 0; d < DBW; ++d) {
+        const int db = wave * DBW + d;
         const int ch = 2 * db + (tr_q >> 1), byte = (tr_q & 1) * 8;
-        const s16x4 lo = lds_read_tr16(&vs[k0 * Cfg::ROWB + vswz(k0, ch) * 16 + byte]);
-        const s16x4 hi = lds_read_tr16(&vs[k1 * Cfg::ROWB + vswz(k1, ch) * 16 + byte]);
-        u32x4 vb;
-        vb[0] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1));
-        vb[1] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3));
-        vb[2] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1));
-        vb[3] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3));
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, vb);
-        o[db] = mfma16(pf, vf, o[db]);   // high parts first,
-        o[db] = mfma16(pfl, vf, o[db]);  // then the low parts, in this fixed order
+        const s16x4 lo = lds_read_tr16(&vb[k0 * (kD * 2) + vswz(k0, ch) * 16 + byte]);
+        const s16x4 hi = lds_read_tr16(&vb[k1 * (kD * 2) + vswz(k1, ch) * 16 + byte]);
+        u32x4 vv;
+        vv[0] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1));
+        vv[1] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3));
+        vv[2] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1));
+        vv[3] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3));
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, vv);
+        o[d] = mfma16(pf, vf, o[d]);
+        o[d] = mfma16(pfl, vf, o[d]);
       }
     }
     if constexpr (MORE) {
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // V reads done before the next chunk's rows land
-      load_v(c + 1);
-      wait_vm<Cfg::VDMA>();  // chunk c + 1's K fragments, issued before its V rows
+      store_v((int)((c + 1) & 1));  // that buffer's last readers finished before this chunk's first barrier
       scores();
     }
   };
   for (int64_t c = c0; c + 1 < c1; ++c) chunk(c, std::true_type{});
   if (c0 < c1) chunk(c1 - 1, std::false_type{});
 
-  // ---- split state: o (rows = heads 4 g4 + r, col d = 16 db + c16), m, l (head c16)
   float* ws = a.ws;
   const int64_t hbase = row * a.Hq + (int64_t)kvh * grp;
 #pragma unroll
@@ -321,10 +323,10 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a, float scal
     if (h < grp) {
       float* st = ws + ((hbase + h) * S + j) * (kD + 2);
 #pragma unroll
-      for (int db = 0; db < 8; ++db) st[db * 16 + c16] = o[db][r];
+      for (int d = 0; d < DBW; ++d) st[(wave * DBW + d) * 16 + c16] = o[d][r];
     }
   }
-  if (g4 == 0 && c16 < grp) {
+  if (wave == 0 && g4 == 0 && c16 < grp) {
     float* st = ws + ((hbase + c16) * S + j) * (kD + 2);
     st[kD] = m_run;
     st[kD + 1] = l_run;
@@ -393,11 +395,11 @@ hipError_t launch_attn_splits(const AttnLaunch& a, hipStream_t s) {
   const float scale = 1.0f / __builtin_sqrtf((float)a.D);
   const int64_t wgs = a.Tq * a.Hkv * (int64_t)(a.split_hi - a.split_lo);
   if (wgs <= 0) return hipSuccess;
-  dim3 grid((unsigned)wgs), block(64);
+  dim3 grid((unsigned)wgs);
   switch (a.kv_chunk) {
-    case 32: hipLaunchKernelGGL(attn_split_kernel<32>, grid, block, 0, s, a, scale); break;
-    case 64: hipLaunchKernelGGL(attn_split_kernel<64>, grid, block, 0, s, a, scale); break;
-    case 128: hipLaunchKernelGGL(attn_split_kernel<128>, grid, block, 0, s, a, scale); break;
+    case 32: hipLaunchKernelGGL(attn_split_kernel<32>, grid, dim3(AttnCfg<32>::NW * 64), 0, s, a, scale); break;
+    case 64: hipLaunchKernelGGL(attn_split_kernel<64>, grid, dim3(AttnCfg<64>::NW * 64), 0, s, a, scale); break;
+    case 128: hipLaunchKernelGGL(attn_split_kernel<128>, grid, dim3(AttnCfg<128>::NW * 64), 0, s, a, scale); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
