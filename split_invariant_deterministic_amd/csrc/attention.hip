@@ -66,17 +66,19 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
 #endif
 }
 
-// Work split inside the workgroup: wave w computes the scores and
-// probabilities of the chunk's 16-key blocks [w KBW, (w+1) KBW) and the P.V
-// products of the output's 16-wide d blocks [w DBW, (w+1) DBW). Block maxima
-// and the packed probabilities pass through LDS, two barriers per chunk. The
-// order of every reduction is that of the schedule above, whichever wave
-// holds the operands: the chunk max is a max over the same set (exact, and a
-// zero max is made +0), wave 0 rebuilds each lane's probability sum from the
-// packed parts in (block, row) order, and each output d block sees the
-// schedule's MFMA chain. Several waves per item keep the chip busy at decode
-// batches of a few rows, where one wave per item left most CUs idle and each
-// wave bound by its own issue rate.
+// Work split inside the workgroup of NW = 2 NWS waves. The NWS score waves
+// load K, compute the scores and probabilities of the chunk's 16-key blocks
+// [w KBW, (w+1) KBW); the NWS V waves load V and stage it in LDS, and the
+// first of them keeps the running sum l. All waves then multiply P by V for
+// the output's 16-wide d blocks [w DBW, (w+1) DBW). Block maxima and the
+// packed probabilities pass through LDS, two barriers per chunk. The order of
+// every reduction is that of the schedule above, whichever wave holds the
+// operands: the chunk max is a max over the same set (exact, and a zero max
+// is made +0), the sum is rebuilt from the packed parts in (block, row) order,
+// and each output d block sees the schedule's MFMA chain. Several waves per
+// item keep the chip busy at decode batches of a few rows (16 splits x 8 kv
+// heads are 128 items at one row), where a chunk's dependent steps, not the
+// bytes, set the time.
 //
 // K and V are read through buffer descriptors whose range ends at the chunk's
 // last visible key, so keys past L read as zero without a per-lane clamp and
@@ -87,23 +89,28 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
 // next chunk's loads stay in flight across the exchange reads.
 template <int CH>
 struct AttnCfg {
-  static constexpr int KB = CH / 16;         // 16-key blocks per chunk
-  static constexpr int NW = KB < 4 ? KB : 4;  // waves per (row, kv head, split)
-  static constexpr int KBW = KB / NW;         // 16-key blocks per wave
-  static constexpr int DBW = 8 / NW;          // 16-wide output d blocks per wave
-  static constexpr int PV = CH / 32;          // 32-key MFMA steps per chunk
-  static constexpr int VLD = CH / 4 / NW;     // 1 KB (4-key) V loads per wave per chunk
+  static constexpr int KB = CH / 16;           // 16-key blocks per chunk
+  static constexpr int NWS = KB < 4 ? KB : 4;  // score waves: K loads, scores, probabilities
+  static constexpr int KBW = KB / NWS;         // 16-key blocks per score wave
+  static constexpr int NW = 2 * NWS;           // waves per item: the score waves, then as many V waves
+  static constexpr int VLD = CH / 4 / NWS;     // 1 KB (4-key) V loads per V wave per chunk
+  static constexpr int DBW = 8 / NW;           // 16-wide output d blocks per wave
+  static constexpr int PV = CH / 32;           // 32-key MFMA steps per chunk
+  static constexpr int NLD = KBW * 4;          // 16-byte loads per lane per chunk, either role
+  static_assert(NLD == VLD, "score and V waves load the same number of registers");
 };
 
 template <int CH>
 __global__ __launch_bounds__(AttnCfg<CH>::NW * 64) void attn_split_kernel(AttnLaunch a, float scale) {
   using Cfg = AttnCfg<CH>;
-  constexpr int NW = Cfg::NW, KBW = Cfg::KBW, DBW = Cfg::DBW, VLD = Cfg::VLD;
+  constexpr int NWS = Cfg::NWS, KBW = Cfg::KBW, DBW = Cfg::DBW, VLD = Cfg::VLD, NLD = Cfg::NLD;
   __shared__ __attribute__((aligned(1024))) uint8_t vs[2][CH * kD * 2];
   __shared__ u32x4 pex[Cfg::KB][64];  // per block and lane: p_hi pairs, then p_lo pairs
-  __shared__ float mex[NW][16];       // per wave: its blocks' max per head
+  __shared__ __attribute__((aligned(16))) float mex[16][NWS][4];  // per head: max of each score wave's lane group
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
+  const bool sw = wave < NWS;             // a score wave (else a V wave)
+  const int sv = sw ? wave : wave - NWS;  // its index within its role
   const int g4 = lane >> 4, c16 = lane & 15;
   const int nsplit = a.split_hi - a.split_lo;
   int64_t idx = blockIdx.x;
@@ -152,7 +159,7 @@ __global__ __launch_bounds__(AttnCfg<CH>::NW * 64) void attn_split_kernel(AttnLa
   };
 
   bf16x8 qf[4];
-  {
+  if (sw) {
     const bool hv = c16 < grp;
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (row * a.Hq + (int64_t)kvh * grp + (hv ? c16 : 0)) * kD;
 #pragma unroll
@@ -167,37 +174,41 @@ __global__ __launch_bounds__(AttnCfg<CH>::NW * 64) void attn_split_kernel(AttnLa
   const uint32_t vvo = (uint32_t)g4 * rb + 16u * c16;  // V: key g4 of a 4-key group, 16-byte slot c16
   const int vlds = g4 * (kD * 2) + vswz(g4, c16) * 16;  // that slot's place in the stage
 
-  bf16x8 kf[KBW][4];
-  auto load_k = [&](int64_t cc) {
-    const buf_rsrc r = chunk_rsrc(Kh, cc);
+  // A score wave's K fragments or a V wave's V rows of one chunk: the same
+  // registers and the same number of loads in both roles.
+  u32x4 ld[NLD];
+  auto load_next = [&](int64_t cc) {
+    if (sw) {
+      const buf_rsrc r = chunk_rsrc(Kh, cc);
 #pragma unroll
-    for (int kb = 0; kb < KBW; ++kb) {
-      const uint32_t so = (uint32_t)((wave * KBW + kb) * 16) * rb;
+      for (int kb = 0; kb < KBW; ++kb) {
+        const uint32_t so = (uint32_t)((sv * KBW + kb) * 16) * rb;
 #pragma unroll
-      for (int ds = 0; ds < 4; ++ds) kf[kb][ds] = __builtin_bit_cast(bf16x8, buf_load16(r, kvo + 64u * ds, so));
+        for (int ds = 0; ds < 4; ++ds) ld[kb * 4 + ds] = buf_load16(r, kvo + 64u * ds, so);
+      }
+    } else {
+      const buf_rsrc r = chunk_rsrc(Vh, cc);
+#pragma unroll
+      for (int i = 0; i < VLD; ++i) {
+        const uint32_t so = (uint32_t)(4 * (sv * VLD + i)) * rb;
+        ld[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, vvo, so, kNT));
+      }
     }
-  };
-  u32x4 vr[VLD];
-  auto load_v = [&](int64_t cc) {
-    const buf_rsrc r = chunk_rsrc(Vh, cc);
-#pragma unroll
-    for (int i = 0; i < VLD; ++i) {
-      const uint32_t so = (uint32_t)(4 * (wave * VLD + i)) * rb;
-      vr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, vvo, so, kNT));
-    }
-  };
-  auto store_v = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < VLD; ++i) *reinterpret_cast<u32x4*>(&vs[buf][(wave * VLD + i) * 1024 + vlds]) = vr[i];
   };
   f32x4 st[KBW];
-  auto scores = [&]() {
+  // K fragments into scores; V rows into LDS buffer buf
+  auto stage_next = [&](int buf) {
+    if (sw) {
 #pragma unroll
-    for (int kb = 0; kb < KBW; ++kb) {
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int kb = 0; kb < KBW; ++kb) {
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ds = 0; ds < 4; ++ds) acc = mfma16(kf[kb][ds], qf[ds], acc);
-      st[kb] = acc;
+        for (int ds = 0; ds < 4; ++ds) acc = mfma16(__builtin_bit_cast(bf16x8, ld[kb * 4 + ds]), qf[ds], acc);
+        st[kb] = acc;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < VLD; ++i) *reinterpret_cast<u32x4*>(&vs[buf][(sv * VLD + i) * 1024 + vlds]) = ld[i];
     }
   };
 
@@ -207,60 +218,107 @@ __global__ __launch_bounds__(AttnCfg<CH>::NW * 64) void attn_split_kernel(AttnLa
   for (int db = 0; db < DBW; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (c0 < c1) {
-    load_v(c0);
-    load_k(c0);
-    store_v((int)(c0 & 1));
-    scores();
+    load_next(c0);
+    stage_next((int)(c0 & 1));
   }
-  // A chunk with a successor issues the successor's V and K loads first and
-  // stages them (V into the other LDS buffer, K into scores) at its end.
+  // A chunk with a successor issues the successor's loads first and stages
+  // them at its end (V into the other LDS buffer, whose last readers finished
+  // before this chunk's first barrier).
   auto chunk = [&](int64_t c, auto has_next) {
     constexpr bool MORE = decltype(has_next)::value;
-    if constexpr (MORE) {
-      load_v(c + 1);
-      load_k(c + 1);
-    }
-    float bmax = -INFINITY;
+    if constexpr (MORE) load_next(c + 1);
+    if (sw) {
+      float bmax = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < KBW; ++kb)
+      for (int kb = 0; kb < KBW; ++kb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float s = st[kb][r] * scale;
-        if constexpr (!MORE) {  // only a split's last chunk can hold keys past L
-          const int64_t pos = c * CH + (wave * KBW + kb) * 16 + 4 * g4 + r;
-          if (pos >= L) s = -INFINITY;
+        for (int r = 0; r < 4; ++r) {
+          float s = st[kb][r] * scale;
+          if constexpr (!MORE) {  // only a split's last chunk can hold keys past L
+            const int64_t pos = c * CH + (sv * KBW + kb) * 16 + 4 * g4 + r;
+            if (pos >= L) s = -INFINITY;
+          }
+          st[kb][r] = s;
+          bmax = fmaxf(bmax, s);
         }
-        st[kb][r] = s;
-        bmax = fmaxf(bmax, s);
-      }
-    bmax = fmaxf(bmax, shfl_xor(bmax, 16));
-    bmax = fmaxf(bmax, shfl_xor(bmax, 32));
-    if (g4 == 0) mex[wave][c16] = bmax;
+      mex[c16][sv][g4] = bmax;
+    }
     __syncthreads();
-    float cmax = mex[0][c16];
+    float cmax;
+    {
+      // the NWS x 4 partial maxima of head c16, read as float4s and reduced
+      // as a tree (a max over a set: the order does not change the value)
+      const f32x4* mp = reinterpret_cast<const f32x4*>(&mex[c16][0][0]);
+      float wm[NWS];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) cmax = fmaxf(cmax, mex[w][c16]);
+      for (int w = 0; w < NWS; ++w) {
+        const f32x4 q = mp[w];
+        wm[w] = fmaxf(fmaxf(q[0], q[1]), fmaxf(q[2], q[3]));
+      }
+#pragma unroll
+      for (int h = NWS / 2; h >= 1; h /= 2)
+#pragma unroll
+        for (int w = 0; w < h; ++w) wm[w] = fmaxf(wm[w], wm[w + h]);
+      cmax = wm[0];
+    }
     const float m_new = fmaxf(m_run, cmax) + 0.0f;  // + 0: a zero max is +0 whatever the order
     const float alpha = exp_shifted(m_run, m_new);
+    if (sw) {
 #pragma unroll
-    for (int kb = 0; kb < KBW; ++kb) {
-      float ph[4], plo[4];
+      for (int kb = 0; kb < KBW; ++kb) {
+        float ph[4], plo[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = exp_shifted(st[kb][r], m_new);
-        ph[r] = bf16_bits_to_f32(f32_to_bf16_bits(p));
-        plo[r] = bf16_bits_to_f32(f32_to_bf16_bits(p - ph[r]));
+        for (int r = 0; r < 4; ++r) {
+          const float p = exp_shifted(st[kb][r], m_new);
+          ph[r] = bf16_bits_to_f32(f32_to_bf16_bits(p));
+          plo[r] = bf16_bits_to_f32(f32_to_bf16_bits(p - ph[r]));  // p - ph is exact in fp32
+        }
+        pex[sv * KBW + kb][lane] = u32x4{pack_bf16x2(ph[0], ph[1]), pack_bf16x2(ph[2], ph[3]),
+                                         pack_bf16x2(plo[0], plo[1]), pack_bf16x2(plo[2], plo[3])};
       }
-      pex[wave * KBW + kb][lane] =
-          u32x4{pack_bf16x2(ph[0], ph[1]), pack_bf16x2(ph[2], ph[3]), pack_bf16x2(plo[0], plo[1]),
-                pack_bf16x2(plo[2], plo[3])};
     }
     m_run = m_new;
     __syncthreads();
     u32x4 px[Cfg::KB];
 #pragma unroll
     for (int kb = 0; kb < Cfg::KB; ++kb) px[kb] = pex[kb][lane];
-    if (wave == 0) {  // the running sum, in the schedule's (block, row) order
+    float al[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      al[r] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((4 * g4 + r) << 2, __builtin_bit_cast(int, alpha)));
+#pragma unroll
+    for (int db = 0; db < DBW; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[db][r] = o[db][r] * al[r];
+    const uint8_t* vb = vs[c & 1];
+#pragma unroll
+    for (int t = 0; t < Cfg::PV; ++t) {
+      // A operand: head c16, keys {32t + 4 g4 + e} (e < 4) and {32t + 16 + 4 g4 + e - 4}
+      const u32x4 pa = u32x4{px[2 * t][0], px[2 * t][1], px[2 * t + 1][0], px[2 * t + 1][1]};
+      const u32x4 pb = u32x4{px[2 * t][2], px[2 * t][3], px[2 * t + 1][2], px[2 * t + 1][3]};
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, pa);
+      const bf16x8 pfl = __builtin_bit_cast(bf16x8, pb);
+      // B operand: the same keys for d = 16 db + c16, by two transpose reads
+      const int k0 = 32 * t + 4 * g4 + tr_m, k1 = k0 + 16;
+#pragma unroll
+      for (int d = 0; d < DBW; ++d) {
+        const int db = wave * DBW + d;
+        const int ch = 2 * db + (tr_q >> 1), byte = (tr_q & 1) * 8;
+        const s16x4 lo = lds_read_tr16(&vb[k0 * (kD * 2) + vswz(k0, ch) * 16 + byte]);
+        const s16x4 hi = lds_read_tr16(&vb[k1 * (kD * 2) + vswz(k1, ch) * 16 + byte]);
+        u32x4 vv;
+        vv[0] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1));
+        vv[1] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3));
+        vv[2] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1));
+        vv[3] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3));
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, vv);
+        o[d] = mfma16(pf, vf, o[d]);   // high parts first,
+        o[d] = mfma16(pfl, vf, o[d]);  // then the low parts, in this fixed order
+      }
+    }
+    // the running sum, kept by the first V wave (off the score waves' path),
+    // in the schedule's (block, row) order
+    if (wave == NWS) {
       float psum = 0.0f;
 #pragma unroll
       for (int kb = 0; kb < Cfg::KB; ++kb)
@@ -275,46 +333,12 @@ __global__ __launch_bounds__(AttnCfg<CH>::NW * 64) void attn_split_kernel(AttnLa
       psum = psum + shfl_xor(psum, 32);
       l_run = l_run * alpha + psum;
     }
-    float al[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      al[r] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((4 * g4 + r) << 2, __builtin_bit_cast(int, alpha)));
-#pragma unroll
-    for (int db = 0; db < DBW; ++db)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) o[db][r] = o[db][r] * al[r];
-    const uint8_t* vb = vs[c & 1];
-#pragma unroll
-    for (int t = 0; t < Cfg::PV; ++t) {
-      const u32x4 pa = u32x4{px[2 * t][0], px[2 * t][1], px[2 * t + 1][0], px[2 * t + 1][1]};
-      const u32x4 pb = u32x4{px[2 * t][2], px[2 * t][3], px[2 * t + 1][2], px[2 * t + 1][3]};
-      const bf16x8 pf = __builtin_bit_cast(bf16x8, pa);
-      const bf16x8 pfl = __builtin_bit_cast(bf16x8, pb);
-      const int k0 = 32 * t + 4 * g4 + tr_m, k1 = k0 + 16;
-#pragma unroll
-      for (int d = 0; d < DBW; ++d) {
-        const int db = wave * DBW + d;
-        const int ch = 2 * db + (tr_q >> 1), byte = (tr_q & 1) * 8;
-        const s16x4 lo = lds_read_tr16(&vb[k0 * (kD * 2) + vswz(k0, ch) * 16 + byte]);
-        const s16x4 hi = lds_read_tr16(&vb[k1 * (kD * 2) + vswz(k1, ch) * 16 + byte]);
-        u32x4 vv;
-        vv[0] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1));
-        vv[1] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3));
-        vv[2] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1));
-        vv[3] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3));
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, vv);
-        o[d] = mfma16(pf, vf, o[d]);
-        o[d] = mfma16(pfl, vf, o[d]);
-      }
-    }
-    if constexpr (MORE) {
-      store_v((int)((c + 1) & 1));  // that buffer's last readers finished before this chunk's first barrier
-      scores();
-    }
+    if constexpr (MORE) stage_next((int)((c + 1) & 1));
   };
   for (int64_t c = c0; c + 1 < c1; ++c) chunk(c, std::true_type{});
   if (c0 < c1) chunk(c1 - 1, std::false_type{});
 
+  // ---- split state: o (rows = heads 4 g4 + r, col d = 16 db + c16), m, l (head c16)
   float* ws = a.ws;
   const int64_t hbase = row * a.Hq + (int64_t)kvh * grp;
 #pragma unroll
@@ -326,7 +350,7 @@ __global__ __launch_bounds__(AttnCfg<CH>::NW * 64) void attn_split_kernel(AttnLa
       for (int d = 0; d < DBW; ++d) st[(wave * DBW + d) * 16 + c16] = o[d][r];
     }
   }
-  if (wave == 0 && g4 == 0 && c16 < grp) {
+  if (wave == NWS && g4 == 0 && c16 < grp) {
     float* st = ws + ((hbase + c16) * S + j) * (kD + 2);
     st[kD] = m_run;
     st[kD + 1] = l_run;
