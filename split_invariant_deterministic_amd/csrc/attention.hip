@@ -105,8 +105,8 @@ __global__ __launch_bounds__(AttnCfg<CH>::NW * 64) void attn_split_kernel(AttnLa
   using Cfg = AttnCfg<CH>;
   constexpr int NWS = Cfg::NWS, KBW = Cfg::KBW, DBW = Cfg::DBW, VLD = Cfg::VLD, NLD = Cfg::NLD;
   __shared__ __attribute__((aligned(1024))) uint8_t vs[2][CH * kD * 2];
-  __shared__ u32x4 pex[Cfg::KB][64];  // per block and lane: p_hi pairs, then p_lo pairs
-  __shared__ __attribute__((aligned(16))) float mex[16][NWS][4];  // per head: max of each score wave's lane group
+  __shared__ u32x4 pex[2][Cfg::KB][64];  // per chunk parity, block and lane: p_hi pairs, then p_lo pairs
+  __shared__ __attribute__((aligned(16))) float mex[2][16][NWS][4];  // per parity and head: max of each score wave's lane group
 
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
   const bool sw = wave < NWS;             // a score wave (else a V wave)
@@ -196,20 +196,36 @@ __global__ __launch_bounds__(AttnCfg<CH>::NW * 64) void attn_split_kernel(AttnLa
     }
   };
   f32x4 st[KBW];
-  // K fragments into scores; V rows into LDS buffer buf
-  auto stage_next = [&](int buf) {
-    if (sw) {
+  auto scores = [&]() {  // score waves: the chunk in ld
 #pragma unroll
-      for (int kb = 0; kb < KBW; ++kb) {
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb < KBW; ++kb) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ds = 0; ds < 4; ++ds) acc = mfma16(__builtin_bit_cast(bf16x8, ld[kb * 4 + ds]), qf[ds], acc);
-        st[kb] = acc;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < VLD; ++i) *reinterpret_cast<u32x4*>(&vs[buf][(sv * VLD + i) * 1024 + vlds]) = ld[i];
+      for (int ds = 0; ds < 4; ++ds) acc = mfma16(__builtin_bit_cast(bf16x8, ld[kb * 4 + ds]), qf[ds], acc);
+      st[kb] = acc;
     }
+  };
+  auto store_v = [&](int buf) {  // V waves: the chunk in ld into LDS buffer buf
+#pragma unroll
+    for (int i = 0; i < VLD; ++i) *reinterpret_cast<u32x4*>(&vs[buf][(sv * VLD + i) * 1024 + vlds]) = ld[i];
+  };
+  // score waves: scaled (and, in a split's last chunk, masked) scores of
+  // chunk cc and their maxima per lane group
+  auto block_max = [&](int64_t cc, auto last) {
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < KBW; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float s = st[kb][r] * scale;
+        if constexpr (decltype(last)::value) {  // only a split's last chunk can hold keys past L
+          const int64_t pos = cc * CH + (sv * KBW + kb) * 16 + 4 * g4 + r;
+          if (pos >= L) s = -INFINITY;
+        }
+        st[kb][r] = s;
+        bmax = fmaxf(bmax, s);
+      }
+    mex[cc & 1][c16][sv][g4] = bmax;
   };
 
   float m_run = -INFINITY, l_run = 0.0f;
@@ -217,38 +233,14 @@ __global__ __launch_bounds__(AttnCfg<CH>::NW * 64) void attn_split_kernel(AttnLa
 #pragma unroll
   for (int db = 0; db < DBW; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (c0 < c1) {
-    load_next(c0);
-    stage_next((int)(c0 & 1));
-  }
-  // A chunk with a successor issues the successor's loads first and stages
-  // them at its end (V into the other LDS buffer, whose last readers finished
-  // before this chunk's first barrier).
-  auto chunk = [&](int64_t c, auto has_next) {
-    constexpr bool MORE = decltype(has_next)::value;
-    if constexpr (MORE) load_next(c + 1);
-    if (sw) {
-      float bmax = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < KBW; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float s = st[kb][r] * scale;
-          if constexpr (!MORE) {  // only a split's last chunk can hold keys past L
-            const int64_t pos = c * CH + (sv * KBW + kb) * 16 + 4 * g4 + r;
-            if (pos >= L) s = -INFINITY;
-          }
-          st[kb][r] = s;
-          bmax = fmaxf(bmax, s);
-        }
-      mex[c16][sv][g4] = bmax;
-    }
-    __syncthreads();
+  // all waves: chunk cc's running max and alpha; score waves: its packed
+  // probabilities into pex[cc & 1]. Returns alpha.
+  auto softmax = [&](int64_t cc) {
     float cmax;
     {
       // the NWS x 4 partial maxima of head c16, read as float4s and reduced
       // as a tree (a max over a set: the order does not change the value)
-      const f32x4* mp = reinterpret_cast<const f32x4*>(&mex[c16][0][0]);
+      const f32x4* mp = reinterpret_cast<const f32x4*>(&mex[cc & 1][c16][0][0]);
       float wm[NWS];
 #pragma unroll
       for (int w = 0; w < NWS; ++w) {
@@ -273,15 +265,19 @@ __global__ __launch_bounds__(AttnCfg<CH>::NW * 64) void attn_split_kernel(AttnLa
           ph[r] = bf16_bits_to_f32(f32_to_bf16_bits(p));
           plo[r] = bf16_bits_to_f32(f32_to_bf16_bits(p - ph[r]));  // p - ph is exact in fp32
         }
-        pex[sv * KBW + kb][lane] = u32x4{pack_bf16x2(ph[0], ph[1]), pack_bf16x2(ph[2], ph[3]),
-                                         pack_bf16x2(plo[0], plo[1]), pack_bf16x2(plo[2], plo[3])};
+        pex[cc & 1][sv * KBW + kb][lane] = u32x4{pack_bf16x2(ph[0], ph[1]), pack_bf16x2(ph[2], ph[3]),
+                                                 pack_bf16x2(plo[0], plo[1]), pack_bf16x2(plo[2], plo[3])};
       }
     }
     m_run = m_new;
-    __syncthreads();
+    return alpha;
+  };
+  // all waves: o = o * alpha + P.V over chunk cc for the wave's d blocks;
+  // the first V wave: l = l * alpha + (the chunk's probability sum)
+  auto pv = [&](int64_t cc, float alpha) {
     u32x4 px[Cfg::KB];
 #pragma unroll
-    for (int kb = 0; kb < Cfg::KB; ++kb) px[kb] = pex[kb][lane];
+    for (int kb = 0; kb < Cfg::KB; ++kb) px[kb] = pex[cc & 1][kb][lane];
     float al[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r)
@@ -290,7 +286,7 @@ __global__ __launch_bounds__(AttnCfg<CH>::NW * 64) void attn_split_kernel(AttnLa
     for (int db = 0; db < DBW; ++db)
 #pragma unroll
       for (int r = 0; r < 4; ++r) o[db][r] = o[db][r] * al[r];
-    const uint8_t* vb = vs[c & 1];
+    const uint8_t* vb = vs[cc & 1];
 #pragma unroll
     for (int t = 0; t < Cfg::PV; ++t) {
       // A operand: head c16, keys {32t + 4 g4 + e} (e < 4) and {32t + 16 + 4 g4 + e - 4}
@@ -316,9 +312,7 @@ __global__ __launch_bounds__(AttnCfg<CH>::NW * 64) void attn_split_kernel(AttnLa
         o[d] = mfma16(pfl, vf, o[d]);  // then the low parts, in this fixed order
       }
     }
-    // the running sum, kept by the first V wave (off the score waves' path),
-    // in the schedule's (block, row) order
-    if (wave == NWS) {
+    if (wave == NWS) {  // the running sum, in the schedule's (block, row) order
       float psum = 0.0f;
 #pragma unroll
       for (int kb = 0; kb < Cfg::KB; ++kb)
@@ -333,10 +327,56 @@ __global__ __launch_bounds__(AttnCfg<CH>::NW * 64) void attn_split_kernel(AttnLa
       psum = psum + shfl_xor(psum, 32);
       l_run = l_run * alpha + psum;
     }
-    if constexpr (MORE) stage_next((int)((c + 1) & 1));
   };
-  for (int64_t c = c0; c + 1 < c1; ++c) chunk(c, std::true_type{});
-  if (c0 < c1) chunk(c1 - 1, std::false_type{});
+
+  // Software pipeline, one barrier per chunk. Iteration c: the score waves
+  // turn chunk c + 1's K into scores and block maxima, then (after the
+  // barrier) every wave takes chunk c + 1's max and alpha, the score waves
+  // its probabilities, the V waves stage its V, and all waves multiply chunk
+  // c's P by its V. The exchange buffers and the V stage alternate by chunk
+  // parity; a buffer is rewritten only after the barrier that follows its
+  // last reads. Each wave issues the loads of chunk c + 2 as soon as its
+  // registers hold nothing of chunk c + 1.
+  using T = std::true_type;
+  using F = std::false_type;
+  float alpha_c = 0.0f;  // alpha of the chunk whose P.V comes next
+  if (c0 < c1) {
+    load_next(c0);
+    if (sw) scores();
+    else store_v((int)(c0 & 1));
+    if (c0 + 1 < c1) load_next(c0 + 1);
+    if (sw) {
+      if (c0 + 1 < c1) block_max(c0, F{});
+      else block_max(c0, T{});
+    }
+    __syncthreads();
+    alpha_c = softmax(c0);
+  }
+  auto step = [&](int64_t c, auto has1, auto has2) {
+    constexpr bool H1 = decltype(has1)::value, H2 = decltype(has2)::value;
+    if constexpr (H1) {
+      if (sw) {
+        scores();  // chunk c + 1
+        if constexpr (H2) load_next(c + 2);
+        block_max(c + 1, std::integral_constant<bool, !H2>{});
+      }
+    }
+    __syncthreads();
+    if constexpr (H1) {
+      if (!sw) {
+        store_v((int)((c + 1) & 1));
+        if constexpr (H2) load_next(c + 2);
+      }
+      const float a_next = softmax(c + 1);
+      pv(c, alpha_c);
+      alpha_c = a_next;
+    } else {
+      pv(c, alpha_c);
+    }
+  };
+  for (int64_t c = c0; c + 2 < c1; ++c) step(c, T{}, T{});
+  if (c0 + 1 < c1) step(c1 - 2, T{}, F{});
+  if (c0 < c1) step(c1 - 1, F{}, F{});
 
   // ---- split state: o (rows = heads 4 g4 + r, col d = 16 db + c16), m, l (head c16)
   float* ws = a.ws;
