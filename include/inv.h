@@ -339,7 +339,9 @@ inv_status inv_logprob_combine(const inv_contract* c, const float* stats, const 
  * s occupying rows [cu_seqlens[s], cu_seqlens[s+1]); query row i belongs to
  * sequence q_seq[i] and sees keys at positions [0, q_pos[i]] of it.
  * out [Tq, Hq, D] bf16. Query head h reads kv head h / (Hq/Hkv).
- * D == 128; Hq % Hkv == 0; Hq/Hkv <= 16.
+ * D == 128; Hq % Hkv == 0; Hq/Hkv <= 16; kv_chunk keys of all kv heads
+ * (kv_chunk * Hkv * D * 2 bytes) < 2 GiB, else INV_E_UNSUPPORTED; q, k, v
+ * 16-byte aligned, else INV_E_ARG.
  * For a row with L = q_pos+1 visible keys: keys form chunks of kv_chunk from
  * position 0, n = ceil(L/kv_chunk); split j (of S = split_kv) owns chunks
  * [floor(j*n/S), floor((j+1)*n/S)), processed in ascending order with an
