@@ -280,10 +280,12 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
   const int nv = (int)min((int64_t)4, H - h);
   float v[KK][4];
   bool bad = false;
-  if (H % 4 == 0 && (reinterpret_cast<uintptr_t>(Y) & 15) == 0) {
+  const bool vec = H % 4 == 0 && (reinterpret_cast<uintptr_t>(Y) & 15) == 0;
+  if (vec) {
     // rows 16-byte aligned and h < H a multiple of 4: one float4 per expert
     // row, all KK loads in flight (a row past the table reads row 0 and the
-    // token becomes NaN below)
+    // token becomes NaN below); the rows are read once, so the loads stream
+    // past the caches
     f32x4 y[KK];
     float wj[KK];
 #pragma unroll
@@ -292,7 +294,7 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
       wj[j] = w[t * KK + j];
       const bool ok = s >= 0 && s < y_rows;
       bad |= !ok;
-      y[j] = *reinterpret_cast<const f32x4*>(Y + (ok ? (int64_t)s : 0) * H + h);
+      y[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Y + (ok ? (int64_t)s : 0) * H + h));
     }
 #pragma unroll
     for (int j = 0; j < KK; ++j)
@@ -310,6 +312,7 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
       for (int q = 0; q < 4; ++q) v[j][q] = (q < nv && ok) ? wj * yr[q] : 0.0f;
     }
   }
+  float r[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     float s;
@@ -324,8 +327,15 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
         for (int j = 0; j < n / 2; ++j) v[j][q] = v[2 * j][q] + v[2 * j + 1][q];
       s = v[0][q];
     }
-    if (bad) s = __builtin_nanf("");
-    if (q < nv) out[t * H + h + q] = f32_to_bf16_bits(s);
+    r[q] = bad ? __builtin_nanf("") : s;
+  }
+  if (vec && (reinterpret_cast<uintptr_t>(out) & 7) == 0) {  // the four bf16 as one 8-byte store
+    typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+    *reinterpret_cast<u32x2*>(out + t * H + h) = u32x2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (q < nv) out[t * H + h + q] = f32_to_bf16_bits(r[q]);
   }
 }
 
