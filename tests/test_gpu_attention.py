@@ -50,6 +50,30 @@ def test_edge_lengths_against_oracle(inv, kv_chunk, split_kv):
     check_bf16(out, _oracle(d), f"edge lengths chunk {kv_chunk} splits {split_kv}")
 
 
+@pytest.mark.parametrize("Hq,Hkv,kv_chunk,split_kv", [(2, 2, 64, 16), (8, 1, 64, 4), (16, 8, 32, 16),
+                                                      (32, 4, 128, 8), (64, 4, 64, 16), (256, 16, 64, 2)])
+def test_head_groups_against_oracle(inv, Hq, Hkv, kv_chunk, split_kv):
+    # GQA groups of 1 to 16 query heads per kv head (the columns of the score MFMA), 1 to 16 kv
+    # heads (the key stride the per-chunk buffer ranges use), every chunk size
+    lengths = [1, 17, 64, 65, 300, 1025]
+    d = synth.attn(torch.tensor(lengths), Hq=Hq, Hkv=Hkv, seed=7)
+    out = _run(inv, _dev(d), inv.contract(split_kv=split_kv, kv_chunk=kv_chunk))
+    check_bf16(out, _oracle(d, Hkv), f"Hq {Hq} Hkv {Hkv} chunk {kv_chunk} splits {split_kv}")
+
+
+def test_full_group_rows_equal_batch(inv):
+    # 16 query heads per kv head fill all 16 columns: single rows against the batch, bitwise
+    d = _dev(synth.attn(torch.tensor([700, 33, 2049, 64]), Hq=128, Hkv=8, seed=8))
+    c = inv.contract()
+    full = _run(inv, d, c)
+    for i in range(4):
+        one = dict(d)
+        one["q"] = d["q"][i:i + 1].contiguous()
+        one["q_seq"] = d["q_seq"][i:i + 1].contiguous()
+        one["q_pos"] = d["q_pos"][i:i + 1].contiguous()
+        assert bitwise_equal(_run(inv, one, c), full[i:i + 1]), i
+
+
 def test_long_context_against_oracle(inv):
     d = synth.attn(torch.tensor([32768, 5000, 2049]), seed=2)
     out = _run(inv, _dev(d), inv.contract())
