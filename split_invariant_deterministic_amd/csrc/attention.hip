@@ -71,7 +71,8 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
 // [w KBW, (w+1) KBW); the NWS V waves load V and stage it in LDS, and the
 // first of them keeps the running sum l. All waves then multiply P by V for
 // the output's 16-wide d blocks [w DBW, (w+1) DBW). Block maxima and the
-// packed probabilities pass through LDS, two barriers per chunk. The order of
+// packed probabilities pass through LDS; the chunk loop below is software-
+// pipelined to one barrier per chunk. The order of
 // every reduction is that of the schedule above, whichever wave holds the
 // operands: the chunk max is a max over the same set (exact, and a zero max
 // is made +0), the sum is rebuilt from the packed parts in (block, row) order,
