@@ -66,6 +66,22 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
 #endif
 }
 
+// v + v[lane ^ 16], then that + its value at lane ^ 32: the same two sums as
+// two xor shuffles, by the gfx950 row and half swaps (VALU, no LDS round
+// trip). Swapping two copies of v leaves each lane holding its own value and
+// its partner's, in one order or the other; fp32 addition is commutative, so
+// the bits equal the shuffle form. Inline asm with the swap's two wait
+// states, because the compiler's builtin for it folds two copies of one value.
+__device__ __forceinline__ float xor_sum_16_32(float v) {
+  float a = v, b = v;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  v = a + b;
+  a = v;
+  b = v;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return a + b;
+}
+
 // Work split inside the workgroup of NW = 2 NWS waves. The NWS score waves
 // load K, compute the scores and probabilities of the chunk's 16-key blocks
 // [w KBW, (w+1) KBW); the NWS V waves load V and stage it in LDS, and the
@@ -324,8 +340,7 @@ __global__ __launch_bounds__(AttnCfg<CH>::NW * 64) void attn_split_kernel(AttnLa
           const float pl = (r & 1) ? bf16_hi(wl) : bf16_lo(wl);
           psum = psum + (ph + pl);
         }
-      psum = psum + shfl_xor(psum, 16);
-      psum = psum + shfl_xor(psum, 32);
+      psum = xor_sum_16_32(psum);
       l_run = l_run * alpha + psum;
     }
   };
