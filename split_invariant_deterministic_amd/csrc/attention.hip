@@ -84,8 +84,8 @@ __device__ __forceinline__ float xor_sum_16_32(float v) {
 
 // Work split inside the workgroup of NW = 2 NWS waves. The NWS score waves
 // load K, compute the scores and probabilities of the chunk's 16-key blocks
-// [w KBW, (w+1) KBW); the NWS V waves load V and stage it in LDS, and the
-// first of them keeps the running sum l. All waves then multiply P by V for
+// [w KBW, (w+1) KBW), and the first of them also keeps the running sum l; the
+// NWS V waves load V and stage it in LDS. All waves then multiply P by V for
 // the output's 16-wide d blocks [w DBW, (w+1) DBW). Block maxima and the
 // packed probabilities pass through LDS; the chunk loop below is software-
 // pipelined to one barrier per chunk. The order of
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(AttnCfg<CH>::NW * 64) void attn_split_kernel(AttnLa
     return alpha;
   };
   // all waves: o = o * alpha + P.V over chunk cc for the wave's d blocks;
-  // the first V wave: l = l * alpha + (the chunk's probability sum)
+  // wave 0: l = l * alpha + (the chunk's probability sum)
   auto pv = [&](int64_t cc, float alpha) {
     u32x4 px[Cfg::KB];
 #pragma unroll
@@ -329,7 +329,7 @@ __global__ __launch_bounds__(AttnCfg<CH>::NW * 64) void attn_split_kernel(AttnLa
         o[d] = mfma16(pfl, vf, o[d]);  // then the low parts, in this fixed order
       }
     }
-    if (wave == NWS) {  // the running sum, in the schedule's (block, row) order
+    if (wave == 0) {  // the running sum, in the schedule's (block, row) order
       float psum = 0.0f;
 #pragma unroll
       for (int kb = 0; kb < Cfg::KB; ++kb)
@@ -406,7 +406,7 @@ __global__ __launch_bounds__(AttnCfg<CH>::NW * 64) void attn_split_kernel(AttnLa
       for (int d = 0; d < DBW; ++d) st[(wave * DBW + d) * 16 + c16] = o[d][r];
     }
   }
-  if (wave == NWS && g4 == 0 && c16 < grp) {
+  if (wave == 0 && g4 == 0 && c16 < grp) {
     float* st = ws + ((hbase + c16) * S + j) * (kD + 2);
     st[kD] = m_run;
     st[kD + 1] = l_run;
