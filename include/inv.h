@@ -340,7 +340,8 @@ inv_status inv_logprob_combine(const inv_contract* c, const float* stats, const 
  * sequence q_seq[i] and sees keys at positions [0, q_pos[i]] of it.
  * out [Tq, Hq, D] bf16. Query head h reads kv head h / (Hq/Hkv).
  * D == 128; Hq % Hkv == 0; Hq/Hkv <= 16; kv_chunk keys of all kv heads
- * (kv_chunk * Hkv * D * 2 bytes) < 2 GiB, else INV_E_UNSUPPORTED; q, k, v
+ * (kv_chunk * Hkv * D * 2 bytes) < 2 GiB; Tq * Hkv * split_kv < 2^23 (one
+ * workgroup per row, kv head and split); else INV_E_UNSUPPORTED. q, k, v
  * 16-byte aligned, else INV_E_ARG.
  * For a row with L = q_pos+1 visible keys: keys form chunks of kv_chunk from
  * position 0, n = ceil(L/kv_chunk); split j (of S = split_kv) owns chunks

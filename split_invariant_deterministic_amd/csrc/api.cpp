@@ -520,6 +520,9 @@ static inv_status attn_check(const inv_contract* c, const void* q, const void* k
   if (Hq % Hkv != 0 || Hq / Hkv > 16) return INV_E_UNSUPPORTED;
   // a chunk's keys of all kv heads are addressed with 32-bit offsets
   if ((int64_t)Hkv * D * 2 * c->kv_chunk >= ((int64_t)1 << 31)) return INV_E_UNSUPPORTED;
+  // one workgroup of up to 512 threads per (row, kv head, split): the grid's
+  // threads must fit 32 bits, and the kernel indexes items in 32 bits
+  if (Tq > (((int64_t)1 << 23) - 1) / ((int64_t)Hkv * c->split_kv)) return INV_E_UNSUPPORTED;
   if (Tq > 0 && (!q || !k || !v || !cu || !q_seq || !q_pos || num_seqs == 0)) return INV_E_ARG;
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v)) & 15u)
     return INV_E_ARG;

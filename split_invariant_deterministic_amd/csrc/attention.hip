@@ -16,8 +16,9 @@
 //     p     = exp2((s - m') * log2e), masked keys give 0, split into two
 //             bf16 parts p_hi = bf16(p), p_lo = bf16(p - p_hi) so that the
 //             P.V MFMAs see p to about 16 bits instead of bf16's 8
-//     l'    = l * alpha + sum_chunk (p_hi + p_lo)  (lane sums in (block,
-//                                        row) order, then xor 16, 32)
+//     l'    = l * alpha + sum_chunk (p_hi + p_lo)  (per lane: a balanced
+//             pairwise tree over a 16-key block's 4 keys, then over the
+//             chunk's blocks in ascending order, then xor 16, xor 32)
 //     o'    = MFMA chain of P.V over the chunk's 32-key steps, started from
 //             o * alpha; per step the p_hi MFMA, then the p_lo MFMA
 //   empty splits are (m, l, o) = (-inf, 0, 0).
@@ -84,15 +85,16 @@ __device__ __forceinline__ float xor_sum_16_32(float v) {
 
 // Work split inside the workgroup of NW = 2 NWS waves. The NWS score waves
 // load K, compute the scores and probabilities of the chunk's 16-key blocks
-// [w KBW, (w+1) KBW), and the first of them also keeps the running sum l; the
-// NWS V waves load V and stage it in LDS. All waves then multiply P by V for
-// the output's 16-wide d blocks [w DBW, (w+1) DBW). Block maxima and the
-// packed probabilities pass through LDS; the chunk loop below is software-
-// pipelined to one barrier per chunk. The order of
-// every reduction is that of the schedule above, whichever wave holds the
-// operands: the chunk max is a max over the same set (exact, and a zero max
-// is made +0), the sum is rebuilt from the packed parts in (block, row) order,
-// and each output d block sees the schedule's MFMA chain. Several waves per
+// [w KBW, (w+1) KBW) and their part of the probability sum; the first of them
+// also keeps the running sum l. The NWS V waves load V and stage it in LDS.
+// All waves then multiply P by V for the output's 16-wide d blocks
+// [w DBW, (w+1) DBW). Block maxima, the packed probabilities and the sum's
+// parts pass through LDS; the chunk loop below is software-pipelined to one
+// barrier per chunk. The order of every reduction is that of the schedule
+// above, whichever wave holds the operands: the chunk max is a max over the
+// same set (exact, and a zero max is made +0), the sum's tree does not depend
+// on which wave adds which node, and each output d block sees the schedule's
+// MFMA chain. Several waves per
 // item keep the chip busy at decode batches of a few rows (16 splits x 8 kv
 // heads are 128 items at one row), where a chunk's dependent steps, not the
 // bytes, set the time.
@@ -124,6 +126,7 @@ __global__ __launch_bounds__(AttnCfg<CH>::NW * 64) void attn_split_kernel(AttnLa
   __shared__ __attribute__((aligned(1024))) uint8_t vs[2][CH * kD * 2];
   __shared__ u32x4 pex[2][Cfg::KB][64];  // per chunk parity, block and lane: p_hi pairs, then p_lo pairs
   __shared__ __attribute__((aligned(16))) float mex[2][16][NWS][4];  // per parity and head: max of each score wave's lane group
+  __shared__ float psx[2][NWS][64];  // per parity, score wave and lane: that wave's part of the probability sum
 
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
   const bool sw = wave < NWS;             // a score wave (else a V wave)
@@ -273,18 +276,26 @@ __global__ __launch_bounds__(AttnCfg<CH>::NW * 64) void attn_split_kernel(AttnLa
     const float m_new = fmaxf(m_run, cmax) + 0.0f;  // + 0: a zero max is +0 whatever the order
     const float alpha = exp_shifted(m_run, m_new);
     if (sw) {
+      float bs[KBW];  // per block: the lane's 4 keys' p_hi + p_lo, summed as a balanced tree
 #pragma unroll
       for (int kb = 0; kb < KBW; ++kb) {
-        float ph[4], plo[4];
+        float ph[4], plo[4], x[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float p = exp_shifted(st[kb][r], m_new);
           ph[r] = bf16_bits_to_f32(f32_to_bf16_bits(p));
           plo[r] = bf16_bits_to_f32(f32_to_bf16_bits(p - ph[r]));  // p - ph is exact in fp32
+          x[r] = ph[r] + plo[r];
         }
         pex[cc & 1][sv * KBW + kb][lane] = u32x4{pack_bf16x2(ph[0], ph[1]), pack_bf16x2(ph[2], ph[3]),
                                                  pack_bf16x2(plo[0], plo[1]), pack_bf16x2(plo[2], plo[3])};
+        bs[kb] = (x[0] + x[1]) + (x[2] + x[3]);
       }
+#pragma unroll
+      for (int h = 1; h < KBW; h *= 2)  // the wave's adjacent blocks, pairwise
+#pragma unroll
+        for (int b = 0; b + h < KBW; b += 2 * h) bs[b] = bs[b] + bs[b + h];
+      psx[cc & 1][sv][lane] = bs[0];
     }
     m_run = m_new;
     return alpha;
@@ -295,6 +306,11 @@ __global__ __launch_bounds__(AttnCfg<CH>::NW * 64) void attn_split_kernel(AttnLa
     u32x4 px[Cfg::KB];
 #pragma unroll
     for (int kb = 0; kb < Cfg::KB; ++kb) px[kb] = pex[cc & 1][kb][lane];
+    float wsum[NWS];
+    if (wave == 0) {
+#pragma unroll
+      for (int w = 0; w < NWS; ++w) wsum[w] = psx[cc & 1][w][lane];
+    }
     float al[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r)
@@ -329,18 +345,12 @@ __global__ __launch_bounds__(AttnCfg<CH>::NW * 64) void attn_split_kernel(AttnLa
         o[d] = mfma16(pfl, vf, o[d]);  // then the low parts, in this fixed order
       }
     }
-    if (wave == 0) {  // the running sum, in the schedule's (block, row) order
-      float psum = 0.0f;
+    if (wave == 0) {  // the running sum: the score waves' parts, pairwise, then across lane groups
 #pragma unroll
-      for (int kb = 0; kb < Cfg::KB; ++kb)
+      for (int h = 1; h < NWS; h *= 2)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const uint32_t wh = px[kb][r >> 1], wl = px[kb][2 + (r >> 1)];
-          const float ph = (r & 1) ? bf16_hi(wh) : bf16_lo(wh);
-          const float pl = (r & 1) ? bf16_hi(wl) : bf16_lo(wl);
-          psum = psum + (ph + pl);
-        }
-      psum = xor_sum_16_32(psum);
+        for (int w = 0; w + h < NWS; w += 2 * h) wsum[w] = wsum[w] + wsum[w + h];
+      const float psum = xor_sum_16_32(wsum[0]);
       l_run = l_run * alpha + psum;
     }
   };

@@ -150,6 +150,11 @@ def test_entry_points_reject_before_any_launch():
     # a chunk of keys over all kv heads is addressed with 32-bit offsets: 128 x 65536 x 128 x 2 B = 2 GiB
     assert lib.inv_decode_attn(by(inv.contract(kv_chunk=128)), fake, fake, fake, fake, 1, fake, fake, fake, 1,
                                65536, 65536, 128, fake, 1 << 30, null) == inv.E_UNSUPPORTED
+    # one workgroup per (row, kv head, split): Tq x Hkv x split_kv < 2^23 (here 65536 x 8 x 16 = 2^23)
+    assert lib.inv_decode_attn(by(ca), fake, fake, fake, fake, 1, fake, fake, fake, 65536, 32, 8, 128, fake,
+                               1 << 40, null) == inv.E_UNSUPPORTED
+    assert lib.inv_attn_splits(by(ca), fake, fake, fake, fake, 1, fake, fake, 65536, 32, 8, 128, 0, 1, fake,
+                               1 << 40, null) == inv.E_UNSUPPORTED
     cm = inv.contract(leaves=8)
     assert lib.inv_moe_route(by(cm), fake, fake, fake, 4, 300, null) == inv.E_UNSUPPORTED
     assert lib.inv_moe_route(by(cm), fake, fake, fake, 4, 4, null) == inv.E_UNSUPPORTED      # k > E
