@@ -31,10 +31,11 @@
 // depend only on its q, its visible keys and L: a decode row equals the same
 // position's row in a multi-row (prefill) launch, and a batch of one row
 // equals its row in a batch of 256. Scores are produced transposed (keys x
-// heads): each lane then holds the probabilities of one head that the P.V
-// MFMA takes as its A operand. The P.V B operand is read back from an LDS
+// heads): each lane then holds the probabilities of one head, which the P.V
+// MFMA takes as its B operand; its A operand is V^T, read back from an LDS
 // stage of V with the gfx950 transpose read, holding the same keys in the
-// same slots.
+// same slots. The output is thus O^T (d x heads), so a lane rescales its
+// column by its own head's alpha.
 #include <type_traits>
 
 #include "common.h"
@@ -311,23 +312,20 @@ __global__ __launch_bounds__(AttnCfg<CH>::NW * 64) void attn_split_kernel(AttnLa
 #pragma unroll
       for (int w = 0; w < NWS; ++w) wsum[w] = psx[cc & 1][w][lane];
     }
-    float al[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      al[r] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((4 * g4 + r) << 2, __builtin_bit_cast(int, alpha)));
+    // o is held transposed (d x heads): a lane's column is its own head c16
 #pragma unroll
     for (int db = 0; db < DBW; ++db)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[db][r] = o[db][r] * al[r];
+      for (int r = 0; r < 4; ++r) o[db][r] = o[db][r] * alpha;
     const uint8_t* vb = vs[cc & 1];
 #pragma unroll
     for (int t = 0; t < Cfg::PV; ++t) {
-      // A operand: head c16, keys {32t + 4 g4 + e} (e < 4) and {32t + 16 + 4 g4 + e - 4}
+      // B operand (P^T): head c16, keys {32t + 4 g4 + e} (e < 4) and {32t + 16 + 4 g4 + e - 4}
       const u32x4 pa = u32x4{px[2 * t][0], px[2 * t][1], px[2 * t + 1][0], px[2 * t + 1][1]};
       const u32x4 pb = u32x4{px[2 * t][2], px[2 * t][3], px[2 * t + 1][2], px[2 * t + 1][3]};
       const bf16x8 pf = __builtin_bit_cast(bf16x8, pa);
       const bf16x8 pfl = __builtin_bit_cast(bf16x8, pb);
-      // B operand: the same keys for d = 16 db + c16, by two transpose reads
+      // A operand (V^T): the same keys for d = 16 db + c16, by two transpose reads
       const int k0 = 32 * t + 4 * g4 + tr_m, k1 = k0 + 16;
 #pragma unroll
       for (int d = 0; d < DBW; ++d) {
@@ -341,8 +339,8 @@ __global__ __launch_bounds__(AttnCfg<CH>::NW * 64) void attn_split_kernel(AttnLa
         vv[2] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1));
         vv[3] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3));
         const bf16x8 vf = __builtin_bit_cast(bf16x8, vv);
-        o[d] = mfma16(pf, vf, o[d]);   // high parts first,
-        o[d] = mfma16(pfl, vf, o[d]);  // then the low parts, in this fixed order
+        o[d] = mfma16(vf, pf, o[d]);   // high parts first,
+        o[d] = mfma16(vf, pfl, o[d]);  // then the low parts, in this fixed order
       }
     }
     if (wave == 0) {  // the running sum: the score waves' parts, pairwise, then across lane groups
@@ -404,22 +402,18 @@ __global__ __launch_bounds__(AttnCfg<CH>::NW * 64) void attn_split_kernel(AttnLa
   if (c0 + 1 < c1) step(c1 - 2, T{}, F{});
   if (c0 < c1) step(c1 - 1, F{}, F{});
 
-  // ---- split state: o (rows = heads 4 g4 + r, col d = 16 db + c16), m, l (head c16)
-  float* ws = a.ws;
+  // ---- split state of head c16: o (d = 16 db + 4 g4 + r), m, l
   const int64_t hbase = row * a.Hq + (int64_t)kvh * grp;
+  if (c16 < grp) {
+    float* st = a.ws + ((hbase + c16) * S + j) * (kD + 2);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int h = 4 * g4 + r;
-    if (h < grp) {
-      float* st = ws + ((hbase + h) * S + j) * (kD + 2);
+    for (int d = 0; d < DBW; ++d)
 #pragma unroll
-      for (int d = 0; d < DBW; ++d) st[(wave * DBW + d) * 16 + c16] = o[d][r];
+      for (int r = 0; r < 4; ++r) st[(wave * DBW + d) * 16 + 4 * g4 + r] = o[d][r];
+    if (wave == 0 && g4 == 0) {
+      st[kD] = m_run;
+      st[kD + 1] = l_run;
     }
-  }
-  if (wave == 0 && g4 == 0 && c16 < grp) {
-    float* st = ws + ((hbase + c16) * S + j) * (kD + 2);
-    st[kD] = m_run;
-    st[kD + 1] = l_run;
   }
 }
 
