@@ -84,6 +84,39 @@ __device__ __forceinline__ float xor_sum_16_32(float v) {
   return a + b;
 }
 
+// The maximum of a set of values, three at a time by the hardware's
+// three-input max. fmaxf would first quiet each operand loaded from LDS (a
+// signalling NaN is not a maximum); the values here are scores or maxima of
+// scores, so any NaN among them is already quiet. A max over a set does not
+// depend on the grouping.
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+template <int N>
+__device__ __forceinline__ float max_of(const float (&v)[N]) {
+  if constexpr (N == 1) {
+    return v[0];
+  } else {
+    constexpr int M = (N + 2) / 3;
+    float u[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i)
+      u[i] = vmax3(v[3 * i], v[3 * i + 1 < N ? 3 * i + 1 : 3 * i], v[3 * i + 2 < N ? 3 * i + 2 : 3 * i]);
+    return max_of<M>(u);
+  }
+}
+
+// Two floats rounded to bf16 (nearest even) as one packed word, element 0 in
+// the low half.
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{lo, hi}, bf16x2v));
+}
+
 // Work split inside the workgroup of NW = 2 NWS waves. The NWS score waves
 // load K, compute the scores and probabilities of the chunk's 16-key blocks
 // [w KBW, (w+1) KBW) and their part of the probability sum; the first of them
@@ -125,7 +158,9 @@ __global__ __launch_bounds__(AttnCfg<CH>::NW * 64) void attn_split_kernel(AttnLa
   using Cfg = AttnCfg<CH>;
   constexpr int NWS = Cfg::NWS, KBW = Cfg::KBW, DBW = Cfg::DBW, VLD = Cfg::VLD, NLD = Cfg::NLD;
   __shared__ __attribute__((aligned(1024))) uint8_t vs[2][CH * kD * 2];
-  __shared__ u32x4 pex[2][Cfg::KB][64];  // per chunk parity, block and lane: p_hi pairs, then p_lo pairs
+  // per chunk parity, 32-key MFMA step and lane: the P.V operand words, p_hi
+  // in pexh and p_lo in pexl (block 2t's two pairs, then block 2t+1's)
+  __shared__ u32x4 pexh[2][Cfg::PV][64], pexl[2][Cfg::PV][64];
   __shared__ __attribute__((aligned(16))) float mex[2][16][NWS][4];  // per parity and head: max of each score wave's lane group
   __shared__ float psx[2][NWS][64];  // per parity, score wave and lane: that wave's part of the probability sum
 
@@ -255,41 +290,39 @@ __global__ __launch_bounds__(AttnCfg<CH>::NW * 64) void attn_split_kernel(AttnLa
   for (int db = 0; db < DBW; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // all waves: chunk cc's running max and alpha; score waves: its packed
-  // probabilities into pex[cc & 1]. Returns alpha.
+  // probabilities into pexh / pexl[cc & 1]. Returns alpha.
   auto softmax = [&](int64_t cc) {
-    float cmax;
+    float mv[4 * NWS + 1];  // the NWS x 4 partial maxima of head c16 (read as float4s) and m
     {
-      // the NWS x 4 partial maxima of head c16, read as float4s and reduced
-      // as a tree (a max over a set: the order does not change the value)
       const f32x4* mp = reinterpret_cast<const f32x4*>(&mex[cc & 1][c16][0][0]);
-      float wm[NWS];
 #pragma unroll
       for (int w = 0; w < NWS; ++w) {
         const f32x4 q = mp[w];
-        wm[w] = fmaxf(fmaxf(q[0], q[1]), fmaxf(q[2], q[3]));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mv[4 * w + i] = q[i];
       }
-#pragma unroll
-      for (int h = NWS / 2; h >= 1; h /= 2)
-#pragma unroll
-        for (int w = 0; w < h; ++w) wm[w] = fmaxf(wm[w], wm[w + h]);
-      cmax = wm[0];
+      mv[4 * NWS] = m_run;
     }
-    const float m_new = fmaxf(m_run, cmax) + 0.0f;  // + 0: a zero max is +0 whatever the order
+    const float m_new = max_of(mv) + 0.0f;  // + 0: a zero max is +0 whatever the order
     const float alpha = exp_shifted(m_run, m_new);
     if (sw) {
       float bs[KBW];  // per block: the lane's 4 keys' p_hi + p_lo, summed as a balanced tree
 #pragma unroll
       for (int kb = 0; kb < KBW; ++kb) {
-        float ph[4], plo[4], x[4];
+        uint32_t hw[2], lw[2];  // p_hi and p_lo of keys (0, 1) and (2, 3), packed
+        float x[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = exp_shifted(st[kb][r], m_new);
-          ph[r] = bf16_bits_to_f32(f32_to_bf16_bits(p));
-          plo[r] = bf16_bits_to_f32(f32_to_bf16_bits(p - ph[r]));  // p - ph is exact in fp32
-          x[r] = ph[r] + plo[r];
+        for (int q = 0; q < 2; ++q) {
+          const float p0 = exp_shifted(st[kb][2 * q], m_new), p1 = exp_shifted(st[kb][2 * q + 1], m_new);
+          hw[q] = cvt_pk_bf16(p0, p1);
+          const float h0 = bf16_lo(hw[q]), h1 = bf16_hi(hw[q]);
+          lw[q] = cvt_pk_bf16(p0 - h0, p1 - h1);  // p - p_hi is exact in fp32
+          x[2 * q] = h0 + bf16_lo(lw[q]);
+          x[2 * q + 1] = h1 + bf16_hi(lw[q]);
         }
-        pex[cc & 1][sv * KBW + kb][lane] = u32x4{pack_bf16x2(ph[0], ph[1]), pack_bf16x2(ph[2], ph[3]),
-                                                 pack_bf16x2(plo[0], plo[1]), pack_bf16x2(plo[2], plo[3])};
+        const int blk = sv * KBW + kb;
+        reinterpret_cast<u32x2*>(&pexh[cc & 1][blk >> 1][lane])[blk & 1] = u32x2{hw[0], hw[1]};
+        reinterpret_cast<u32x2*>(&pexl[cc & 1][blk >> 1][lane])[blk & 1] = u32x2{lw[0], lw[1]};
         bs[kb] = (x[0] + x[1]) + (x[2] + x[3]);
       }
 #pragma unroll
@@ -304,9 +337,12 @@ __global__ __launch_bounds__(AttnCfg<CH>::NW * 64) void attn_split_kernel(AttnLa
   // all waves: o = o * alpha + P.V over chunk cc for the wave's d blocks;
   // wave 0: l = l * alpha + (the chunk's probability sum)
   auto pv = [&](int64_t cc, float alpha) {
-    u32x4 px[Cfg::KB];
+    u32x4 pxh[Cfg::PV], pxl[Cfg::PV];
 #pragma unroll
-    for (int kb = 0; kb < Cfg::KB; ++kb) px[kb] = pex[cc & 1][kb][lane];
+    for (int t = 0; t < Cfg::PV; ++t) {
+      pxh[t] = pexh[cc & 1][t][lane];
+      pxl[t] = pexl[cc & 1][t][lane];
+    }
     float wsum[NWS];
     if (wave == 0) {
 #pragma unroll
@@ -321,10 +357,8 @@ __global__ __launch_bounds__(AttnCfg<CH>::NW * 64) void attn_split_kernel(AttnLa
 #pragma unroll
     for (int t = 0; t < Cfg::PV; ++t) {
       // B operand (P^T): head c16, keys {32t + 4 g4 + e} (e < 4) and {32t + 16 + 4 g4 + e - 4}
-      const u32x4 pa = u32x4{px[2 * t][0], px[2 * t][1], px[2 * t + 1][0], px[2 * t + 1][1]};
-      const u32x4 pb = u32x4{px[2 * t][2], px[2 * t][3], px[2 * t + 1][2], px[2 * t + 1][3]};
-      const bf16x8 pf = __builtin_bit_cast(bf16x8, pa);
-      const bf16x8 pfl = __builtin_bit_cast(bf16x8, pb);
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, pxh[t]);
+      const bf16x8 pfl = __builtin_bit_cast(bf16x8, pxl[t]);
       // A operand (V^T): the same keys for d = 16 db + c16, by two transpose reads
       const int k0 = 32 * t + 4 * g4 + tr_m, k1 = k0 + 16;
 #pragma unroll
