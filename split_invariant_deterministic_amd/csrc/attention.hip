@@ -173,19 +173,51 @@ __global__ __launch_bounds__(AttnCfg<CH>::NW * 64) void attn_split_kernel(AttnLa
   const int j = a.split_lo + (int)(idx % nsplit);
   idx /= nsplit;
   const int kvh = (int)(idx % a.Hkv);
-  const int64_t row = idx / a.Hkv;
+  int64_t row = idx / a.Hkv;
   const int grp = a.Hq / a.Hkv;
   const int S = a.split_kv;
 
-  const int seq = a.q_seq[row];
-  bool valid = seq >= 0 && seq < a.num_seqs;
+  bool valid;
   int64_t start = 0, L = 1;
-  if (valid) {
-    start = a.cu_seqlens[seq];
-    const int64_t len = (int64_t)a.cu_seqlens[seq + 1] - start;
-    const int64_t p = a.q_pos[row];
-    valid = p >= 0 && p < len;
-    L = p + 1;
+  if (a.Tq >= 2 && a.Tq <= 64) {
+    // A few rows of unequal length: the workgroups take the rows in order of
+    // decreasing chunk count (ties by row index), so the longest rows are
+    // dispatched first and the launch does not end on a long row that was
+    // dispatched last. Which workgroup computes an item does not change its
+    // arithmetic. Lane i holds row i's bounds; every wave ranks the rows alike.
+    const int nr = (int)a.Tq;
+    int si = -1, pi = -1, s0 = 0, len = 0;
+    if (lane < nr) {
+      si = a.q_seq[lane];
+      pi = a.q_pos[lane];
+    }
+    const bool sok = si >= 0 && si < a.num_seqs;
+    if (sok) {
+      s0 = a.cu_seqlens[si];
+      len = a.cu_seqlens[si + 1] - s0;
+    }
+    const bool vi = sok && pi >= 0 && pi < len;
+    const int ni = vi ? (int)(((int64_t)pi + CH) / CH) : 0;  // chunks of the row's visible keys
+    int rank = 0;
+    for (int q = 0; q < nr; ++q) {
+      const int nq = __builtin_amdgcn_readlane(ni, q);
+      rank += (nq > ni || (nq == ni && q < lane)) ? 1 : 0;
+    }
+    const int r = (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(lane < nr && rank == (int)row));
+    row = r;
+    valid = __builtin_amdgcn_readlane((int)vi, r) != 0;
+    start = __builtin_amdgcn_readlane(s0, r);
+    L = (int64_t)__builtin_amdgcn_readlane(pi, r) + 1;
+  } else {
+    const int seq = a.q_seq[row];
+    valid = seq >= 0 && seq < a.num_seqs;
+    if (valid) {
+      start = a.cu_seqlens[seq];
+      const int64_t len = (int64_t)a.cu_seqlens[seq + 1] - start;
+      const int64_t p = a.q_pos[row];
+      valid = p >= 0 && p < len;
+      L = p + 1;
+    }
   }
   if (!valid) {  // uniform over the block
     if (wave == 0) {
