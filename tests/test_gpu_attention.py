@@ -160,6 +160,23 @@ def test_batch_invariance_256(inv, big_batch):
         check_bf16(full[i:i + 1], _oracle(one), f"row {i}")
 
 
+def test_split_ranges_small_batch(inv, big_batch):
+    # 2 to 64 rows are dispatched longest first: split ranges computed separately (emulated
+    # context-parallel ranks) still merge to the full launch's bits, at 8 and 64 rows
+    d = big_batch
+    c = inv.contract()
+    for B in (8, 64):
+        q = d["q"][:B].contiguous()
+        qs, qp = d["q_seq"][:B].contiguous(), d["q_pos"][:B].contiguous()
+        full = _run(inv, {"q": q, "k": d["k"], "v": d["v"], "cu_seqlens": d["cu_seqlens"], "q_seq": qs,
+                          "q_pos": qp}, c)
+        for R in (2, 16):
+            ws = inv.attn_workspace(q, c)
+            for r in reversed(range(R)):
+                inv.attn_splits(q, d["k"], d["v"], d["cu_seqlens"], qs, qp, r * 16 // R, (r + 1) * 16 // R, c, ws)
+            assert bitwise_equal(inv.attn_combine(ws, B, 32, 128, c), full), (B, R)
+
+
 def test_left_fold_changes_bits(inv, big_batch):
     d = big_batch
     bal = _run(inv, d, inv.contract())
