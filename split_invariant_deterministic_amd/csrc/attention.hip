@@ -128,10 +128,9 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
 // above, whichever wave holds the operands: the chunk max is a max over the
 // same set (exact, and a zero max is made +0), the sum's tree does not depend
 // on which wave adds which node, and each output d block sees the schedule's
-// MFMA chain. Several waves per
-// item keep the chip busy at decode batches of a few rows (16 splits x 8 kv
-// heads are 128 items at one row), where a chunk's dependent steps, not the
-// bytes, set the time.
+// MFMA chain. Several waves per item keep the chip busy at decode batches of
+// a few rows (16 splits x 8 kv heads are 128 items at one row), where a
+// chunk's dependent steps, not the bytes, set the time.
 //
 // K and V are read through buffer descriptors whose range ends at the chunk's
 // last visible key, so keys past L read as zero without a per-lane clamp and
