@@ -80,6 +80,34 @@ def test_long_context_against_oracle(inv):
     check_bf16(out, _oracle(d), "long")
 
 
+@pytest.mark.parametrize("kv_chunk", [32, 64, 128])
+def test_keys_past_the_row_are_never_read(inv, kv_chunk):
+    # every K and V row after a query's visible keys holds NaN (inside the same allocation, and
+    # past the last sequence); the per-chunk buffer ranges end at each row's last visible key,
+    # so the outputs equal those with finite rows, bit for bit (a read of a NaN row would
+    # survive the zero probability as NaN)
+    lengths = [1, 17, 64, 65, 300, 1025, 2000]
+    d = synth.attn(torch.tensor(lengths), seed=10)
+    g = torch.Generator().manual_seed(10)
+    pos = [int(torch.randint(0, L, (1,), generator=g)) for L in lengths]
+    pos[0], pos[-1] = 0, 1000  # a single key, and a row whose chunk ends mid-sequence
+    d["q_pos"] = torch.tensor(pos, dtype=torch.int32)
+    c = inv.contract(kv_chunk=kv_chunk)
+    clean = _run(inv, _dev(d), c)
+    T = int(d["cu_seqlens"][-1])
+    k = torch.full((T + 256,) + tuple(d["k"].shape[1:]), float("nan"), dtype=torch.bfloat16)
+    v = k.clone()
+    k[:T], v[:T] = d["k"], d["v"]
+    for i, L in enumerate(lengths):
+        s0 = int(d["cu_seqlens"][i])
+        k[s0 + pos[i] + 1:s0 + L] = float("nan")
+        v[s0 + pos[i] + 1:s0 + L] = float("nan")
+    dn = _dev(d)
+    kd, vd = k.to(DEV), v.to(DEV)
+    dn["k"], dn["v"] = kd[:T], vd[:T]
+    assert bitwise_equal(_run(inv, dn, c), clean)
+
+
 def test_single_key_returns_v0_bitwise(inv):
     d = _dev(synth.attn(torch.tensor([1, 1, 1]), seed=3))
     out = _run(inv, d, inv.contract()).cpu()
