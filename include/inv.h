@@ -229,6 +229,8 @@ inv_status inv_sha256(const void* data, size_t bytes, uint8_t digest[32]);
  * reports G*M*N*4 bytes; given that much, G aligned subtrees are reduced in
  * parallel and combined by the same tree (bitwise the same result as without
  * the workspace).
+ * A and B are 16-byte aligned, C is aligned to its element (2 bytes bf16, 4
+ * fp32) and ws, when given, is 4-byte aligned; else INV_E_ARG.
  * ------------------------------------------------------------------------ */
 inv_status inv_gemm(const inv_contract* c, const void* A, const void* B, void* C,
                     int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes,
@@ -268,7 +270,8 @@ inv_status inv_gemm_leaves(const inv_contract* c, const void* A, const void* B, 
 /* Combine `count` fp32 partials P [count, M, N] with the contract's tree
  * and cast to out_dtype: C = round_out(tree(P[0..count-1])). count is a power
  * of two; with BALANCED, combining the R rank partials of inv_gemm_rank, or
- * the L leaf partials of inv_gemm_leaves, reproduces inv_gemm bit for bit. */
+ * the L leaf partials of inv_gemm_leaves, reproduces inv_gemm bit for bit.
+ * P is 4-byte aligned and C aligned to its element, else INV_E_ARG. */
 inv_status inv_tree_combine(const inv_contract* c, const float* P, uint32_t count, void* C,
                             int64_t M, int64_t N, hipStream_t stream);
 
@@ -353,7 +356,9 @@ inv_status inv_logprob_combine(const inv_contract* c, const float* stats, const 
  * The S split states are merged by the contract's tree (o scaled like l) and
  * out = bf16(o / l). Every row's bits depend only on its own q, its visible
  * keys and L, so a decode row equals the same position's prefill row.
- * Workspace: ws_bytes >= inv_workspace_bytes(INV_OP_DECODE_ATTN, Tq, Hq, D).
+ * Workspace: ws_bytes >= inv_workspace_bytes(INV_OP_DECODE_ATTN, Tq, Hq, D),
+ * else INV_E_WORKSPACE; ws 4-byte aligned and out 2-byte aligned, else
+ * INV_E_ARG (the same for the two calls below).
  * ------------------------------------------------------------------------ */
 inv_status inv_decode_attn(const inv_contract* c, const void* q, const void* k, const void* v,
                            const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* q_seq,

@@ -74,6 +74,8 @@ size_t gdn_prefill_ws_bytes(int64_t T, int64_t H, int64_t S, int64_t C) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+// fp32 and bf16 buffers are read and written at least one element at a time
+bool aligned_to(const void* p, unsigned bytes) { return (reinterpret_cast<uintptr_t>(p) & (bytes - 1u)) == 0; }
 
 inv_status check_logprob_contract(const inv_contract* c, int64_t V) {
   inv_status s = check_contract(c);
@@ -222,13 +224,14 @@ static inv::GemmLaunch gemm_launch(const void* A, const void* B, void* C, int64_
   return g;
 }
 
-static inv_status gemm_shape_check(const void* A, const void* B, const void* C, int64_t M, int64_t N,
-                                   int64_t K) {
+static inv_status gemm_shape_check(const void* A, const void* B, const void* C, unsigned c_elem, int64_t M,
+                                   int64_t N, int64_t K) {
   if (M < 0 || N < 0 || K <= 0) return INV_E_ARG;
   if (M > (int64_t)1 << 31 || N > (int64_t)1 << 31) return INV_E_UNSUPPORTED;
   if (M > 0 && N > 0 && (!A || !B || !C)) return INV_E_ARG;
   // 16-byte vector loads along K
   if ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) & 15u) return INV_E_ARG;
+  if (!aligned_to(C, c_elem)) return INV_E_ARG;
   return INV_OK;
 }
 
@@ -236,7 +239,8 @@ inv_status inv_gemm(const inv_contract* c, const void* A, const void* B, void* C
                     int64_t K, void* ws, size_t ws_bytes, hipStream_t stream) {
   inv_status s = check_gemm_contract(c, K);
   if (s != INV_OK) return s;
-  if ((s = gemm_shape_check(A, B, C, M, N, K)) != INV_OK) return s;
+  if ((s = gemm_shape_check(A, B, C, out_is_bf16(c) ? 2u : 4u, M, N, K)) != INV_OK) return s;
+  if (!aligned_to(ws, 4u)) return INV_E_ARG;  // fp32 partial planes
   if (M == 0 || N == 0) return INV_OK;
   const int L = (int)c->leaves, R = (int)c->ranks;
   const int kl = (int)(K / L);
@@ -264,7 +268,7 @@ inv_status inv_gemm_noalloc(const inv_contract* c, const void* A, const void* B,
                             int64_t K, hipStream_t stream) {
   inv_status s = check_gemm_contract(c, K);
   if (s != INV_OK) return s;
-  if ((s = gemm_shape_check(A, B, C, M, N, K)) != INV_OK) return s;
+  if ((s = gemm_shape_check(A, B, C, out_is_bf16(c) ? 2u : 4u, M, N, K)) != INV_OK) return s;
   if (M == 0 || N == 0) return INV_OK;
   const int L = (int)c->leaves, R = (int)c->ranks;
   const int kl = (int)(K / L);
@@ -287,7 +291,7 @@ inv_status inv_gemm_rank(const inv_contract* c, const void* A, const void* B, fl
                          int64_t K, uint32_t rank, hipStream_t stream) {
   inv_status s = check_gemm_contract(c, K);
   if (s != INV_OK) return s;
-  if ((s = gemm_shape_check(A, B, P_r, M, N, K)) != INV_OK) return s;
+  if ((s = gemm_shape_check(A, B, P_r, 4u, M, N, K)) != INV_OK) return s;
   if (rank >= c->ranks) return INV_E_ARG;
   if (M == 0 || N == 0) return INV_OK;
   const int L = (int)c->leaves, R = (int)c->ranks;
@@ -300,7 +304,7 @@ inv_status inv_gemm_leaves(const inv_contract* c, const void* A, const void* B, 
                            int64_t K, uint32_t leaf_lo, uint32_t leaf_hi, hipStream_t stream) {
   inv_status s = check_gemm_contract(c, K);
   if (s != INV_OK) return s;
-  if ((s = gemm_shape_check(A, B, P, M, N, K)) != INV_OK) return s;
+  if ((s = gemm_shape_check(A, B, P, 4u, M, N, K)) != INV_OK) return s;
   if (leaf_lo >= leaf_hi || leaf_hi > c->leaves) return INV_E_ARG;
   if (M == 0 || N == 0) return INV_OK;
   const int L = (int)c->leaves;
@@ -316,6 +320,7 @@ inv_status inv_tree_combine(const inv_contract* c, const float* P, uint32_t coun
   if (!is_pow2(count) || count > 64) return INV_E_UNSUPPORTED;
   if (M == 0 || N == 0) return INV_OK;
   if (!P || !C) return INV_E_ARG;
+  if (!aligned_to(P, 4u) || !aligned_to(C, out_is_bf16(c) ? 2u : 4u)) return INV_E_ARG;
   return hip_status(inv::launch_tree_combine(P, (int)count, M * N, C, out_is_bf16(c), c->tree == INV_TREE_LEFT_FOLD,
                                              stream));
 }
@@ -453,7 +458,7 @@ inv_status inv_lmhead_logprob(const inv_contract* c, const void* h, const void* 
   if (s != INV_OK) return s;
   if (c->out_dtype != INV_FP32) return INV_E_CONTRACT;  // logits are never rounded below fp32
   if (c->ranks != 1) return INV_E_UNSUPPORTED;
-  if ((s = gemm_shape_check(h, W, out, M, V, K)) != INV_OK) return s;
+  if ((s = gemm_shape_check(h, W, out, 4u, M, V, K)) != INV_OK) return s;
   if ((s = check_block16(c, M, V, ws, ws_bytes)) != INV_OK) return s;
   if (M == 0) return INV_OK;
   if (!target) return INV_E_ARG;
@@ -563,6 +568,7 @@ inv_status inv_decode_attn(const inv_contract* c, const void* q, const void* k, 
   if (!out) return INV_E_ARG;
   const size_t need = inv_workspace_bytes(c, INV_OP_DECODE_ATTN, Tq, Hq, D);
   if (!ws || ws_bytes < need) return INV_E_WORKSPACE;
+  if (!aligned_to(ws, 4u) || !aligned_to(out, 2u)) return INV_E_ARG;  // fp32 split states, bf16 output
   hipError_t e = inv::launch_attn_splits(
       attn_launch(c, q, k, v, cu_seqlens, num_seqs, q_seq, q_pos, Tq, Hq, Hkv, D, 0, c->split_kv, ws), stream);
   if (e != hipSuccess) return INV_E_HIP;
@@ -580,6 +586,7 @@ inv_status inv_attn_splits(const inv_contract* c, const void* q, const void* k, 
   if (Tq == 0) return INV_OK;
   const size_t need = inv_workspace_bytes(c, INV_OP_DECODE_ATTN, Tq, Hq, D);
   if (!ws || ws_bytes < need) return INV_E_WORKSPACE;
+  if (!aligned_to(ws, 4u)) return INV_E_ARG;
   return hip_status(inv::launch_attn_splits(
       attn_launch(c, q, k, v, cu_seqlens, num_seqs, q_seq, q_pos, Tq, Hq, Hkv, D, split_lo, split_hi, ws), stream));
 }
@@ -594,6 +601,7 @@ inv_status inv_attn_combine(const inv_contract* c, const void* ws, size_t ws_byt
   if (!out) return INV_E_ARG;
   const size_t need = inv_workspace_bytes(c, INV_OP_DECODE_ATTN, Tq, Hq, D);
   if (!ws || ws_bytes < need) return INV_E_WORKSPACE;
+  if (!aligned_to(ws, 4u) || !aligned_to(out, 2u)) return INV_E_ARG;
   return hip_status(inv::launch_attn_combine(static_cast<const float*>(ws), out, Tq, Hq, D, (int)c->split_kv,
                                              c->tree == INV_TREE_LEFT_FOLD, stream));
 }

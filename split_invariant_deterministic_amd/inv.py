@@ -233,6 +233,23 @@ def _need(t, dtype, name, ndim=None):
     return t
 
 
+def _ws_bytes(ws, name="ws"):
+    """Size in bytes of a workspace tensor, 0 for None.
+
+    The library checks this size against what the call needs, so it must be
+    the tensor's real size whatever its element type, and the pointer must be
+    a device allocation the kernels can write from its start onwards."""
+    if ws is None:
+        return 0
+    if not isinstance(ws, torch.Tensor):
+        raise TypeError(f"{name}: expected a tensor")
+    if ws.device.type != "cuda":
+        raise ValueError(f"{name}: expected a device tensor, got {ws.device}")
+    if not ws.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return ws.numel() * ws.element_size()
+
+
 def _shape(t, shape, name):
     """Raises before any launch if t's shape is not ``shape`` (a wrong-sized
     buffer would be read or written out of bounds by the kernels)."""
@@ -266,7 +283,7 @@ def gemm(A, B, c, out=None, ws=None, use_ws=True):
     nbytes = workspace_bytes(c, OP_GEMM, M, N, K)
     if ws is None and nbytes > 0 and (use_ws or c.ranks > 1):
         ws = torch.empty(nbytes, dtype=torch.uint8, device=A.device)
-    wsz = ws.numel() * ws.element_size() if ws is not None else 0
+    wsz = _ws_bytes(ws)
     _call("inv_gemm", ctypes.byref(c), _ptr(A), _ptr(B), _ptr(out), M, N, K, _ptr(ws), wsz, _stream())
     return out
 
@@ -445,7 +462,7 @@ def lmhead_logprob(h, W, target, c, out=None, ws=None):
     if ws is None:
         ws = block16_workspace(M, V, h.device)
     _call("inv_lmhead_logprob", ctypes.byref(c), _ptr(h), _ptr(W), _ptr(target), _ptr(out), M, V, K, _ptr(ws),
-          ws.numel() * ws.element_size(), _stream())
+          _ws_bytes(ws), _stream())
     return out
 
 
@@ -462,7 +479,7 @@ def logprob_block16(logits, target, c, out=None, ws=None):
     if ws is None:
         ws = block16_workspace(M, V, logits.device)
     _call("inv_logprob_block16", ctypes.byref(c), _ptr(logits), ldl, _ptr(target), _ptr(out), M, V, _ptr(ws),
-          ws.numel() * ws.element_size(), _stream())
+          _ws_bytes(ws), _stream())
     return out
 
 
@@ -500,7 +517,7 @@ def gdn_prefill(q, k, v, g, beta, cu_seqlens, c, out=None, cache=None, ws=None):
     if ws is None:
         ws = torch.empty(workspace_bytes(c, OP_GDN_PREFILL, T, H, S), dtype=torch.uint8, device=q.device)
     _call("inv_gdn_prefill", ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), S,
-          T, H, D, _ptr(out), _ptr(cache), _ptr(ws), ws.numel() * ws.element_size(), _stream())
+          T, H, D, _ptr(out), _ptr(cache), _ptr(ws), _ws_bytes(ws), _stream())
     return out
 
 
@@ -569,14 +586,14 @@ def decode_attn(q, k, v, cu_seqlens, q_seq, q_pos, c, ws=None, out=None):
     _need(out, torch.bfloat16, "out", 3)
     _shape(out, q.shape, "out")
     _call("inv_decode_attn", ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), S, _ptr(q_seq),
-          _ptr(q_pos), _ptr(out), Tq, Hq, Hkv, D, _ptr(ws), ws.numel() * 4, _stream())
+          _ptr(q_pos), _ptr(out), Tq, Hq, Hkv, D, _ptr(ws), _ws_bytes(ws), _stream())
     return out
 
 
 def attn_splits(q, k, v, cu_seqlens, q_seq, q_pos, split_lo, split_hi, c, ws):
     Tq, Hq, Hkv, D, S = _attn_args(q, k, v, cu_seqlens, q_seq, q_pos)
     _call("inv_attn_splits", ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), S, _ptr(q_seq),
-          _ptr(q_pos), Tq, Hq, Hkv, D, split_lo, split_hi, _ptr(ws), ws.numel() * 4, _stream())
+          _ptr(q_pos), Tq, Hq, Hkv, D, split_lo, split_hi, _ptr(ws), _ws_bytes(ws), _stream())
     return ws
 
 
@@ -585,7 +602,7 @@ def attn_combine(ws, Tq, Hq, D, c, out=None, device=None):
         out = torch.empty((Tq, Hq, D), dtype=torch.bfloat16, device=ws.device)
     _need(out, torch.bfloat16, "out", 3)
     _shape(out, (Tq, Hq, D), "out")
-    _call("inv_attn_combine", ctypes.byref(c), _ptr(ws), ws.numel() * 4, _ptr(out), Tq, Hq, D, _stream())
+    _call("inv_attn_combine", ctypes.byref(c), _ptr(ws), _ws_bytes(ws), _ptr(out), Tq, Hq, D, _stream())
     return out
 
 

@@ -155,6 +155,23 @@ def test_entry_points_reject_before_any_launch():
                                1 << 40, null) == inv.E_UNSUPPORTED
     assert lib.inv_attn_splits(by(ca), fake, fake, fake, fake, 1, fake, fake, 65536, 32, 8, 128, 0, 1, fake,
                                1 << 40, null) == inv.E_UNSUPPORTED
+    # fp32 workspaces and partials are accessed an element at a time, bf16 outputs likewise: a pointer off
+    # its element's alignment is rejected before any launch
+    odd2, odd1 = ctypes.c_void_p((1 << 20) + 2), ctypes.c_void_p((1 << 20) + 1)
+    assert lib.inv_decode_attn(by(ca), fake, fake, fake, fake, 1, fake, fake, fake, 1, 32, 8, 128, odd2,
+                               1 << 30, null) == inv.E_ARG
+    assert lib.inv_decode_attn(by(ca), fake, fake, fake, fake, 1, fake, fake, odd1, 1, 32, 8, 128, fake,
+                               1 << 30, null) == inv.E_ARG
+    assert lib.inv_attn_splits(by(ca), fake, fake, fake, fake, 1, fake, fake, 1, 32, 8, 128, 0, 1, odd2,
+                               1 << 30, null) == inv.E_ARG
+    assert lib.inv_attn_combine(by(ca), odd2, 1 << 30, fake, 1, 32, 128, null) == inv.E_ARG
+    assert lib.inv_attn_combine(by(ca), fake, 1 << 30, odd1, 1, 32, 128, null) == inv.E_ARG
+    assert lib.inv_gemm(by(c), fake, fake, fake, 4, 4, 4096, odd2, 1 << 30, null) == inv.E_ARG
+    assert lib.inv_gemm(by(c), fake, fake, odd1, 4, 4, 4096, null, 0, null) == inv.E_ARG
+    assert lib.inv_gemm(by(inv.contract(out="fp32")), fake, fake, odd2, 4, 4, 4096, null, 0, null) == inv.E_ARG
+    assert lib.inv_gemm_rank(by(c2), fake, fake, odd2, 4, 4, 4096, 0, null) == inv.E_ARG
+    assert lib.inv_tree_combine(by(c), odd2, 2, fake, 4, 4, null) == inv.E_ARG
+    assert lib.inv_tree_combine(by(c), fake, 2, odd1, 4, 4, null) == inv.E_ARG
     cm = inv.contract(leaves=8)
     assert lib.inv_moe_route(by(cm), fake, fake, fake, 4, 300, null) == inv.E_UNSUPPORTED
     assert lib.inv_moe_route(by(cm), fake, fake, fake, 4, 4, null) == inv.E_UNSUPPORTED      # k > E
@@ -198,6 +215,18 @@ def test_entry_points_reject_before_any_launch():
     assert lib.inv_gdn_decode(by(cg), fake, fake, fake, fake, fake, fake, 0, 16, 128, fake, fake, null) == inv.OK
     assert lib.inv_gdn_decode(by(cg), fake, fake, fake, fake, fake, fake, 4, 16, 128, fake, null, null) \
         == inv.E_ARG
+
+
+def test_binding_workspace_checked_before_the_call():
+    """The binding reports a workspace's size in bytes from its element type
+    and refuses a host tensor, before the library sees the pointer."""
+    import torch
+    inv = _inv()
+    assert inv._ws_bytes(None) == 0
+    with pytest.raises(ValueError):
+        inv._ws_bytes(torch.empty(16, dtype=torch.uint8))
+    with pytest.raises(TypeError):
+        inv._ws_bytes(16)
 
 
 def test_status_strings():

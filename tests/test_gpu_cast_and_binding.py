@@ -99,3 +99,39 @@ def test_binding_rejects_wrong_shapes_before_launch(inv):
     with pytest.raises(ValueError):
         inv.moe_combine(Y, torch.zeros((2, 4), device=DEV), torch.zeros((2, 8), dtype=torch.int32, device=DEV), c8)
     torch.cuda.synchronize()
+
+
+def test_attention_workspace_size_is_counted_in_bytes(inv):
+    """The attention entry points hand the library the workspace's size in
+    bytes whatever its element type: a byte workspace of exactly the size the
+    library asks for gives the same output as the default one, one of four
+    bytes less is refused by the library's size check, and a host tensor is
+    refused before the call."""
+    g = torch.Generator().manual_seed(5)
+    S, L, Hq, Hkv, D = 2, 300, 8, 2, 128
+    q = torch.randn((S, Hq, D), generator=g).to(torch.bfloat16).to(DEV)
+    k = torch.randn((S * L, Hkv, D), generator=g).to(torch.bfloat16).to(DEV)
+    v = torch.randn((S * L, Hkv, D), generator=g).to(torch.bfloat16).to(DEV)
+    cu = torch.tensor([0, L, 2 * L], dtype=torch.int32, device=DEV)
+    q_seq = torch.tensor([0, 1], dtype=torch.int32, device=DEV)
+    q_pos = torch.tensor([L - 1, L - 7], dtype=torch.int32, device=DEV)
+    c = inv.contract()
+    ref = inv.decode_attn(q, k, v, cu, q_seq, q_pos, c)
+    need = inv.workspace_bytes(c, inv.OP_DECODE_ATTN, S, Hq, D)
+    assert need > 4
+    ws8 = torch.empty(need, dtype=torch.uint8, device=DEV)
+    out = inv.decode_attn(q, k, v, cu, q_seq, q_pos, c, ws=ws8)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    with pytest.raises(inv.InvError) as e:
+        inv.decode_attn(q, k, v, cu, q_seq, q_pos, c, ws=ws8[: need - 4])
+    assert e.value.status == inv.E_WORKSPACE
+    with pytest.raises(inv.InvError) as e:
+        inv.attn_splits(q, k, v, cu, q_seq, q_pos, 0, c.split_kv, c, ws8[: need - 4])
+    assert e.value.status == inv.E_WORKSPACE
+    with pytest.raises(inv.InvError) as e:
+        inv.attn_combine(ws8[: need - 4], S, Hq, D, c)
+    assert e.value.status == inv.E_WORKSPACE
+    with pytest.raises(ValueError):
+        inv.decode_attn(q, k, v, cu, q_seq, q_pos, c, ws=torch.empty(need, dtype=torch.uint8))
+    torch.cuda.synchronize()
