@@ -112,6 +112,26 @@ def test_tree_shape_pin(inv):
     assert bal[0, 0].item() == g["balanced"]
 
 
+@pytest.mark.parametrize("count", [2, 8, 16, 32])
+@pytest.mark.parametrize("shape", [(5, 12), (3, 7), (64, 4100)])
+def test_tree_combine_against_oracle(inv, count, shape):
+    """inv_tree_combine against the oracle's fp32 tree and boundary cast, bit
+    for bit, for both trees and both output types, on planes of 60, 21 and
+    262400 elements. Partials mix magnitudes over 2^-20 .. 2^20 so that the
+    order of the adds decides bits."""
+    M, N = shape
+    rng = np.random.default_rng(count * 1000 + M)
+    P = (rng.standard_normal((count, M, N)) * np.exp2(rng.integers(-20, 21, (count, M, N)))).astype(np.float32)
+    Pd = torch.from_numpy(P).to(DEV)
+    for tree in ("balanced", "left_fold"):
+        for out in ("fp32", "bf16"):
+            c = inv.contract(leaves=count, out=out, tree=tree)
+            want = ogemm.cast_out(ogemm.combine_partials(P, tree), out)
+            got = inv.tree_combine(Pd, c).float().cpu().numpy()
+            assert np.array_equal(got.astype(np.float64).view(np.uint64),
+                                  np.asarray(want, dtype=np.float64).view(np.uint64)), (tree, out)
+
+
 # ------------------------------------------------------------ invariance
 
 DENSE = [(4096, 12288), (12288, 4096)]
