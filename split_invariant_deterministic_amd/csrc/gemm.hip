@@ -1066,10 +1066,15 @@ struct StreamCtx {
   // Ring depth: the weight bytes in flight over the grid are
   // N/16 * leaves * depth KiB whatever FM is, so the ring is as deep as the
   // registers allow: up to 8 blocks for 16-32 rows, 4 for 48-64, the largest
-  // power of two that divides spl.
+  // power of two that divides spl. A single 16-row block with leaves of 32
+  // blocks or more (few, long-lived waves) takes 16: the rotated
+  // 4096-12288-4096 pair at M = 1 and 7 gains about 2.4 %, while 16 for the
+  // 16-block leaves of the first projection (many short waves) or 24 for the
+  // second lost occupancy (+23 % and about even).
   static constexpr int D = FM <= 2 ? 8 : 4;
   __device__ __forceinline__ void leaf(Acc& acc) {
-    if (D >= 8 && spl % 8 == 0) leaf_ring<(D >= 8 ? 8 : 1)>(acc);
+    if (FM == 1 && spl >= 32 && spl % 16 == 0) leaf_ring<(FM == 1 ? 16 : 1)>(acc);
+    else if (D >= 8 && spl % 8 == 0) leaf_ring<(D >= 8 ? 8 : 1)>(acc);
     else if (D >= 4 && spl % 4 == 0) leaf_ring<(D >= 4 ? 4 : 1)>(acc);
     else if (spl % 2 == 0) leaf_ring<2>(acc);
     else leaf_ring<1>(acc);
