@@ -405,6 +405,22 @@ struct RingCtx {
     if (more) issue_done();
     ++g;
   }
+  // The stages of a tile for a wave whose 64 rows are all padding (the last
+  // row tile of a grouped expert): the same waits, barriers and share of the
+  // loads as stage64, no fragment reads and no MFMAs, then the ks = 0
+  // fragments of the stage that follows (the next tile's first stage64
+  // expects them).
+  __device__ __forceinline__ void idle_stages(int n) {
+    static_assert(BK == 64, "64-k stages");
+    for (int st = 0; st < n; ++st) {
+      wait_vm_rem<R::LOADS, R::NS - 2>(issued - 2 - g);
+      block_barrier();  // stage g+1 visible; every wave's reads of stage g are done
+      rd_off = next_slot(rd_off);
+      if (issued < limit) issue_next();
+      ++g;
+    }
+    read_frags(rd_off, 0, fa0, fb0);
+  }
   template <bool FIRST>
   __device__ __forceinline__ void stage32(Acc& acc) {
     // this thread's loads of stage g are done once at most the loads of
@@ -970,27 +986,38 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void gemm_ring_kernel(TileParam
         if (c.issued == c.iss_end) c.take_next();  // this tile's stages were all issued already
       }
     }
-    typename Ctx::Acc acc;
-    if constexpr (SPILL > 0) {
-      float* spill = reinterpret_cast<float*>(&lds[R::NS * R::STAGE]) + wave * 64 * WN + lane;
-      run_tree<4>(c, acc);
-  #pragma unroll
-      for (int i = 0; i < 4; ++i)
-  #pragma unroll
-        for (int j = 0; j < FN; ++j)
-  #pragma unroll
-          for (int r = 0; r < 4; ++r) spill[((i * FN + j) * 4 + r) * 64] = acc.v[i][j][r];
-      run_tree<4>(c, acc);
-  #pragma unroll
-      for (int i = 0; i < 4; ++i)
-  #pragma unroll
-        for (int j = 0; j < FN; ++j)
-  #pragma unroll
-          for (int r = 0; r < 4; ++r) acc.v[i][j][r] = spill[((i * FN + j) * 4 + r) * 64] + acc.v[i][j][r];
+    // All 64 rows of this wave past the expert's last row (grouped launches):
+    // the wave keeps the ring's waits, barriers and loads and skips the
+    // MFMAs, the tree and the epilogue (which would store nothing). Halves
+    // the LDS reads and MFMAs of a tile with 64 valid rows or fewer.
+    bool idle = false;
+    if constexpr (GROUPED && SPILL > 0 && BK == 64)
+      idle = __builtin_amdgcn_readfirstlane((int)(cur.m0 + wm * 64 >= cur.m_end)) != 0;
+    if (idle) {
+      if constexpr (GROUPED && SPILL > 0 && BK == 64) c.idle_stages(stages);
     } else {
-      run_tree<NL>(c, acc);
+      typename Ctx::Acc acc;
+      if constexpr (SPILL > 0) {
+        float* spill = reinterpret_cast<float*>(&lds[R::NS * R::STAGE]) + wave * 64 * WN + lane;
+        run_tree<4>(c, acc);
+  #pragma unroll
+        for (int i = 0; i < 4; ++i)
+  #pragma unroll
+          for (int j = 0; j < FN; ++j)
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) spill[((i * FN + j) * 4 + r) * 64] = acc.v[i][j][r];
+        run_tree<4>(c, acc);
+  #pragma unroll
+        for (int i = 0; i < 4; ++i)
+  #pragma unroll
+          for (int j = 0; j < FN; ++j)
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) acc.v[i][j][r] = spill[((i * FN + j) * 4 + r) * 64] + acc.v[i][j][r];
+      } else {
+        run_tree<NL>(c, acc);
+      }
+      finish(cur, acc);
     }
-    finish(cur, acc);
     if (!more_tiles) break;
     cur = nx;
     tile = tn;
