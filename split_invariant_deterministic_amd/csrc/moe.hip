@@ -25,7 +25,59 @@ namespace {
 // The selection is then written in ascending expert id, and the weights are
 // the softmax over the selected logits: e_j = exp2((z_j - max) * log2e),
 // denominator summed over j in ascending id, w_j = e_j / denominator.
+//
+// The argmax runs on 64-bit keys whose unsigned order is the selection order:
+// high word the logit mapped monotonically to an unsigned integer (-0 taken
+// as +0, since the two compare equal), low word 0xFFFF - id. NaN logits,
+// experts past E and taken experts have key 0. A round is a branch-free
+// maximum over the lane's keys, then over the wave by four DPP steps inside
+// each row of 16 lanes and the row and half swaps (VALU only).
 constexpr int kRouteMaxK = 32;
+
+__device__ __forceinline__ uint32_t route_key_hi(float z) {
+  uint32_t u = __float_as_uint(z);
+  if (u == 0x80000000u) u = 0u;  // -0 -> +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// (hi, lo) <- the larger of itself and (ohi, olo), unsigned 64-bit order
+__device__ __forceinline__ void key_take_max(uint32_t& hi, uint32_t& lo, uint32_t ohi, uint32_t olo) {
+  const bool t = ohi > hi || (ohi == hi && olo > lo);
+  hi = t ? ohi : hi;
+  lo = t ? olo : lo;
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+
+// Maximum key over the 64 lanes, left in every lane. Within a row: quad
+// pairs (xor 1, xor 2), then the half-row and row mirrors; then the row swap
+// (lane ^ 16) and the half swap (lane ^ 32), each exchanging two copies of
+// the key so that every lane holds its own and its partner's. The maximum of
+// a set does not depend on the order it is taken in.
+__device__ __forceinline__ void wave_key_max(uint32_t& hi, uint32_t& lo) {
+  key_take_max(hi, lo, dpp_u32<0xB1>(hi), dpp_u32<0xB1>(lo));
+  key_take_max(hi, lo, dpp_u32<0x4E>(hi), dpp_u32<0x4E>(lo));
+  key_take_max(hi, lo, dpp_u32<0x141>(hi), dpp_u32<0x141>(lo));
+  key_take_max(hi, lo, dpp_u32<0x140>(hi), dpp_u32<0x140>(lo));
+  uint32_t a = hi, b = hi, c = lo, d = lo;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\tv_permlane16_swap_b32 %2, %3"
+               : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+  hi = a;
+  lo = c;
+  key_take_max(hi, lo, b, d);
+  a = hi;
+  b = hi;
+  c = lo;
+  d = lo;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\tv_permlane32_swap_b32 %2, %3"
+               : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+  hi = a;
+  lo = c;
+  key_take_max(hi, lo, b, d);
+}
 
 __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict__ logits, int32_t* __restrict__ ids,
                                                         float* __restrict__ w, int64_t T, int E, int k) {
@@ -35,41 +87,34 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict_
   const bool live = t < T;  // no early return: the block meets at a barrier below
 
   float z[4];
+  uint32_t khi[4], klo[4];
   bool taken[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int e = lane + 64 * q;
     z[q] = (live && e < E) ? logits[t * E + e] : -INFINITY;
+    const bool cand = live && e < E && !__builtin_isnan(z[q]);
+    khi[q] = cand ? route_key_hi(z[q]) : 0u;
+    klo[q] = cand ? 0xFFFFu - (uint32_t)e : 0u;
     taken[q] = false;
   }
   int found = 0;
   for (int r = 0; r < k; ++r) {
-    // this lane's best untaken candidate
-    float bv = -INFINITY;
-    int bid = 0x7fffffff;
+    uint32_t hi = khi[0], lo = klo[0];
+#pragma unroll
+    for (int q = 1; q < 4; ++q) key_take_max(hi, lo, khi[q], klo[q]);
+    wave_key_max(hi, lo);
+    const uint32_t best = __builtin_amdgcn_readfirstlane(lo);
+    if (best == 0u) break;  // wave-uniform: nothing selectable left
+    ++found;
+    const int bid = (int)(0xFFFFu - best);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int e = lane + 64 * q;
-      if (e < E && !taken[q] && (z[q] > bv || (z[q] == bv && e < bid))) {
-        bv = z[q];
-        bid = e;
-      }
+      const bool hit = bid == lane + 64 * q;
+      taken[q] = taken[q] || hit;
+      khi[q] = hit ? 0u : khi[q];
+      klo[q] = hit ? 0u : klo[q];
     }
-    // wave argmax, same comparison
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = shfl_xor(bv, off);
-      const int oid = __builtin_amdgcn_ds_bpermute((lane ^ off) << 2, bid);
-      if (ov > bv || (ov == bv && oid < bid)) {
-        bv = ov;
-        bid = oid;
-      }
-    }
-    if (bid == 0x7fffffff) break;  // wave-uniform: nothing selectable left
-    ++found;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (bid == lane + 64 * q) taken[q] = true;
   }
   // position of each selected expert in ascending id order
   int before = 0;
