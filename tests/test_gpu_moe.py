@@ -53,6 +53,29 @@ def test_route_ties_go_to_lower_ids(inv):
     assert ids5.cpu().tolist() == [[3, 9]]
 
 
+def test_route_signed_zeros_and_minus_inf(inv):
+    # -0 and +0 compare equal, so the lower id takes the last slot between
+    # them whichever sign it has; -inf logits are selectable (after every
+    # finite one) and get weight exactly 0
+    x = torch.full((5, 64), -1.0)
+    x[0:2, 0:7] = 1.0
+    x[0, [10, 50]] = torch.tensor([-0.0, 0.0])
+    x[1, [10, 50]] = torch.tensor([0.0, -0.0])
+    x[2, :] = float("-inf")
+    x[2, [5, 40]] = torch.tensor([0.5, -2.0])      # two finite, then -inf by id
+    x[3, :] = float("-inf")
+    x[3, 63] = -0.0
+    x[4] = torch.randn(64, generator=torch.Generator().manual_seed(7)).round()  # many ties
+    ids, w = inv.moe_route(x.to(DEV), inv.contract(leaves=8))
+    oid, ow = omoe.route(x.double().numpy(), 8)
+    assert np.array_equal(ids.cpu().numpy(), oid)
+    assert np.allclose(w.cpu().numpy(), ow, rtol=1e-6, atol=0)
+    assert ids[0].cpu().tolist() == [0, 1, 2, 3, 4, 5, 6, 10]
+    assert ids[1].cpu().tolist() == [0, 1, 2, 3, 4, 5, 6, 10]
+    finite = (ids[2] == 5) | (ids[2] == 40)
+    assert (w[2][~finite] == 0).all() and (w[2][finite] > 0).all()
+
+
 def test_route_nan_rows_are_marked(inv):
     x = torch.randn((2, 16), generator=torch.Generator().manual_seed(1))
     x[0, :13] = float("nan")   # only 3 selectable experts for k = 4
