@@ -87,6 +87,13 @@ inv_status check_logprob_contract(const inv_contract* c, int64_t V) {
 
 bool out_is_bf16(const inv_contract* c) { return c->out_dtype == INV_BF16; }
 
+// A dispatch counts its work-items (workgroups x 256 lanes here) in 32 bits.
+// Kernels with one 256-lane workgroup per row therefore take fewer than 2^24
+// rows per launch, and those with four rows (one wave each) per workgroup
+// fewer than 2^26; more is refused before any launch.
+constexpr int64_t kMaxRowsWg = (int64_t)1 << 24;
+constexpr int64_t kMaxRowsWave = (int64_t)1 << 26;
+
 // Leaf groups for the single-rank GEMM when 128 x 128 tiles alone leave
 // compute units idle (M >= 8; below 8 rows the stream kernel reads the
 // weights fastest in one pass): G aligned subtrees of L/G leaves each are
@@ -340,6 +347,7 @@ inv_status inv_rmsnorm(const inv_contract* c, const void* x, const void* gamma, 
   if (s != INV_OK) return s;
   if (M < 0 || H < 0) return INV_E_ARG;
   if (H % 8 != 0 || H > 16384 || (H > 0 && H < 8)) return INV_E_UNSUPPORTED;
+  if (M >= kMaxRowsWave) return INV_E_UNSUPPORTED;
   if (M == 0 || H == 0) return INV_OK;
   if (!x || !gamma || !y) return INV_E_ARG;
   if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(gamma) | reinterpret_cast<uintptr_t>(y)) & 15u)
@@ -355,6 +363,7 @@ inv_status inv_logprob(const inv_contract* c, const float* logits, int64_t ldl, 
   inv_status s = check_logprob_contract(c, V);
   if (s != INV_OK) return s;
   if (M < 0 || V <= 0 || ldl < V) return INV_E_ARG;
+  if (M >= kMaxRowsWg) return INV_E_UNSUPPORTED;
   if (M == 0) return INV_OK;
   if (!logits || !target || !out) return INV_E_ARG;
   return hip_status(inv::launch_logprob(logits, ldl, target, out, nullptr, nullptr, M, V, (int)c->leaves, 0,
@@ -443,7 +452,7 @@ size_t block16_ws_bytes(int64_t M, int64_t V) {
 
 inv_status check_block16(const inv_contract* c, int64_t M, int64_t V, void* ws, size_t ws_bytes) {
   if (M < 0 || V <= 0) return INV_E_ARG;
-  if ((V + 15) / 16 > kMaxBlocks16 || M > (int64_t)1 << 31) return INV_E_UNSUPPORTED;
+  if ((V + 15) / 16 > kMaxBlocks16 || M >= kMaxRowsWg) return INV_E_UNSUPPORTED;
   if (M > 0 && (!ws || ws_bytes < block16_ws_bytes(M, V))) return INV_E_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(ws) & 7u) return INV_E_ARG;  // (m, s) pairs are read as float2
   (void)c;
@@ -496,6 +505,7 @@ inv_status inv_logprob_partials(const inv_contract* c, const float* logits, int6
   if (s != INV_OK) return s;
   if (M < 0 || V <= 0 || ldl < V) return INV_E_ARG;
   if (chunk_lo >= chunk_hi || chunk_hi > c->leaves) return INV_E_ARG;
+  if (M >= kMaxRowsWg) return INV_E_UNSUPPORTED;
   if (M == 0) return INV_OK;
   if (!logits || !target || !stats || !tlogit) return INV_E_ARG;
   return hip_status(inv::launch_logprob(logits, ldl, target, nullptr, stats, tlogit, M, V, (int)c->leaves,
@@ -507,6 +517,7 @@ inv_status inv_logprob_combine(const inv_contract* c, const float* stats, const 
   inv_status s = check_logprob_contract(c, V);
   if (s != INV_OK) return s;
   if (M < 0 || V <= 0) return INV_E_ARG;
+  if (M >= kMaxRowsWg) return INV_E_UNSUPPORTED;
   if (M == 0) return INV_OK;
   if (!stats || !tlogit || !target || !out) return INV_E_ARG;
   return hip_status(inv::launch_logprob_combine(stats, tlogit, target, out, M, V, (int)c->leaves,
@@ -623,6 +634,7 @@ inv_status inv_moe_route(const inv_contract* c, const float* logits, int32_t* id
   if (s != INV_OK) return s;
   if (T < 0 || E <= 0) return INV_E_ARG;
   if (E > 256 || (int64_t)c->leaves > E || c->leaves > 32) return INV_E_UNSUPPORTED;
+  if (T >= kMaxRowsWave) return INV_E_UNSUPPORTED;  // one wave per token
   if (T == 0) return INV_OK;
   if (!logits || !ids || !w) return INV_E_ARG;
   return hip_status(inv::launch_moe_route(logits, ids, w, T, E, (int)c->leaves, stream));
@@ -703,6 +715,7 @@ inv_status inv_moe_combine(const inv_contract* c, const float* Y, const float* w
   if (s != INV_OK) return s;
   if (c->leaves > 32) return INV_E_UNSUPPORTED;
   if (T < 0 || H < 0 || y_rows < 0) return INV_E_ARG;
+  if (T > ((int64_t)1 << 31) - 1) return INV_E_UNSUPPORTED;  // tokens index the grid's second dimension
   if (T == 0 || H == 0) return INV_OK;
   if (!Y || !w || !slot || !out) return INV_E_ARG;
   if (c->out_dtype != INV_BF16) return INV_E_CONTRACT;

@@ -505,14 +505,16 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(const uint32_t* __restric
                                                        const float* __restrict__ g, float* __restrict__ qh,
                                                        float* __restrict__ kh, float* __restrict__ alpha,
                                                        int64_t TH) {
-  const int64_t th = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (th >= TH) return;  // uniform per wave; no block-wide barrier below
-  const float2 kk = l2norm_pair(k[th * 64 + lane], 1.0f);
-  const float2 qq = l2norm_pair(q[th * 64 + lane], kInvSqrtD);
-  reinterpret_cast<float2*>(kh)[th * 64 + lane] = kk;
-  reinterpret_cast<float2*>(qh)[th * 64 + lane] = qq;
-  if (lane == 0) alpha[th] = gate_alpha(g[th]);
+  // one wave per (token, head), the grid striding over the rest (uniform per
+  // wave; no block-wide barrier below)
+  for (int64_t th = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); th < TH; th += (int64_t)gridDim.x * 4) {
+    const float2 kk = l2norm_pair(k[th * 64 + lane], 1.0f);
+    const float2 qq = l2norm_pair(q[th * 64 + lane], kInvSqrtD);
+    reinterpret_cast<float2*>(kh)[th * 64 + lane] = kk;
+    reinterpret_cast<float2*>(qh)[th * 64 + lane] = qq;
+    if (lane == 0) alpha[th] = gate_alpha(g[th]);
+  }
 }
 
 // Sequence bounds from the device table, clamped to [0, T] so that a
@@ -808,7 +810,7 @@ __global__ __launch_bounds__(64 * kStateWaves) __attribute__((amdgpu_waves_per_e
 hipError_t launch_gdn_prefill(const GdnArgs& a, int C, bool out_bf16, hipStream_t s) {
   const int64_t TH = a.T * a.H;
   if (TH > 0) {
-    hipLaunchKernelGGL(gdn_prep_kernel, dim3((unsigned)((TH + 3) / 4)), dim3(256), 0, s,
+    hipLaunchKernelGGL(gdn_prep_kernel, dim3(stride_grid(TH, 4)), dim3(256), 0, s,
                        reinterpret_cast<const uint32_t*>(a.q), reinterpret_cast<const uint32_t*>(a.k), a.g, a.qh, a.kh,
                        a.alpha, TH);
   }

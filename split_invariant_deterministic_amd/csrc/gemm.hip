@@ -1193,33 +1193,33 @@ __global__ __launch_bounds__(64 * NW) void gemm_stream_kernel(TileParams p) {
 template <int CNT, bool OUT_BF16, bool FOLD>
 __global__ __launch_bounds__(256) void tree_combine_kernel(const float* __restrict__ P, int64_t plane,
                                                            void* __restrict__ C) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= plane) return;
-  float v[CNT];
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < plane; i += (int64_t)gridDim.x * 256) {
+    float v[CNT];
 #pragma unroll
-  for (int j = 0; j < CNT; ++j) v[j] = P[(int64_t)j * plane + i];
-  float s;
-  if constexpr (FOLD) {
-    s = v[0];
+    for (int j = 0; j < CNT; ++j) v[j] = P[(int64_t)j * plane + i];
+    float s;
+    if constexpr (FOLD) {
+      s = v[0];
 #pragma unroll
-    for (int j = 1; j < CNT; ++j) s = s + v[j];
-  } else {
+      for (int j = 1; j < CNT; ++j) s = s + v[j];
+    } else {
 #pragma unroll
-    for (int w = CNT; w > 1; w /= 2)
+      for (int w = CNT; w > 1; w /= 2)
 #pragma unroll
-      for (int j = 0; j < w / 2; ++j) v[j] = v[2 * j] + v[2 * j + 1];
-    s = v[0];
+        for (int j = 0; j < w / 2; ++j) v[j] = v[2 * j] + v[2 * j + 1];
+      s = v[0];
+    }
+    if constexpr (OUT_BF16)
+      reinterpret_cast<uint16_t*>(C)[i] = f32_to_bf16_bits(s);
+    else
+      reinterpret_cast<float*>(C)[i] = s;
   }
-  if constexpr (OUT_BF16)
-    reinterpret_cast<uint16_t*>(C)[i] = f32_to_bf16_bits(s);
-  else
-    reinterpret_cast<float*>(C)[i] = s;
 }
 
 __global__ __launch_bounds__(256) void cast_bf16_kernel(const float* __restrict__ x, uint16_t* __restrict__ y,
                                                         int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) y[i] = f32_to_bf16_bits(x[i]);
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    y[i] = f32_to_bf16_bits(x[i]);
 }
 
 // ------------------------------------------------------------------ dispatch
@@ -1298,7 +1298,7 @@ hipError_t stream_dispatch(const TileParams& p, int fm, dim3 grid, int nw, hipSt
 
 template <int CNT>
 hipError_t combine_cnt(const float* P, int64_t plane, void* C, bool out_bf16, bool fold, hipStream_t s) {
-  dim3 grid((unsigned)((plane + 255) / 256));
+  dim3 grid(stride_grid(plane, 256));
   if (out_bf16) {
     if (fold) hipLaunchKernelGGL((tree_combine_kernel<CNT, true, true>), grid, dim3(256), 0, s, P, plane, C);
     else hipLaunchKernelGGL((tree_combine_kernel<CNT, true, false>), grid, dim3(256), 0, s, P, plane, C);
@@ -1414,7 +1414,7 @@ hipError_t launch_tree_combine(const float* P, int count, int64_t plane, void* C
 }
 
 hipError_t launch_cast_bf16(const float* x, uint16_t* y, int64_t n, hipStream_t s) {
-  hipLaunchKernelGGL(cast_bf16_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, y, n);
+  hipLaunchKernelGGL(cast_bf16_kernel, dim3(stride_grid(n, 256)), dim3(256), 0, s, x, y, n);
   return hipGetLastError();
 }
 

@@ -7,6 +7,15 @@
 
 namespace inv {
 
+// Workgroups of a grid-stride elementwise launch: enough to cover n items at
+// `per` items per workgroup, at most 2^20 (so the dispatch's work-item count,
+// workgroups times 256 lanes, stays below 2^32 whatever n is; the kernels
+// walk the rest by the grid stride).
+inline unsigned stride_grid(int64_t n, int64_t per) {
+  const int64_t g = (n + per - 1) / per;
+  return (unsigned)(g < ((int64_t)1 << 20) ? (g > 0 ? g : 1) : ((int64_t)1 << 20));
+}
+
 // ---- GEMM -----------------------------------------------------------------
 // One launch reduces, for every output element, `groups` independent balanced
 // subtrees of `nl` consecutive leaves each: group z covers leaves

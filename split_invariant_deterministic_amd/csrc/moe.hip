@@ -286,28 +286,28 @@ __global__ __launch_bounds__(256) void moe_scatter_kernel(const int32_t* __restr
 // Scalar form (any F).
 __global__ __launch_bounds__(256) void swiglu_kernel(const uint16_t* __restrict__ gu, uint16_t* __restrict__ a,
                                                      int64_t R, int64_t F) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= R * F) return;
-  const int64_t r = i / F, f = i - r * F;
-  const float g = bf16_bits_to_f32(gu[r * 2 * F + f]);
-  const float u = bf16_bits_to_f32(gu[r * 2 * F + F + f]);
-  a[i] = f32_to_bf16_bits(silu_mul(g, u));
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < R * F; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / F, f = i - r * F;
+    const float g = bf16_bits_to_f32(gu[r * 2 * F + f]);
+    const float u = bf16_bits_to_f32(gu[r * 2 * F + F + f]);
+    a[i] = f32_to_bf16_bits(silu_mul(g, u));
+  }
 }
 
 // F % 8 == 0: 8 outputs per thread with 16-byte accesses (same per-element math).
 __global__ __launch_bounds__(256) void swiglu8_kernel(const uint16_t* __restrict__ gu, uint16_t* __restrict__ a,
                                                       int64_t R, int64_t F) {
-  const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 8-element group
   const int64_t F8 = F >> 3;
-  if (v >= R * F8) return;
-  const int64_t r = v / F8, f = (v - r * F8) * 8;
-  const u32x4 g = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(gu + r * 2 * F + f));
-  const u32x4 u = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(gu + r * 2 * F + F + f));
-  u32x4 o;
+  for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < R * F8; v += (int64_t)gridDim.x * 256) {
+    const int64_t r = v / F8, f = (v - r * F8) * 8;  // 8-element group v
+    const u32x4 g = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(gu + r * 2 * F + f));
+    const u32x4 u = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(gu + r * 2 * F + F + f));
+    u32x4 o;
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-    o[q] = pack_bf16x2(silu_mul(bf16_lo(g[q]), bf16_lo(u[q])), silu_mul(bf16_hi(g[q]), bf16_hi(u[q])));
-  __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(a + r * F + f));
+    for (int q = 0; q < 4; ++q)
+      o[q] = pack_bf16x2(silu_mul(bf16_lo(g[q]), bf16_lo(u[q])), silu_mul(bf16_hi(g[q]), bf16_hi(u[q])));
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(a + r * F + f));
+  }
 }
 
 // ----------------------------------------------------------------- combine
@@ -422,10 +422,10 @@ hipError_t launch_swiglu(const void* gu, void* a, int64_t R, int64_t F, hipStrea
   const bool vec = F % 8 == 0 && ((reinterpret_cast<uintptr_t>(gu) | reinterpret_cast<uintptr_t>(a)) & 15u) == 0;
   if (vec) {
     const int64_t n = R * (F / 8);
-    hipLaunchKernelGGL(swiglu8_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, G, O, R, F);
+    hipLaunchKernelGGL(swiglu8_kernel, dim3(stride_grid(n, 256)), dim3(256), 0, s, G, O, R, F);
   } else {
     const int64_t n = R * F;
-    hipLaunchKernelGGL(swiglu_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, G, O, R, F);
+    hipLaunchKernelGGL(swiglu_kernel, dim3(stride_grid(n, 256)), dim3(256), 0, s, G, O, R, F);
   }
   return hipGetLastError();
 }

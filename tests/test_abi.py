@@ -217,6 +217,28 @@ def test_entry_points_reject_before_any_launch():
         == inv.E_ARG
 
 
+def test_row_counts_beyond_a_dispatch_are_refused():
+    # a dispatch counts workgroups x 256 lanes in 32 bits: one-workgroup-per-row
+    # kernels take fewer than 2^24 rows, one-wave-per-row ones fewer than 2^26
+    inv = _inv()
+    lib = inv._lib
+    by = ctypes.byref
+    null = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(1 << 20)
+    c = inv.contract()
+    rows_wg, rows_wave = 1 << 24, 1 << 26
+    assert lib.inv_rmsnorm(by(c), fake, fake, fake, rows_wave, 8, null) == inv.E_UNSUPPORTED
+    clp = inv.contract(leaves=4)
+    assert lib.inv_logprob(by(clp), fake, 16, fake, fake, rows_wg, 16, null) == inv.E_UNSUPPORTED
+    assert lib.inv_logprob_partials(by(clp), fake, 16, fake, fake, fake, rows_wg, 16, 0, 4, null) \
+        == inv.E_UNSUPPORTED
+    assert lib.inv_logprob_combine(by(clp), fake, fake, fake, fake, rows_wg, 16, null) == inv.E_UNSUPPORTED
+    assert lib.inv_logprob_block16(by(c), fake, 16, fake, fake, rows_wg, 16, fake, 1 << 40, null) \
+        == inv.E_UNSUPPORTED
+    assert lib.inv_moe_route(by(c), fake, fake, fake, rows_wave, 128, null) == inv.E_UNSUPPORTED
+    assert lib.inv_moe_combine(by(c), fake, fake, fake, 4, fake, 1 << 31, 64, null) == inv.E_UNSUPPORTED
+
+
 def test_binding_workspace_checked_before_the_call():
     """The binding reports a workspace's size in bytes from its element type
     and refuses a host tensor, before the library sees the pointer."""
