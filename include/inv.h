@@ -291,6 +291,7 @@ inv_status inv_cast_bf16(const float* x, uint16_t* y, int64_t n, hipStream_t str
  * 64-lane group; each lane runs fused multiply-adds over its elements in
  * ascending h; the 64 lane sums are combined by an xor butterfly with
  * offsets 32, 16, 8, 4, 2, 1. H % 8 == 0, 8 <= H <= 16384. eps = c->eps.
+ * M < 2^26 (one wave per row; else INV_E_UNSUPPORTED).
  * ------------------------------------------------------------------------ */
 inv_status inv_rmsnorm(const inv_contract* c, const void* x, const void* gamma, void* y,
                        int64_t M, int64_t H, hipStream_t stream);
@@ -309,7 +310,9 @@ inv_status inv_rmsnorm(const inv_contract* c, const void* x, const void* gamma, 
  * element e of the chunk on lane e % 64, each lane summing in ascending e and
  * the lanes combined by an xor butterfly 32..1. The (m_j, s_j) are merged by
  * the contract's tree with m = max(m1,m2), s = s1*exp(m1-m) + s2*exp(m2-m);
- * LSE = m + log(s). A target outside [0, V) gives NaN.
+ * LSE = m + log(s). A target outside [0, V) gives NaN. M < 2^24 (one
+ * workgroup per row) here and in every logprob entry point below, else
+ * INV_E_UNSUPPORTED.
  * ------------------------------------------------------------------------ */
 inv_status inv_logprob(const inv_contract* c, const float* logits, int64_t ldl,
                        const int32_t* target, float* out, int64_t M, int64_t V,
@@ -392,7 +395,8 @@ inv_status inv_attn_combine(const inv_contract* c, const void* ws, size_t ws_byt
  * (fp32; ties go to the lower expert id), emitted in ascending expert id;
  * w = softmax over the k selected logits in fp32 (max-shifted, exp2 form,
  * denominator summed in ascending expert id). logits [T, E] fp32,
- * ids [T, k] int32, w [T, k] fp32. E <= 256, k <= E. */
+ * ids [T, k] int32, w [T, k] fp32. E <= 256, k <= E, T < 2^26 (one wave
+ * per token; else INV_E_UNSUPPORTED). */
 inv_status inv_moe_route(const inv_contract* c, const float* logits, int32_t* ids, float* w,
                          int64_t T, int32_t E, hipStream_t stream);
 
@@ -542,7 +546,7 @@ inv_status inv_swiglu(const inv_contract* c, const void* GU, void* Aout, int64_t
  * emits), fp32 products and the contract's fp32 tree (balanced; left fold
  * only as the contrasting schedule). Y [y_rows, H] fp32, w [T, k] fp32,
  * slot [T, k] int32, out [T, H] bf16. A slot outside [0, y_rows) makes that
- * token's row NaN. */
+ * token's row NaN. T < 2^31, else INV_E_UNSUPPORTED. */
 inv_status inv_moe_combine(const inv_contract* c, const float* Y, const float* w,
                            const int32_t* slot, int64_t y_rows, void* out, int64_t T, int64_t H,
                            hipStream_t stream);
