@@ -18,8 +18,8 @@ namespace {
 
 // ------------------------------------------------------------------ routing
 //
-// One wave per token. Lane l holds experts l, l+64, l+128, l+192. k rounds of
-// a wave-wide argmax (larger logit wins, equal logits go to the lower id)
+// Sixteen lanes per token. k rounds of an argmax over the token's experts
+// (larger logit wins, equal logits go to the lower id)
 // select the top k; NaN logits are never selected, and a round without a
 // candidate leaves id -1 and weight NaN (a data error marks the token).
 // The selection is then written in ascending expert id, and the weights are
@@ -30,8 +30,8 @@ namespace {
 // high word the logit mapped monotonically to an unsigned integer (-0 taken
 // as +0, since the two compare equal), low word 0xFFFF - id. NaN logits,
 // experts past E and taken experts have key 0. A round is a branch-free
-// maximum over the lane's keys, then over the wave by four DPP steps inside
-// each row of 16 lanes and the row and half swaps (VALU only).
+// maximum over the lane's keys, then over the token's 16 lanes by four DPP
+// steps (VALU only).
 constexpr int kRouteMaxK = 32;
 
 __device__ __forceinline__ uint32_t route_key_hi(float z) {
@@ -52,46 +52,38 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
 }
 
-// Maximum key over the 64 lanes, left in every lane. Within a row: quad
-// pairs (xor 1, xor 2), then the half-row and row mirrors; then the row swap
-// (lane ^ 16) and the half swap (lane ^ 32), each exchanging two copies of
-// the key so that every lane holds its own and its partner's. The maximum of
-// a set does not depend on the order it is taken in.
-__device__ __forceinline__ void wave_key_max(uint32_t& hi, uint32_t& lo) {
+// Maximum key over each row of 16 lanes, left in every lane of the row:
+// quad pairs (xor 1, xor 2), then the half-row and row mirrors. The maximum
+// of a set does not depend on the order it is taken in.
+__device__ __forceinline__ void row_key_max(uint32_t& hi, uint32_t& lo) {
   key_take_max(hi, lo, dpp_u32<0xB1>(hi), dpp_u32<0xB1>(lo));
   key_take_max(hi, lo, dpp_u32<0x4E>(hi), dpp_u32<0x4E>(lo));
   key_take_max(hi, lo, dpp_u32<0x141>(hi), dpp_u32<0x141>(lo));
   key_take_max(hi, lo, dpp_u32<0x140>(hi), dpp_u32<0x140>(lo));
-  uint32_t a = hi, b = hi, c = lo, d = lo;
-  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\tv_permlane16_swap_b32 %2, %3"
-               : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
-  hi = a;
-  lo = c;
-  key_take_max(hi, lo, b, d);
-  a = hi;
-  b = hi;
-  c = lo;
-  d = lo;
-  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\tv_permlane32_swap_b32 %2, %3"
-               : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
-  hi = a;
-  lo = c;
-  key_take_max(hi, lo, b, d);
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+// Sixteen lanes per token, four tokens per wave: lane l of a row holds
+// experts l, l + 16, ..., l + 16 (NQ - 1) (NQ = ceil(E / 16) rounded up to
+// 4, 8 or 16).
+template <int NQ>
 __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict__ logits, int32_t* __restrict__ ids,
                                                         float* __restrict__ w, int64_t T, int E, int k) {
-  __shared__ float ez[4][kRouteMaxK];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+  __shared__ float ez[16][kRouteMaxK];
+  const int lane = threadIdx.x & 63, l16 = lane & 15, row = threadIdx.x >> 4;  // row: token of the block
+  const int64_t t = (int64_t)blockIdx.x * 16 + row;
   const bool live = t < T;  // no early return: the block meets at a barrier below
 
-  float z[4];
-  uint32_t khi[4], klo[4];
-  bool taken[4];
+  float z[NQ];
+  uint32_t khi[NQ], klo[NQ];
+  bool taken[NQ];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = lane + 64 * q;
+  for (int q = 0; q < NQ; ++q) {
+    const int e = l16 + 16 * q;
     z[q] = (live && e < E) ? logits[t * E + e] : -INFINITY;
     const bool cand = live && e < E && !__builtin_isnan(z[q]);
     khi[q] = cand ? route_key_hi(z[q]) : 0u;
@@ -102,50 +94,53 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict_
   for (int r = 0; r < k; ++r) {
     uint32_t hi = khi[0], lo = klo[0];
 #pragma unroll
-    for (int q = 1; q < 4; ++q) key_take_max(hi, lo, khi[q], klo[q]);
-    wave_key_max(hi, lo);
-    const uint32_t best = __builtin_amdgcn_readfirstlane(lo);
-    if (best == 0u) break;  // wave-uniform: nothing selectable left
-    ++found;
-    const int bid = (int)(0xFFFFu - best);
+    for (int q = 1; q < NQ; ++q) key_take_max(hi, lo, khi[q], klo[q]);
+    row_key_max(hi, lo);  // this token's best remaining key, in all 16 lanes
+    if (__ballot(lo != 0u) == 0) break;  // wave-uniform: no token of the wave has a candidate left
+    found += lo != 0u;
+    const int bid = lo != 0u ? (int)(0xFFFFu - lo) : -1;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const bool hit = bid == lane + 64 * q;
+    for (int q = 0; q < NQ; ++q) {
+      const bool hit = bid == l16 + 16 * q;
       taken[q] = taken[q] || hit;
       khi[q] = hit ? 0u : khi[q];
       klo[q] = hit ? 0u : klo[q];
     }
   }
-  // position of each selected expert in ascending id order
+  // position of each selected expert in ascending id order within the token
+  const int sh = 16 * ((threadIdx.x >> 4) & 3);
   int before = 0;
-  int pos[4];
+  int pos[NQ];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint64_t bal = __ballot(taken[q]);
-    pos[q] = before + __popcll(bal & ((1ull << lane) - 1ull));
-    before += __popcll(bal);
+  for (int q = 0; q < NQ; ++q) {
+    const uint32_t bits = (uint32_t)(__ballot(taken[q]) >> sh) & 0xFFFFu;
+    pos[q] = before + __popc(bits & ((1u << l16) - 1u));
+    before += __popc(bits);
   }
   float m = -INFINITY;
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
+  for (int q = 0; q < NQ; ++q)
     if (taken[q]) m = fmaxf(m, z[q]);
-  m = wave_max(m);
+  m = fmaxf(m, dpp_f32<0xB1>(m));
+  m = fmaxf(m, dpp_f32<0x4E>(m));
+  m = fmaxf(m, dpp_f32<0x141>(m));
+  m = fmaxf(m, dpp_f32<0x140>(m));
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-    if (taken[q]) ez[wave][pos[q]] = exp_shifted(z[q], m);
+  for (int q = 0; q < NQ; ++q)
+    if (taken[q]) ez[row][pos[q]] = exp_shifted(z[q], m);
   __syncthreads();
   float den = 0.0f;
-  for (int j = 0; j < found; ++j) den = den + ez[wave][j];
+  for (int j = 0; j < found; ++j) den = den + ez[row][j];
   if (!live) return;
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
+  for (int q = 0; q < NQ; ++q)
     if (taken[q]) {
-      ids[t * k + pos[q]] = lane + 64 * q;
-      w[t * k + pos[q]] = ez[wave][pos[q]] / den;
+      ids[t * k + pos[q]] = l16 + 16 * q;
+      w[t * k + pos[q]] = ez[row][pos[q]] / den;
     }
-  if (lane >= found && lane < k) {  // rounds that found no candidate
-    ids[t * k + lane] = -1;
-    w[t * k + lane] = __builtin_nanf("");
+  for (int j = found + l16; j < k; j += 16) {  // rounds that found no candidate
+    ids[t * k + j] = -1;
+    w[t * k + j] = __builtin_nanf("");
   }
 }
 
@@ -398,7 +393,10 @@ hipError_t combine_k(const float* Y, const float* w, const int32_t* slot, int64_
 
 hipError_t launch_moe_route(const float* logits, int32_t* ids, float* w, int64_t T, int E, int k, hipStream_t s) {
   if (k > kRouteMaxK || E > 256) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(moe_route_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, logits, ids, w, T, E, k);
+  const dim3 grid((unsigned)((T + 15) / 16));
+  if (E <= 64) hipLaunchKernelGGL(moe_route_kernel<4>, grid, dim3(256), 0, s, logits, ids, w, T, E, k);
+  else if (E <= 128) hipLaunchKernelGGL(moe_route_kernel<8>, grid, dim3(256), 0, s, logits, ids, w, T, E, k);
+  else hipLaunchKernelGGL(moe_route_kernel<16>, grid, dim3(256), 0, s, logits, ids, w, T, E, k);
   return hipGetLastError();
 }
 
