@@ -395,8 +395,8 @@ inv_status inv_attn_combine(const inv_contract* c, const void* ws, size_t ws_byt
  * (fp32; ties go to the lower expert id), emitted in ascending expert id;
  * w = softmax over the k selected logits in fp32 (max-shifted, exp2 form,
  * denominator summed in ascending expert id). logits [T, E] fp32,
- * ids [T, k] int32, w [T, k] fp32. E <= 256, k <= E, T < 2^26 (one wave
- * per token; else INV_E_UNSUPPORTED). */
+ * ids [T, k] int32, w [T, k] fp32. E <= 256, k <= E, T < 2^26, else
+ * INV_E_UNSUPPORTED. */
 inv_status inv_moe_route(const inv_contract* c, const float* logits, int32_t* ids, float* w,
                          int64_t T, int32_t E, hipStream_t stream);
 

@@ -634,7 +634,7 @@ inv_status inv_moe_route(const inv_contract* c, const float* logits, int32_t* id
   if (s != INV_OK) return s;
   if (T < 0 || E <= 0) return INV_E_ARG;
   if (E > 256 || (int64_t)c->leaves > E || c->leaves > 32) return INV_E_UNSUPPORTED;
-  if (T >= kMaxRowsWave) return INV_E_UNSUPPORTED;  // one wave per token
+  if (T >= kMaxRowsWave) return INV_E_UNSUPPORTED;  // (16 lanes per token: within the bound)
   if (T == 0) return INV_OK;
   if (!logits || !ids || !w) return INV_E_ARG;
   return hip_status(inv::launch_moe_route(logits, ids, w, T, E, (int)c->leaves, stream));
