@@ -135,3 +135,20 @@ def test_attention_workspace_size_is_counted_in_bytes(inv):
     with pytest.raises(ValueError):
         inv.decode_attn(q, k, v, cu, q_seq, q_pos, c, ws=torch.empty(need, dtype=torch.uint8))
     torch.cuda.synchronize()
+
+
+def test_elementwise_launches_past_one_grid_pass(inv):
+    # More elements than the capped grid covers in one pass (2^20 workgroups
+    # x 256 lanes = 2^28): the tree combine and the cast walk the rest by the
+    # grid stride, and every element still matches torch's fp32 sum and
+    # round-to-nearest-even cast bit for bit.
+    M, N = 4099, 65537
+    assert M * N > (1 << 28)
+    g = torch.Generator(device=DEV).manual_seed(11)
+    P = torch.randn((2, M, N), generator=g, device=DEV, dtype=torch.float32)
+    out = inv.tree_combine(P, inv.contract(leaves=2, out="bf16"))
+    ref = (P[0] + P[1]).to(torch.bfloat16)
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    del out, ref
+    y = inv.cast_bf16(P[0])
+    assert torch.equal(y.view(torch.int16), P[0].to(torch.bfloat16).view(torch.int16))
